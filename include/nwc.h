@@ -1,0 +1,170 @@
+/*
+ * nwc.h -- C ABI of libnwc: lossless BF16 weight compression decoded inside
+ * the matrix-vector kernel, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages, cited by title and section):
+ *  - "NWC -- Neural Weight Compression" (PyPI description of
+ *    neural-weight-compression 0.9.0), "How it works": a BF16 weight splits
+ *    into a near-random byte stored raw and an exponent byte that is entropy
+ *    coded (bullet "Byte planes"); the matrix-vector kernel decodes in
+ *    registers so no decompressed weight reaches memory (bullet "Fused
+ *    kernel"); dequantization runs on the same decoder (bullet
+ *    "Dequantization and embedding lookup"); the encoder needs only the
+ *    weights ("Status and limitations").
+ *  - "Unweight: how we compressed an LLM 22% without sacrificing quality"
+ *    (Techlist.io summary), "Compressing BF16 Weights": Huffman code on the
+ *    exponent, sign and mantissa unchanged; "Direct GPU Decompression":
+ *    weights stay compressed in HBM and are decompressed on chip right
+ *    before the product.
+ *
+ * Data format: one self-describing, position-independent blob per matrix W
+ * [rows, cols] (nn.Linear [out, in], row-major BF16).  The raw byte of a
+ * weight holds its sign (bit 7) and 7 fraction bits; the 8-bit exponent is
+ * coded with one canonical Huffman code per tensor, length-limited to
+ * max_code_len bits, in tiles of tile_rows x tile_cols split into
+ * chunks_per_tile column-strip chunks; per-tile word offsets and per-chunk bit
+ * lengths let every tile (and chunk) decode on its own.
+ *
+ * Conventions for every function:
+ *  - Every call returns an nwc_status; nothing throws across the ABI and there
+ *    is no global error state.  Host-side validation (null pointers, sizes,
+ *    alignment, header consistency) happens before any device work: on an
+ *    error nothing is enqueued.
+ *  - The caller owns all memory (host blob, device blob, inputs, outputs,
+ *    workspace).  The library never allocates device memory, never frees and
+ *    never synchronizes a stream; device calls only enqueue work on `stream`
+ *    (a hipStream_t, 0 = the null stream) and every buffer must stay valid
+ *    until that work completes.
+ *  - BF16 data is passed as uint16_t bit patterns.
+ *  - Device pointers: blob 256-byte aligned; x, y, X, Y, W 16-byte aligned;
+ *    leading dimensions in elements, multiples of 8 for 16-byte rows.
+ *  - The device blob must hold the same bytes that were passed to
+ *    nwc_inspect.  Corrupted device data is not detected: kernels clamp every
+ *    read to the blob, so it yields wrong numbers, never a memory fault.
+ *  - Results are deterministic: a fixed summation order, no floating-point
+ *    atomics, so repeated calls give bitwise-identical outputs.
+ *  - Functions are reentrant; the library holds no mutable global state.
+ */
+#ifndef NWC_H
+#define NWC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NWC_OK = 0,
+  NWC_ERR_INVALID_ARG = -1,      /* null pointer, bad size, bad parameter */
+  NWC_ERR_BUFFER_TOO_SMALL = -2, /* output or workspace capacity too small */
+  NWC_ERR_BAD_FORMAT = -3,       /* blob fails validation */
+  NWC_ERR_UNSUPPORTED = -4,      /* valid request this build cannot run */
+  NWC_ERR_ALIGNMENT = -5,        /* pointer or leading dimension misaligned */
+  NWC_ERR_HIP = -6               /* a HIP runtime call or launch failed */
+} nwc_status;
+
+typedef enum {
+  NWC_OUT_BF16 = 0, /* round-to-nearest-even from the FP32 accumulator */
+  NWC_OUT_F32 = 1
+} nwc_out_type;
+
+/* Encoding parameters; a zero field takes the default in brackets.
+ * Constraints: tile_cols % chunks_per_tile == 0, 8 <= max_code_len <= 12,
+ * tile_rows * (tile_cols / chunks_per_tile) * max_code_len <= 65535. */
+typedef struct {
+  uint32_t tile_rows;       /* TR rows per tile [16] */
+  uint32_t tile_cols;       /* TC columns per tile [512] */
+  uint32_t chunks_per_tile; /* S column-strip chunks per tile [64] */
+  uint32_t max_code_len;    /* L, longest code in bits [12] */
+} nwc_params;
+
+/* Everything a device call needs, read from a validated blob. */
+typedef struct {
+  uint64_t rows, cols;             /* N, K */
+  uint64_t blob_bytes;             /* total blob size */
+  uint32_t tile_rows, tile_cols, chunks_per_tile, max_code_len;
+  uint64_t n_tiles, n_chunks;
+  uint64_t raw_ld;                 /* raw-plane row stride in bytes */
+  uint64_t stream_words;           /* 32-bit words of exponent codes */
+  uint64_t off_code_len, off_table, off_tile_words, off_chunk_bits, off_raw, off_stream;
+  uint32_t max_tile_words;         /* largest single-tile stream, in words */
+  uint32_t n_symbols;              /* distinct exponent values present */
+  uint64_t payload_bits;           /* sum of all chunk lengths */
+  uint8_t code_len[256];           /* code length per exponent value */
+} nwc_info;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *nwc_status_str(nwc_status s);
+
+/* Upper bound on the blob size of any rows x cols matrix with parameters p
+ * (NULL = defaults).  Host only, synchronous. */
+nwc_status nwc_encode_bound(uint64_t rows, uint64_t cols, const nwc_params *p,
+                            size_t *max_bytes);
+
+/* Encode W (host, rows x cols BF16 patterns, row stride ld >= cols elements)
+ * into blob (host, capacity cap bytes); *used receives the blob size.
+ * Steps (pages above): split each weight into raw byte and exponent, count
+ * exponents over the tensor, build optimal code lengths <= max_code_len by
+ * package-merge and canonical codes from them, write each tile's chunks in
+ * order, record offsets, and write the decode table.  A pure function of
+ * (W, shape, p): identical inputs give identical bytes.  Multithreaded on the
+ * host; no device work.  Errors: INVALID_ARG (bad shape/params/NULL),
+ * BUFFER_TOO_SMALL (then *used holds the needed size). */
+nwc_status nwc_encode(const uint16_t *w, uint64_t rows, uint64_t cols, uint64_t ld,
+                      const nwc_params *p, void *blob, size_t cap, size_t *used);
+
+/* Parse and validate a host blob and fill *info.  Checks the header, section
+ * layout, that the code lengths form a prefix code <= max_code_len, that the
+ * decode table matches the lengths, and that tile offsets agree with the
+ * chunk lengths.  Does not decode the stream.  Host only.
+ * Errors: INVALID_ARG (NULL), BAD_FORMAT. */
+nwc_status nwc_inspect(const void *blob, size_t bytes, nwc_info *info);
+
+/* Standalone decode (pages: "Dequantization and embedding lookup"): write
+ * the exact original BF16 bits of W into w_dev (device, rows x cols, row
+ * stride ld >= cols elements).  Reads the compressed bytes once and writes
+ * 2 bytes per weight.  Async on `stream`.
+ * Errors: INVALID_ARG, ALIGNMENT (w_dev not 16-byte aligned or ld % 8), HIP. */
+nwc_status nwc_decode(const nwc_info *info, const void *blob_dev, uint16_t *w_dev,
+                      uint64_t ld, void *stream);
+
+/* Workspace bytes needed by nwc_gemv (batch = 1) or nwc_gemm_skinny
+ * (batch 2..16) for this blob: FP32 partial sums, one per (column tile,
+ * batch row, output row). */
+nwc_status nwc_workspace_size(const nwc_info *info, int batch, size_t *bytes);
+
+/* Fused decode-GEMV (pages: "Fused kernel"; Unweight "Direct GPU
+ * Decompression"): y = W x with x (device, cols BF16) and y (device, rows
+ * entries of y_type).  Weights are decoded in registers and LDS and never
+ * written to memory; products accumulate in FP32 in a fixed order.  ws is a
+ * device workspace of at least nwc_workspace_size(info, 1) bytes whose
+ * contents need not be initialised.  x and y must not alias.  Async.
+ * Errors: INVALID_ARG, BUFFER_TOO_SMALL (ws), ALIGNMENT, HIP. */
+nwc_status nwc_gemv(const nwc_info *info, const void *blob_dev, const uint16_t *x_dev,
+                    void *y_dev, nwc_out_type y_type, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Skinny decode-GEMM for batch 2..16: Y[b, n] = sum_k X[b, k] W[n, k] with X
+ * (device, batch x cols, row stride ldx) and Y (device, batch x rows, row
+ * stride ldy, y_type).  Same decode as nwc_gemv; FP32 accumulation.  Async.
+ * Errors: INVALID_ARG (batch outside 2..16), BUFFER_TOO_SMALL, ALIGNMENT, HIP. */
+nwc_status nwc_gemm_skinny(const nwc_info *info, const void *blob_dev, const uint16_t *X_dev,
+                           uint64_t ldx, int batch, void *Y_dev, uint64_t ldy,
+                           nwc_out_type y_type, void *ws, size_t ws_bytes, void *stream);
+
+/* Uncompressed comparator: the same GEMV on a plain BF16 matrix (device,
+ * rows x cols, row stride ld), with the same tiling, summation order and
+ * workspace layout (nwc_workspace_size of a blob of that shape with default
+ * parameters, or nwc_bf16_workspace_size).  Async. */
+nwc_status nwc_bf16_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
+nwc_status nwc_gemv_bf16(const uint16_t *w_dev, uint64_t rows, uint64_t cols, uint64_t ld,
+                         const uint16_t *x_dev, void *y_dev, nwc_out_type y_type, void *ws,
+                         size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NWC_H */

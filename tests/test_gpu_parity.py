@@ -1,0 +1,305 @@
+"""GPU parity of libnwc's HIP kernels against the CPU oracle (MI355X only).
+
+Bars:
+* decode: bit-exact against the original BF16 bits;
+* GEMV / skinny GEMM: per output |y - y_oracle| <= 2^-10 * sum|w x| (FP32
+  output), plus 2^-8 * |y_oracle| for BF16 output (one final rounding), with
+  y_oracle and sum|w x| from the oracle's FP64 products;
+* repeated calls give bitwise-identical results.
+Small cases compare every output; full-size workloads compare sampled rows,
+which the oracle computes one by one.
+"""
+import functools
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+import decode_gemv_byte_amd as nwc  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _say(msg):
+    print("[gpu-case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class Blob:
+    def __init__(self, w: np.ndarray, params=None):
+        self.w = w
+        self.host = nwc.nwc_encode(w, params)
+        self.info = nwc.nwc_inspect(self.host)
+        self.dev = dev(self.host)
+
+    def ws(self, batch=1):
+        return torch.empty(nwc.nwc_workspace_size(self.info, batch), dtype=torch.uint8, device="cuda")
+
+
+@functools.lru_cache(maxsize=None)
+def _w(cid, name, layer=0):
+    return workloads.weights(cid, name, layer=layer)
+
+
+def _check_y(y_gpu, y_ref, a_ref, out_f32, what):
+    y_gpu = np.asarray(y_gpu, np.float64)
+    tol = 2.0 ** -10 * a_ref
+    if not out_f32:
+        tol = tol + 2.0 ** -8 * np.abs(y_ref)
+    err = np.abs(y_gpu - y_ref)
+    bad = np.flatnonzero(~(err <= tol))
+    assert bad.size == 0, "%s: %d/%d outside tolerance, first %s: got %r want %r tol %r" % (
+        what, bad.size, err.size, bad[:5], y_gpu[bad[:5]], y_ref[bad[:5]], tol[bad[:5]])
+
+
+def _to_f64(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def _gemv(blob: Blob, x: np.ndarray, out_f32: bool):
+    xd = dev(x)
+    y = torch.empty(blob.info.rows, dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+    nwc.nwc_gemv(blob.info, blob.dev, xd, y, blob.ws())
+    torch.cuda.synchronize()
+    return y
+
+
+# ----------------------------------------------------------------- decode --
+
+def _special(name):
+    rng = np.random.default_rng(5)
+    return {
+        "cfg1": lambda: _w(1, "w"),
+        "all_patterns": workloads.all_patterns,
+        "127x1001": lambda: workloads.gaussian_bits((127, 1001), 0.02, 4),
+        "1x1": lambda: workloads.gaussian_bits((1, 1), 0.02, 1),
+        "1000x256": lambda: workloads.gaussian_bits((1000, 256), 0.02, 7),
+        "nan_payloads": lambda: (0x7F80 | rng.integers(1, 128, (33, 64)) |
+                                 (rng.integers(0, 2, (33, 64)) << 15)).astype(np.uint16),
+        "subnormal": lambda: (rng.integers(1, 128, (48, 72)) | (rng.integers(0, 2, (48, 72)) << 15)).astype(np.uint16),
+        "one_symbol": lambda: (0x3C00 | rng.integers(0, 128, (50, 64))).astype(np.uint16),
+        "random_bits": lambda: workloads.random_bits((300, 264), 6),
+        "wide_odd": lambda: workloads.gaussian_bits((40, 3000), 0.05, 8),
+    }[name]()
+
+
+DECODE_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=8)), ("cfg1", dict(tile_rows=32)),
+                ("cfg1", dict(tile_rows=5, tile_cols=24, chunks_per_tile=3, max_code_len=11)),
+                ("all_patterns", None), ("127x1001", None), ("1x1", None), ("1000x256", None),
+                ("nan_payloads", None), ("subnormal", None), ("one_symbol", None), ("random_bits", None),
+                ("wide_odd", None), ("wide_odd", dict(tile_rows=3, tile_cols=7, chunks_per_tile=7, max_code_len=10))]
+
+
+@pytest.mark.parametrize("name,params", DECODE_CASES)
+def test_decode_bit_exact(name, params):
+    w = _special(name)
+    _say("decode %s %s %s" % (name, w.shape, params))
+    b = Blob(w, params)
+    out = torch.full(w.shape, 0x5A5A, dtype=torch.int16, device="cuda")
+    nwc.nwc_decode(b.info, b.dev, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, w)
+
+
+def test_decode_padded_leading_dimension():
+    w = _special("127x1001")
+    b = Blob(w)
+    for ld in (1008, 1013):           # vector path (ld % 8 == 0) and scalar path
+        _say("decode ld=%d" % ld)
+        out = torch.full((w.shape[0], ld), 0x1234, dtype=torch.int16, device="cuda")
+        nwc.nwc_decode(b.info, b.dev, out, ld=ld)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got[:, :1001], w)
+        assert np.all(got[:, 1001:] == 0x1234)     # nothing written past the row
+
+
+def test_decode_oracle_written_blob():
+    # the GPU decoder follows the format, not just the library's encoder
+    w = _w(1, "w")
+    host = oracle.encode(w, 16, 512, 64, 12)
+    info = nwc.nwc_inspect(host)
+    out = torch.empty(w.shape, dtype=torch.int16, device="cuda")
+    nwc.nwc_decode(info, dev(host), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), w)
+
+
+# ------------------------------------------------------------------- GEMV --
+
+GEMV_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=8)), ("cfg1", dict(tile_rows=32)),
+              ("cfg1", dict(tile_rows=5, tile_cols=24, chunks_per_tile=3, max_code_len=11)),
+              ("127x1001", None), ("1x1", None), ("1000x256", None), ("subnormal", None),
+              ("one_symbol", None), ("wide_odd", None)]
+
+
+@pytest.mark.parametrize("out_f32", [False, True])
+@pytest.mark.parametrize("name,params", GEMV_CASES)
+def test_gemv_small(name, params, out_f32):
+    w = _special(name)
+    x = workloads.gaussian_bits((w.shape[1],), 1.0, 11)
+    _say("gemv %s %s %s f32=%s" % (name, w.shape, params, out_f32))
+    b = Blob(w, params)
+    y = _gemv(b, x, out_f32)
+    y_ref, a_ref = oracle.gemv(w, x)
+    _check_y(_to_f64(y), y_ref, a_ref, out_f32, name)
+
+
+def test_gemv_subnormal_products_kept():
+    # every weight subnormal and x = 1: FP32 keeps the exact sums (no flush)
+    rng = np.random.default_rng(3)
+    w = rng.integers(1, 128, (64, 512)).astype(np.uint16)
+    x = np.full(512, 0x3F80, np.uint16)
+    b = Blob(w)
+    y = _gemv(b, x, True)
+    y_ref, a_ref = oracle.gemv(w, x)
+    assert np.all(y_ref > 0)
+    _check_y(_to_f64(y), y_ref, a_ref, True, "subnormal")
+
+
+def test_gemv_deterministic():
+    w = _w(2, "q")
+    x = workloads.activations(2, "q")[0]
+    b = Blob(w)
+    y1 = _gemv(b, x, True).cpu().numpy()
+    y2 = _gemv(b, x, True).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "gate", "up", "down"])
+def test_gemv_qwen3_4b_layer_full(name):
+    w = _w(2, name)
+    x = workloads.activations(2, name)[0]
+    _say("gemv workload 2 %s %s" % (name, w.shape))
+    b = Blob(w)
+    y_ref, a_ref = oracle.gemv(w, x)
+    for out_f32 in (False, True):
+        _check_y(_to_f64(_gemv(b, x, out_f32)), y_ref, a_ref, out_f32, name)
+
+
+def _sample_rows(n, k=512, seed=0):
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([rng.choice(n, min(k, n), replace=False), [0, n - 1]]))
+    return idx
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "gate", "up", "down"])
+@pytest.mark.parametrize("layer", [0, 31])
+def test_gemv_llama31_8b_step_sampled(name, layer):
+    w = workloads.weights(3, name, layer=layer)
+    x = workloads.activations(3, name, layer=layer)[0]
+    _say("gemv workload 3 layer %d %s %s" % (layer, name, w.shape))
+    b = Blob(w)
+    y = _to_f64(_gemv(b, x, False))
+    idx = _sample_rows(w.shape[0])
+    y_ref, a_ref = oracle.gemv_rows(w, x, idx)
+    _check_y(y[idx], y_ref, a_ref, False, name)
+
+
+def test_gemv_lm_head_sampled():
+    w = _w(5, "lm_head")
+    x = workloads.activations(5, "lm_head")[0]
+    _say("gemv workload 5 lm_head %s" % (w.shape,))
+    b = Blob(w)
+    idx = _sample_rows(w.shape[0], 1024)
+    y_ref, a_ref = oracle.gemv_rows(w, x, idx)
+    for out_f32 in (False, True):
+        y = _to_f64(_gemv(b, x, out_f32))
+        _check_y(y[idx], y_ref, a_ref, out_f32, "lm_head")
+        assert np.all(np.isfinite(y))
+
+
+# ------------------------------------------------------------ skinny GEMM --
+
+def _gemm(blob: Blob, X: np.ndarray, out_f32: bool):
+    Xd = dev(X)
+    Y = torch.empty((X.shape[0], blob.info.rows), dtype=torch.float32 if out_f32 else torch.bfloat16,
+                    device="cuda")
+    nwc.nwc_gemm_skinny(blob.info, blob.dev, Xd, Y, blob.ws(X.shape[0]))
+    torch.cuda.synchronize()
+    return Y
+
+
+@pytest.mark.parametrize("batch", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("name,params", [("cfg1", None), ("127x1001", None), ("1000x256", None),
+                                         ("cfg1", dict(tile_rows=8)), ("wide_odd", None)])
+def test_gemm_small(name, params, batch):
+    w = _special(name)
+    X = workloads.gaussian_bits((batch, w.shape[1]), 1.0, 12)
+    _say("gemm %s %s batch %d %s" % (name, w.shape, batch, params))
+    b = Blob(w, params)
+    Y_ref, A_ref = oracle.gemm(w, X)
+    for out_f32 in (False, True):
+        Y = _to_f64(_gemm(b, X, out_f32))
+        for beta in range(batch):
+            _check_y(Y[beta], Y_ref[beta], A_ref[beta], out_f32, "%s b%d" % (name, beta))
+
+
+@pytest.mark.parametrize("batch", [2, 4, 8, 16])
+@pytest.mark.parametrize("name", ["w_4096x14336", "w_14336x4096"])
+def test_gemm_skinny_workload_sampled(name, batch):
+    w = _w(4, name)
+    X = workloads.activations(4, name, batch=batch)
+    _say("gemm workload 4 %s batch %d" % (name, batch))
+    b = Blob(w)
+    Y = _to_f64(_gemm(b, X, False))
+    idx = _sample_rows(w.shape[0], 256, seed=batch)
+    Y_ref, A_ref = oracle.gemm(np.ascontiguousarray(w[idx]), X)
+    for beta in range(batch):
+        _check_y(Y[beta][idx], Y_ref[beta], A_ref[beta], False, "%s b%d" % (name, beta))
+
+
+def test_gemm_lm_head_batch8_sampled():
+    w = _w(5, "lm_head")
+    X = workloads.activations(5, "lm_head", batch=8)
+    b = Blob(w)
+    Y = _to_f64(_gemm(b, X, False))
+    idx = _sample_rows(w.shape[0], 256, seed=8)
+    Y_ref, A_ref = oracle.gemm(np.ascontiguousarray(w[idx]), X)
+    for beta in range(8):
+        _check_y(Y[beta][idx], Y_ref[beta], A_ref[beta], False, "lm_head b%d" % beta)
+
+
+def test_gemm_deterministic():
+    w = _w(4, "w_4096x14336")
+    X = workloads.activations(4, "w_4096x14336", batch=16)
+    b = Blob(w)
+    a = _gemm(b, X, True).cpu().numpy()
+    c = _gemm(b, X, True).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+# ------------------------------------------------------ BF16 comparator ----
+
+@pytest.mark.parametrize("cid,name", [(1, "w"), (2, "q"), (2, "down")])
+def test_gemv_bf16_comparator(cid, name):
+    w = _w(cid, name)
+    x = workloads.activations(cid, name)[0]
+    wd = dev(w)
+    xd = dev(x)
+    y = torch.empty(w.shape[0], dtype=torch.float32, device="cuda")
+    ws = torch.empty(nwc.nwc_bf16_workspace_size(*w.shape), dtype=torch.uint8, device="cuda")
+    nwc.nwc_gemv_bf16(wd, xd, y, ws)
+    torch.cuda.synchronize()
+    y_ref, a_ref = oracle.gemv(w, x)
+    _check_y(_to_f64(y), y_ref, a_ref, True, name)
+
+
+def test_native_library_is_in_tree():
+    assert os.path.dirname(os.path.abspath(nwc.LIB_PATH)).startswith(ROOT)
+    maps = open("/proc/self/maps").read()
+    assert nwc.LIB_PATH in maps

@@ -1,0 +1,195 @@
+"""Host side of libnwc on the CPU: exported symbols, encoder byte identity with
+the oracle, blob validation, and argument checks that must fail before any
+device work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import decode_gemv_byte_amd as nwc
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nwc.h")
+
+DEFAULT = dict(tile_rows=16, tile_cols=512, chunks_per_tile=64, max_code_len=12)
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nwc_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", nwc.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (nwc_[a-z0-9_]+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(ctypes.CDLL(nwc.LIB_PATH), n)
+    assert set(nwc.EXPORTS) == set(names)
+
+
+def test_status_strings():
+    for s in range(0, -7, -1):
+        assert nwc.nwc_status_str(s).startswith("NWC_")
+    assert nwc.nwc_status_str(-99) == "NWC_ERR_UNKNOWN"
+
+
+def _oracle_blob(w, p):
+    q = dict(DEFAULT)
+    q.update(p or {})
+    return oracle.encode(w, q["tile_rows"], q["tile_cols"], q["chunks_per_tile"], q["max_code_len"])
+
+
+GEOMS = [None, dict(tile_rows=8), dict(tile_rows=32), dict(tile_rows=5, tile_cols=24, chunks_per_tile=3,
+                                                              max_code_len=11),
+         dict(tile_rows=3, tile_cols=7, chunks_per_tile=7, max_code_len=10), dict(max_code_len=8)]
+
+
+@pytest.mark.parametrize("geom", GEOMS)
+@pytest.mark.parametrize("name", ["cfg1", "all_patterns", "127x1001", "subnormal", "one_symbol", "1x1",
+                                  "random_bits"])
+def test_encoder_bytes_equal_oracle(name, geom):
+    rng = np.random.default_rng(5)
+    w = {
+        "cfg1": lambda: workloads.weights(1, "w"),
+        "all_patterns": workloads.all_patterns,
+        "127x1001": lambda: workloads.gaussian_bits((127, 1001), 0.02, 4),
+        "subnormal": lambda: (rng.integers(1, 128, (48, 70)) | (rng.integers(0, 2, (48, 70)) << 15)).astype(np.uint16),
+        "one_symbol": lambda: (0x3C00 | rng.integers(0, 128, (50, 60))).astype(np.uint16),
+        "1x1": lambda: workloads.gaussian_bits((1, 1), 0.02, 1),
+        "random_bits": lambda: workloads.random_bits((300, 257), 6),
+    }[name]()
+    assert np.array_equal(nwc.nwc_encode(w, geom), _oracle_blob(w, geom))
+
+
+@pytest.mark.parametrize("cid,name", [(2, "q"), (2, "down"), (3, "gate"), (4, "w_4096x14336"), (5, "lm_head")])
+def test_encoder_bytes_equal_oracle_workload_slices(cid, name):
+    w = workloads.weights(cid, name, rows=slice(0, 512))
+    assert np.array_equal(nwc.nwc_encode(w), _oracle_blob(w, None))
+
+
+def test_encoder_strided_input():
+    big = workloads.gaussian_bits((40, 300), 0.02, 3)
+    view = big[:, 10:250]
+    assert not view.flags.c_contiguous
+    assert np.array_equal(nwc.nwc_encode(view), _oracle_blob(np.ascontiguousarray(view), None))
+
+
+def test_inspect_matches_oracle_header():
+    w = workloads.weights(1, "w")
+    blob = nwc.nwc_encode(w)
+    info = nwc.nwc_inspect(blob)
+    h = oracle.header(blob)
+    for k in ("rows", "cols", "tile_rows", "tile_cols", "chunks_per_tile", "max_code_len", "n_tiles",
+              "n_chunks", "raw_ld", "stream_words", "off_code_len", "off_table", "off_tile_words",
+              "off_chunk_bits", "off_raw", "off_stream"):
+        assert getattr(info, k) == h[k], k
+    assert info.blob_bytes == h["total_bytes"] == blob.size
+    sec = oracle.sections(blob)
+    assert info.max_tile_words == int(np.diff(sec["tile_words"].astype(np.int64)).max())
+    assert info.payload_bits == int(sec["chunk_bits"].astype(np.int64).sum())
+    assert bytes(info.code_len) == bytes(sec["code_len"])
+    e, _ = oracle.split(w)
+    assert info.n_symbols == int((oracle.histogram(e) > 0).sum())
+
+
+def _corrupt(blob):
+    h = oracle.header(blob)
+    out = {}
+    b = blob.copy(); b[0] ^= 1; out["magic"] = b
+    b = blob.copy(); b[4] = 9; out["version"] = b
+    out["truncated"] = blob[: blob.size - 300].copy()
+    b = blob.copy(); b[h["off_table"] + 40] ^= 0x10; out["table"] = b
+    b = blob.copy(); b[h["off_tile_words"] + 8] ^= 0x01; out["tile_words"] = b
+    b = blob.copy(); b[h["off_chunk_bits"] + 1] ^= 0x40; out["chunk_bits_range"] = b
+    b = blob.copy(); lens = b[h["off_code_len"]: h["off_code_len"] + 256]
+    nz = np.flatnonzero(lens)
+    lens[nz[0]] = 1; lens[nz[1]] = 1; lens[nz[2]] = 1; out["kraft"] = b
+    b = blob.copy(); b[h["off_code_len"] + nz[0]] = 13; out["too_long"] = b
+    b = blob.copy(); b[8] ^= 0x01; out["rows"] = b
+    b = blob.copy(); b[28] = 0x07; out["geometry"] = b
+    b = blob.copy(); b[44] = 1; out["flags"] = b
+    b = blob.copy(); b[40] = 2; out["table_kind"] = b
+    return out
+
+
+def test_inspect_rejects_corruption():
+    w = workloads.gaussian_bits((127, 1001), 0.02, 4)
+    blob = nwc.nwc_encode(w)
+    for name, bad in _corrupt(blob).items():
+        with pytest.raises(nwc.NwcError) as ei:
+            nwc.nwc_inspect(bad)
+        assert ei.value.status == nwc.NWC_ERR_BAD_FORMAT, name
+        assert oracle.validate(bad) != 0, name
+
+
+def test_encode_errors():
+    w = workloads.gaussian_bits((10, 20), 0.02, 1)
+    for p in [dict(tile_cols=500), dict(max_code_len=13), dict(max_code_len=7),
+              dict(tile_rows=4096, tile_cols=4096, chunks_per_tile=1)]:
+        with pytest.raises(nwc.NwcError) as ei:
+            nwc.nwc_encode(w, p)
+        assert ei.value.status == nwc.NWC_ERR_INVALID_ARG
+    # capacity too small reports the needed size
+    need = nwc.nwc_encode(w).size
+    buf = np.zeros(need - 1, np.uint8)
+    used = ctypes.c_size_t(0)
+    st = nwc._lib.nwc_encode(w.ctypes.data, 10, 20, 20, None, buf.ctypes.data, buf.size, ctypes.byref(used))
+    assert st == nwc.NWC_ERR_BUFFER_TOO_SMALL and used.value == need
+    st = nwc._lib.nwc_encode(None, 10, 20, 20, None, buf.ctypes.data, buf.size, ctypes.byref(used))
+    assert st == nwc.NWC_ERR_INVALID_ARG
+    assert nwc._lib.nwc_encode(w.ctypes.data, 10, 20, 19, None, buf.ctypes.data, buf.size,
+                               ctypes.byref(used)) == nwc.NWC_ERR_INVALID_ARG
+    assert nwc.nwc_encode_bound(10, 20) >= need
+
+
+def test_workspace_sizes():
+    blob = nwc.nwc_encode(workloads.gaussian_bits((100, 1500), 0.02, 2))
+    info = nwc.nwc_inspect(blob)
+    assert nwc.nwc_workspace_size(info, 1) == 3 * 100 * 4
+    assert nwc.nwc_workspace_size(info, 16) == 3 * 16 * 100 * 4
+    for bad in (0, 17):
+        with pytest.raises(nwc.NwcError):
+            nwc.nwc_workspace_size(info, bad)
+    assert nwc.nwc_bf16_workspace_size(100, 1500) == 3 * 100 * 4
+
+
+def test_device_calls_validate_before_launch():
+    # Every failure below is detected on the host, so these run without a GPU.
+    blob = nwc.nwc_encode(workloads.gaussian_bits((64, 512), 0.02, 2))
+    info = nwc.nwc_inspect(blob)
+    L = nwc._lib
+    ref = ctypes.byref(info)
+    A = 0x10000          # 256-aligned fake device addresses, never dereferenced
+    ws = nwc.nwc_workspace_size(info, 1)
+    assert L.nwc_gemv(None, A, A, A, 0, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, None, A, A, 0, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, None, A, 0, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, A, A, 0, None, ws, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, A, A, 7, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, A, A, 0, A, ws - 4, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
+    assert L.nwc_gemv(ref, A + 16, A, A, 0, A, ws, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv(ref, A, A, A + 1, 0, A, ws, None) == nwc.NWC_ERR_ALIGNMENT
+    ws16 = nwc.nwc_workspace_size(info, 16)
+    for batch in (0, 1, 17):
+        assert L.nwc_gemm_skinny(ref, A, A, 512, batch, A, 64, 0, A, ws16, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemm_skinny(ref, A, A, 100, 4, A, 64, 0, A, ws16, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_decode(ref, A, None, 512, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_decode(ref, A, A, 100, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_decode(ref, A + 8, A, 512, None) == nwc.NWC_ERR_ALIGNMENT
+    bad = nwc.nwc_info.from_buffer_copy(info)
+    bad.n_tiles += 1
+    assert L.nwc_gemv(ctypes.byref(bad), A, A, A, 0, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
+    wsb = nwc.nwc_bf16_workspace_size(64, 512)
+    assert L.nwc_gemv_bf16(A, 64, 512, 500, A, A, 0, A, wsb, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_bf16(A, 64, 500, 512, A, A, 0, A, wsb, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_bf16(A, 64, 512, 512, A, A, 0, A, wsb - 1, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
