@@ -189,26 +189,35 @@ def nwc_decode(info: nwc_info, blob_dev, w_dev, ld: Optional[int] = None, stream
     _check(_lib.nwc_decode(ctypes.byref(info), _dptr(blob_dev), _dptr(w_dev), ld, _stream(stream)), "nwc_decode")
 
 
-def nwc_gemv(info: nwc_info, blob_dev, x_dev, y_dev, ws, stream=None):
-    """y = W x; y_dev float32 or bfloat16 (rows); ws a device byte tensor."""
+def _ws(ws):
+    if ws is None:
+        return ctypes.c_void_p(None), 0
+    return _dptr(ws), ws.numel() * ws.element_size()
+
+
+def nwc_gemv(info: nwc_info, blob_dev, x_dev, y_dev, ws=None, stream=None):
+    """y = W x; y_dev float32 or bfloat16 (rows); ws a device byte tensor of
+    nwc_workspace_size(info, 1) bytes, or None when that size is 0."""
+    wp, wn = _ws(ws)
     _check(_lib.nwc_gemv(ctypes.byref(info), _dptr(blob_dev), _dptr(x_dev), _dptr(y_dev), _ytype(y_dev),
-                         _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "nwc_gemv")
+                         wp, wn, _stream(stream)), "nwc_gemv")
 
 
-def nwc_gemm_skinny(info: nwc_info, blob_dev, X_dev, Y_dev, ws, stream=None):
+def nwc_gemm_skinny(info: nwc_info, blob_dev, X_dev, Y_dev, ws=None, stream=None):
     """Y[b] = W X[b] for X_dev [batch, cols] and Y_dev [batch, rows]."""
     batch = int(X_dev.shape[0])
+    wp, wn = _ws(ws)
     _check(_lib.nwc_gemm_skinny(ctypes.byref(info), _dptr(blob_dev), _dptr(X_dev), int(X_dev.stride(0)), batch,
-                                _dptr(Y_dev), int(Y_dev.stride(0)), _ytype(Y_dev), _dptr(ws),
-                                ws.numel() * ws.element_size(), _stream(stream)), "nwc_gemm_skinny")
+                                _dptr(Y_dev), int(Y_dev.stride(0)), _ytype(Y_dev), wp, wn, _stream(stream)),
+           "nwc_gemm_skinny")
 
 
-def nwc_gemv_bf16(w_dev, x_dev, y_dev, ws, stream=None):
+def nwc_gemv_bf16(w_dev, x_dev, y_dev, ws=None, stream=None):
     """Uncompressed comparator: y = W x with W a device BF16 matrix [rows, cols]."""
     rows, cols = int(w_dev.shape[0]), int(w_dev.shape[1])
+    wp, wn = _ws(ws)
     _check(_lib.nwc_gemv_bf16(_dptr(w_dev), rows, cols, int(w_dev.stride(0)), _dptr(x_dev), _dptr(y_dev),
-                              _ytype(y_dev), _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "nwc_gemv_bf16")
+                              _ytype(y_dev), wp, wn, _stream(stream)), "nwc_gemv_bf16")
 
 
 def info_dict(info: nwc_info) -> dict:

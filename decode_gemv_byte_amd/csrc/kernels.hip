@@ -10,25 +10,31 @@
 // "A bandwidth ceiling, not a promise").
 //
 // Kernel structure (MI355X-specific; not the pages' NVIDIA design):
-//  * A wavefront (64 lanes) owns one tile of TR rows x 512 columns at a time.
-//    Lane l owns chunk l: all TR rows of columns [8l, 8l+8), decoded row by
-//    row.  Raw-plane loads are 8 bytes per lane per row, 512 contiguous bytes
-//    per wavefront per row.
-//  * The tile's exponent stream (word aligned, about 2.7 KB) is staged in LDS
-//    with coalesced loads; each lane finds its chunk's start bit by a
-//    wavefront prefix sum over the chunk lengths.
-//  * The 4096-entry decode table lives in LDS (16 KB per workgroup).  One
-//    lookup of the 12-bit window yields two exponents already placed at BF16
-//    bit positions 7..14 and 23..30; a byte permute spreads two raw bytes and
-//    one bit-field insert builds two BF16 weights in one dword.
-//  * B = 1: v_dot2c_f32_bf16 accumulates into one FP32 register per row
-//    (subnormal inputs are kept); a transposed butterfly reduces the TR row
-//    sums across lanes; per-(column tile, row) partials go to the workspace
-//    and a second kernel adds them in column-tile order.
+//  * A wavefront (64 lanes) decodes one tile of TR rows x 512 columns at a
+//    time.  Lane l owns chunk l: all TR rows of columns [8l, 8l+8), decoded
+//    row by row.  Raw-plane loads are 8 bytes per lane per row, 512
+//    contiguous bytes per wavefront per row.
+//  * All global loads of a tile are issued before the first use (rows past
+//    the matrix edge are clamped, not branched around), so a tile costs one
+//    memory latency.  The tile's exponent stream (word aligned, about 2.7 KB)
+//    goes straight to LDS with global_load_lds_dwordx4; each lane finds its
+//    chunk's start bit by a wavefront prefix sum over the chunk lengths.
+//  * Each lane keeps a 64-bit bit buffer in two registers plus the next word,
+//    so one decode step costs one LDS lookup: the 4096-entry decode table
+//    (16 KB per workgroup) maps the next 12 bits to two exponents already at
+//    BF16 bit positions 7..14 and 23..30.  A byte permute spreads two raw
+//    bytes and one bit-field insert builds two BF16 weights in one dword.
+//  * B = 1: v_dot2c_f32_bf16 accumulates one FP32 register per row (subnormal
+//    inputs are kept).  A workgroup owns whole row blocks and splits their
+//    column tiles across its wavefronts; a transposed butterfly reduces each
+//    wavefront's row sums across lanes and the workgroup adds the wavefronts'
+//    sums through LDS in a fixed order, so y is written once, by one kernel.
 //  * B = 2..16: decoded BF16 rows go to LDS and feed
-//    v_mfma_f32_16x16x32_bf16 (A = 16 weight rows x 32 columns, B = the
-//    batch rows of X padded to 16).
-//  * Every read from the blob is clamped to its sections.
+//    v_mfma_f32_16x16x32_bf16 (A = 16 weight rows x 32 columns, B = the batch
+//    rows of X padded to 16); the same workgroup split and LDS reduction.
+//  * Shapes or geometries outside the fast path use one-symbol-at-a-time
+//    kernels with an FP32 partial-sum workspace and a separate reduction.
+//  * Every global read from the blob is clamped to its sections.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -44,11 +50,11 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kThreads = kWave * kWavesPerBlock;
+constexpr int kMaxWaves = 16;      // wavefronts per workgroup, fused kernels
+constexpr int kGenericWaves = 4;   // wavefronts per workgroup, generic kernels
 constexpr int kTable = 4096;
-constexpr int kGuardWords = 4;
 constexpr uint32_t kExpMask = 0x7F807F80u;  // exponent bits of two packed BF16
+constexpr int kMfmaRowPad = 512 + 8;        // bf16 per LDS row of a decoded tile
 
 struct BlobDev {
   const uint32_t* table;
@@ -57,25 +63,65 @@ struct BlobDev {
   const uint8_t* raw;
   const uint32_t* stream;
   uint64_t rows, cols, raw_ld;
-  uint64_t n_tiles;
+  uint64_t n_tiles, n_tr;
   uint32_t n_tc, tr, tc, s, v;
-  uint32_t stream_words;
-  uint32_t buf_words;  // LDS stream buffer per wavefront (>= max tile words + guard)
+  uint32_t stream_words;  // words of codes; 4 zero guard words follow in the blob
+  uint32_t buf_words;     // LDS stream buffer per wavefront
+};
+
+// How a fused launch splits the matrix: a work item is `rb` row blocks; its
+// workgroup has rb * nw wavefronts and wavefront (i, j) takes column tiles
+// j, j + nw, ... of row block i.
+struct Split {
+  uint32_t nw, rb, waves;
+  uint64_t items;
 };
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Exclusive prefix sum of v across the 64 lanes.
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v) {
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t y = __shfl_up(incl, off, kWave);
-    if (lane_id() >= static_cast<uint32_t>(off)) incl += y;
-  }
-  return incl - v;
+// DPP move of v from a lane chosen by CTRL (0 where the source lane is
+// outside the row or the row is masked off).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, true));
 }
+constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143, kRowMirror = 0x140,
+              kRowHalfMirror = 0x141;
+
+// Exclusive prefix sum of v across the 64 lanes (DPP: shifts within rows of
+// 16 lanes, then row broadcasts).
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v) {
+  uint32_t s = v;
+  s += dpp<kRowShr + 1>(s);
+  s += dpp<kRowShr + 2>(s);
+  s += dpp<kRowShr + 4>(s);
+  s += dpp<kRowShr + 8>(s);
+  s += dpp<kRowBcast15, 0xA>(s);
+  s += dpp<kRowBcast31, 0xC>(s);
+  return s - v;
+}
+
+// Value of v in a partner lane whose lane index differs in bit M (M = 1..32),
+// for the butterflies below: quad permutes, half-row and row mirrors, a
+// 32-lane swizzle and, for bit 5, a lane permute through the LDS crossbar.
+template <int M>
+__device__ __forceinline__ float partner(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  uint32_t r;
+  if constexpr (M == 1) r = dpp<0xB1>(u);                 // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) r = dpp<0x4E>(u);            // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) r = dpp<kRowHalfMirror>(u);  // lane i <-> 7 - i within 8
+  else if constexpr (M == 8) r = dpp<kRowMirror>(u);      // lane i <-> 15 - i within 16
+  else if constexpr (M == 16) r = static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(u), 0x401F));
+  else r = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(static_cast<int>((lane_id() ^ 32u) << 2),
+                                                             static_cast<int>(u)));
+  return __builtin_bit_cast(float, r);
+}
+
+// Wait for every outstanding vector-memory load (including loads into LDS).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -83,56 +129,106 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Copy the decode table into LDS (whole workgroup).
+// Copy the decode table into LDS with 16-byte loads straight to LDS; the
+// caller synchronizes the workgroup.
 __device__ __forceinline__ void load_table(uint32_t* lds_table, const uint32_t* table) {
-  const uint4* src = reinterpret_cast<const uint4*>(table);
-  uint4* dst = reinterpret_cast<uint4*>(lds_table);
-  for (int i = threadIdx.x; i < kTable / 4; i += blockDim.x) dst[i] = src[i];
-}
-
-// Stage tile t's stream words into this wavefront's LDS buffer; returns the
-// number of words (clamped to the buffer and to the stream).
-__device__ __forceinline__ void stage_tile(const BlobDev& b, uint64_t t, uint32_t* buf) {
-  const uint32_t w0 = b.tile_words[t];
-  uint32_t w1 = b.tile_words[t + 1];
-  w1 = w1 < w0 ? w0 : w1;
-  uint32_t n = w1 - w0;
-  const uint32_t cap = b.buf_words - kGuardWords;
-  n = n > cap ? cap : n;
-  for (uint32_t i = lane_id(); i < n + kGuardWords; i += kWave) {
-    const uint32_t g = w0 + i;
-    buf[i] = (i < n && g < b.stream_words) ? b.stream[g] : 0u;
+  const uint32_t nthreads = blockDim.x;
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  for (uint32_t base = wave * kWave * 4; base < kTable; base += nthreads * 4) {
+    __builtin_amdgcn_global_load_lds(table + base + lane_id() * 4, lds_table + base, 16, 0, 0);
   }
-  wave_sync_lds();
+  wait_vmem();
 }
 
-// 64-bit window at bit q of the LDS buffer, shifted so bit q is bit 0.
-__device__ __forceinline__ uint32_t window_at(const uint32_t* buf, uint32_t q, uint32_t limit) {
-  uint32_t wi = q >> 5;
-  wi = wi > limit ? limit : wi;
-  const uint32_t lo = buf[wi], hi = buf[wi + 1];
-  return __builtin_amdgcn_alignbit(hi, lo, q);
-}
-
-// Decode the next two exponents at bit q: returns a dword with exponent 0 at
-// bits 7..14, exponent 1 at bits 23..30, and advances q.
-__device__ __forceinline__ uint32_t decode_pair(const uint32_t* tab, const uint32_t* buf, uint32_t& q,
-                                                uint32_t limit) {
-  const uint32_t win = window_at(buf, q, limit);
-  uint32_t ent = tab[win & 0xFFFu];
-  if (ent >> 31) {  // second code did not fit in the 12-bit window
-    const uint32_t l0 = ent & 0xFu;
-    const uint32_t ent2 = tab[(win >> l0) & 0xFFFu];
-    // the merged advance l0 + l1 can reach 24: it uses bits 0..4 (bits
-    // 4..6 are zero in table entries)
-    ent = (ent & 0x7F80u) | ((ent2 & 0x7F80u) << 16) | (l0 + ((ent2 >> 16) & 0xFu));
+// Issue the loads that bring tile t's stream words [a0, a0 + 256 * n) into
+// this wavefront's LDS buffer (a0 = first word rounded down to 4 words).
+// Sources past the stream's guard words are redirected to its start; those
+// LDS words are never read for a well-formed blob.
+__device__ __forceinline__ void stage_stream(const BlobDev& b, uint32_t a0, uint32_t n, uint32_t* buf) {
+  const uint32_t lane = lane_id();
+  if (lane < 4) buf[lane] = 0u;  // guard words before the stream
+  buf += 4;
+  for (uint32_t j = 0; j < n; j++) {
+    uint32_t g = a0 + 256 * j + 4 * lane;
+    g = g + 4 <= b.stream_words + 4 ? g : 0u;
+    __builtin_amdgcn_global_load_lds(b.stream + g, buf + 256 * j, 16, 0, 0);
   }
-  q += ent & 0x1Fu;
-  return ent;
 }
 
-// Two BF16 weights from the pair entry and 4 raw bytes; `hi` selects raw
-// bytes 2,3 instead of 0,1.
+// Number of 256-word blocks to stage for a tile [w0, w1): covers the bit
+// buffer's two words of look-ahead, capped by the buffer.
+__device__ __forceinline__ uint32_t stage_blocks(const BlobDev& b, uint32_t a0, uint32_t w1) {
+  uint32_t need = (w1 - a0 + 2 + 255) / 256;
+  const uint32_t cap = (b.buf_words - 4) / 256;
+  return need > cap ? cap : need;
+}
+
+// Bit reader over a wavefront's LDS stream buffer.  The buffer keeps 4 zero
+// guard words before the staged stream, so every start bit b >= 128.  State:
+// a 64-bit window (lo = word wi, hi = word wi + 1), the following word nxt,
+// and qm = (bit offset in lo) - 2, kept in [0, 32): the funnel shift by qm
+// then leaves the next 12 stream bits at bits 2..13, i.e. already scaled to a
+// byte address into the 4-byte-entry decode table at LDS address 0.
+struct Bits {
+  uint32_t lo, hi, nxt, qm, wi;
+  __device__ __forceinline__ void init(const uint32_t* buf, uint32_t bit) {
+    const uint32_t b2 = bit - 2;
+    wi = b2 >> 5;
+    qm = b2 & 31u;
+    lo = buf[wi];
+    hi = buf[wi + 1];
+    nxt = buf[wi + 2];
+  }
+  // window for the current qm, which may have run up to 55: both funnel
+  // shifts are computed next to the compare, so the select is the only step
+  // between the new position and the next table address
+  __device__ __forceinline__ uint32_t window() const {
+    const uint32_t a = __builtin_amdgcn_alignbit(hi, lo, qm);
+    const uint32_t b = __builtin_amdgcn_alignbit(nxt, hi, qm);
+    return qm >= 32 ? b : a;
+  }
+  // commit a position that may have crossed into the next word
+  __device__ __forceinline__ void settle(const uint32_t* buf) {
+    const bool c = qm >= 32;
+    lo = c ? hi : lo;
+    hi = c ? nxt : hi;
+    wi += c ? 1u : 0u;
+    qm &= 31u;
+    nxt = buf[wi + 2];
+  }
+  // Decode the next two exponents: returns a dword with exponent 0 at bits
+  // 7..14 and exponent 1 at bits 23..30.
+  __device__ __forceinline__ uint32_t pair(const uint32_t* tab, const uint32_t* buf) {
+    const uint32_t win = window();
+    settle(buf);
+    uint32_t ent = tab[(win & 0x3FFCu) >> 2];
+    // Rarely the second code does not fit in the 12-bit window.  The test is
+    // made for the whole wavefront, and inside the branch every lane does the
+    // second lookup and keeps it only if it needs it, so the common path has
+    // no exec-mask changes.
+    const bool single = static_cast<int32_t>(ent) < 0;
+    if (__builtin_amdgcn_ballot_w64(single)) {
+      const uint32_t l0 = ent & 0xFu;
+      const uint32_t ent2 = tab[((win >> l0) & 0x3FFCu) >> 2];
+      // merged advance l0 + l1 may reach 24: it occupies bits 0..4
+      const uint32_t merged = (ent & 0x7F80u) | ((ent2 & 0x7F80u) << 16) | (l0 + ((ent2 >> 16) & 0xFu));
+      ent = single ? merged : ent;
+    }
+    qm += ent & 0x1Fu;
+    return ent;
+  }
+  // One exponent (generic paths): returns it and advances.
+  __device__ __forceinline__ uint32_t one(const uint32_t* tab, const uint32_t* buf) {
+    const uint32_t win = window();
+    settle(buf);
+    const uint32_t ent = tab[(win & 0x3FFCu) >> 2];
+    qm += (ent >> 16) & 0xFu;
+    return (ent >> 7) & 0xFFu;
+  }
+};
+
+// Two BF16 weights from a pair entry and 4 raw bytes; `hi` selects raw bytes
+// 2,3 instead of 0,1.
 __device__ __forceinline__ uint32_t assemble(uint32_t ent, uint32_t raw4, bool hi) {
   const uint32_t spread = __builtin_amdgcn_perm(raw4, raw4, hi ? 0x03030202u : 0x01010000u);
   return (ent & kExpMask) | (spread & ~kExpMask);
@@ -150,206 +246,369 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Transposed butterfly: on entry every lane holds R partial sums (rows
-// 0..R-1); on exit lane l with (l & (64/R - 1)) == 0 holds the full sum of
-// row l / (64/R), summed in a fixed order.
-template <int R>
-__device__ __forceinline__ float reduce_rows(float (&v)[R]) {
-  const uint32_t lane = lane_id();
+__device__ __forceinline__ void store_y(void* y, uint64_t i, float v, int y_f32) {
+  if (y_f32)
+    static_cast<float*>(y)[i] = v;
+  else
+    static_cast<uint16_t*>(y)[i] = f32_to_bf16_rne(v);
+}
+
+// One level of the transposed butterfly: lanes with bit M set keep the upper
+// half of their sums and receive the partner's upper half; the others keep
+// the lower half.  Indices are compile-time, so no dynamic register indexing.
+// Partners differ in bit M and hold sums over disjoint lane sets, so after
+// all levels every row's sum covers all 64 lanes exactly once.
+template <int R, int HALF, int M>
+__device__ __forceinline__ void butterfly(float (&v)[R], uint32_t lane) {
+  const bool up = (lane & M) != 0;
 #pragma unroll
-  for (int half = R / 2, m = 32; half >= 1; half >>= 1, m >>= 1) {
-    const bool up = (lane & m) != 0;
-#pragma unroll
-    for (int i = 0; i < half; i++) {
-      const float keep = up ? v[half + i] : v[i];
-      const float send = up ? v[i] : v[half + i];
-      v[i] = keep + __shfl_xor(send, m, kWave);
-    }
+  for (int i = 0; i < HALF; i++) {
+    const float keep = up ? v[HALF + i] : v[i];
+    const float send = up ? v[i] : v[HALF + i];
+    v[i] = keep + partner<M>(send);
   }
-  float s = v[0];
-#pragma unroll
-  for (int m = 32 / R; m >= 1; m >>= 1) s += __shfl_xor(s, m, kWave);
+  if constexpr (HALF > 1) butterfly<R, HALF / 2, M / 2>(v, lane);
+}
+
+template <int M>
+__device__ __forceinline__ float allsum_low(float s) {
+  if constexpr (M >= 1) {
+    s += partner<M>(s);
+    return allsum_low<M / 2>(s);
+  }
   return s;
 }
 
+// Transposed butterfly: on entry every lane holds R partial sums (rows
+// 0..R-1); on exit lane l holds the full sum of row (l / (64/R)) % R (every
+// lane of a row's group holds it), added in a fixed order.
+template <int R>
+__device__ __forceinline__ float reduce_rows(float (&v)[R]) {
+  butterfly<R, R / 2, 32>(v, lane_id());
+  return allsum_low<32 / R>(v[0]);
+}
+
+// Everything one lane needs from global memory for one tile, loaded up front.
+template <int TR>
+struct TileIn {
+  uint2 raw[TR];
+  uint32_t cb, a0, w0;
+  uint64_t c0;
+  uint32_t nrows;
+  bool active;
+
+  __device__ __forceinline__ void load(const BlobDev& b, uint64_t ti, uint32_t tj, uint32_t* buf) {
+    const uint32_t lane = lane_id();
+    const uint64_t t = ti * b.n_tc + tj;
+    const uint64_t row0 = ti * TR;
+    nrows = static_cast<uint32_t>(umin64(TR, b.rows - row0));
+    c0 = static_cast<uint64_t>(tj) * 512 + lane * 8;
+    active = c0 < b.cols;
+    const uint64_t cc = active ? c0 : 0;
+    w0 = uniform(b.tile_words[t]);
+    const uint32_t w1 = uniform(b.tile_words[t + 1]);
+    a0 = w0 & ~3u;
+    stage_stream(b, a0, stage_blocks(b, a0, w1 < w0 ? w0 : w1), buf);
+    cb = b.chunk_bits[t * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < TR; r++) {
+      const uint64_t row = row0 + (static_cast<uint32_t>(r) < nrows ? r : nrows - 1);
+      raw[r] = *reinterpret_cast<const uint2*>(b.raw + row * b.raw_ld + cc);
+    }
+  }
+  // start bit of this lane's chunk inside the LDS buffer (after the 4 guard words)
+  __device__ __forceinline__ uint32_t start_bit() const { return 128 + (w0 - a0) * 32 + wave_excl_scan(cb); }
+};
+
 // ------------------------------------------------------------------ decode
 
-// Fast path: S = 64 chunks of 8 columns, K a multiple of 8.
+// Fast path (S = 64 chunks of 8 columns, K % 8 == 0): wavefronts take tiles
+// in a grid-stride loop and write 16 bytes per lane per row.
 template <int TR>
-__global__ __launch_bounds__(kThreads) void k_decode_fast(BlobDev b, uint16_t* __restrict__ out, uint64_t ld) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* tab = lds;
-  const uint32_t wave = threadIdx.x / kWave;
-  uint32_t* buf = lds + kTable + wave * b.buf_words;
+__global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_fast(BlobDev b, uint16_t* __restrict__ out,
+                                                                       uint64_t ld) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* buf = lds + wave * b.buf_words;
   load_table(tab, b.table);
   __syncthreads();
-  const uint32_t lane = lane_id();
-  const uint32_t limit = b.buf_words - 2;
-  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * kWavesPerBlock + wave; t < b.n_tiles;
-       t += static_cast<uint64_t>(gridDim.x) * kWavesPerBlock) {
-    const uint64_t ti = t / b.n_tc, tj = t % b.n_tc;
-    const uint64_t row0 = ti * TR;
-    const uint32_t nrows = static_cast<uint32_t>(umin64(TR, b.rows - row0));
-    const uint64_t c0 = tj * 512 + lane * 8;
-    const bool active = c0 < b.cols;
-    const uint32_t cb = b.chunk_bits[t * 64 + lane];
-    uint32_t q = wave_excl_scan(cb);
-    stage_tile(b, t, buf);
-    if (active) {
-      for (uint32_t r = 0; r < nrows; r++) {
-        const uint2 rw = *reinterpret_cast<const uint2*>(b.raw + (row0 + r) * b.raw_ld + c0);
+  const uint64_t nwaves = static_cast<uint64_t>(gridDim.x) * (blockDim.x / kWave);
+  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + wave; t < b.n_tiles; t += nwaves) {
+    const uint64_t ti = t / b.n_tc;
+    const uint32_t tj = static_cast<uint32_t>(t % b.n_tc);
+    TileIn<TR> in;
+    in.load(b, ti, tj, buf);
+    const uint32_t bit = in.start_bit();
+    wait_vmem();
+    wave_sync_lds();
+    if (in.active) {
+      Bits br;
+      br.init(buf, bit);
+      const uint64_t row0 = ti * TR;
+#pragma unroll
+      for (int r = 0; r < TR; r++) {
         uint4 o;
-        o.x = assemble(decode_pair(tab, buf, q, limit), rw.x, false);
-        o.y = assemble(decode_pair(tab, buf, q, limit), rw.x, true);
-        o.z = assemble(decode_pair(tab, buf, q, limit), rw.y, false);
-        o.w = assemble(decode_pair(tab, buf, q, limit), rw.y, true);
-        *reinterpret_cast<uint4*>(out + (row0 + r) * ld + c0) = o;
+        o.x = assemble(br.pair(tab, buf), in.raw[r].x, false);
+        o.y = assemble(br.pair(tab, buf), in.raw[r].x, true);
+        o.z = assemble(br.pair(tab, buf), in.raw[r].y, false);
+        o.w = assemble(br.pair(tab, buf), in.raw[r].y, true);
+        if (static_cast<uint32_t>(r) < in.nrows) *reinterpret_cast<uint4*>(out + (row0 + r) * ld + in.c0) = o;
       }
     }
+    wave_sync_lds();
   }
 }
 
-// Generic path: any geometry, one symbol at a time.
-__global__ __launch_bounds__(kThreads) void k_decode_generic(BlobDev b, uint16_t* __restrict__ out, uint64_t ld) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* tab = lds;
-  const uint32_t wave = threadIdx.x / kWave;
-  uint32_t* buf = lds + kTable + wave * b.buf_words;
+// Generic path: any geometry, one symbol at a time, scalar stores.
+__global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDev b, uint16_t* __restrict__ out,
+                                                                          uint64_t ld) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* buf = lds + wave * b.buf_words;
   load_table(tab, b.table);
   __syncthreads();
   const uint32_t lane = lane_id();
-  const uint32_t limit = b.buf_words - 2;
-  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * kWavesPerBlock + wave; t < b.n_tiles;
-       t += static_cast<uint64_t>(gridDim.x) * kWavesPerBlock) {
+  const uint64_t nwaves = static_cast<uint64_t>(gridDim.x) * (blockDim.x / kWave);
+  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + wave; t < b.n_tiles; t += nwaves) {
     const uint64_t ti = t / b.n_tc, tj = t % b.n_tc;
     const uint64_t row0 = ti * b.tr;
     const uint64_t r1 = umin64(b.rows, row0 + b.tr);
     const uint64_t tile_c1 = umin64(b.cols, tj * b.tc + b.tc);
-    stage_tile(b, t, buf);
-    uint32_t base = 0;  // start bit of the first chunk handled in this round
+    const uint32_t w0 = uniform(b.tile_words[t]);
+    const uint32_t w1 = uniform(b.tile_words[t + 1]);
+    const uint32_t a0 = w0 & ~3u;
+    stage_stream(b, a0, stage_blocks(b, a0, w1 < w0 ? w0 : w1), buf);
+    wait_vmem();
+    wave_sync_lds();
+    uint32_t base = 128 + (w0 - a0) * 32;  // start bit of the first chunk of this round
     for (uint32_t c0i = 0; c0i < b.s; c0i += kWave) {
       const uint32_t c = c0i + lane;
       const uint32_t cb = c < b.s ? b.chunk_bits[t * b.s + c] : 0u;
       const uint32_t excl = wave_excl_scan(cb);
-      uint32_t q = base + excl;
-      base += __shfl(excl + cb, kWave - 1, kWave);
-      if (c >= b.s) continue;
-      const uint64_t cc0 = tj * b.tc + static_cast<uint64_t>(c) * b.v;
-      if (cc0 >= tile_c1) continue;
-      const uint64_t cc1 = umin64(tile_c1, cc0 + b.v);
-      for (uint64_t r = row0; r < r1; r++)
-        for (uint64_t k = cc0; k < cc1; k++) {
-          const uint32_t ent = tab[window_at(buf, q, limit) & 0xFFFu];
-          q += (ent >> 16) & 0xFu;
-          const uint32_t e = (ent >> 7) & 0xFFu;
-          const uint32_t rb = b.raw[r * b.raw_ld + k];
-          out[r * ld + k] = static_cast<uint16_t>(((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu));
+      const uint32_t bit = base + excl;
+      base += __builtin_amdgcn_readlane(excl + cb, kWave - 1);
+      if (c < b.s) {
+        const uint64_t cc0 = tj * b.tc + static_cast<uint64_t>(c) * b.v;
+        if (cc0 < tile_c1) {
+          const uint64_t cc1 = umin64(tile_c1, cc0 + b.v);
+          Bits br;
+          br.init(buf, bit);
+          for (uint64_t r = row0; r < r1; r++)
+            for (uint64_t k = cc0; k < cc1; k++) {
+              const uint32_t e = br.one(tab, buf);
+              const uint32_t rb = b.raw[r * b.raw_ld + k];
+              out[r * ld + k] = static_cast<uint16_t>(((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu));
+            }
         }
+      }
     }
+    wave_sync_lds();
   }
 }
 
 // -------------------------------------------------------------------- GEMV
 
-// Fast path, batch 1: partial[tj * rows + n] = sum over the tile's columns.
+// One tile of the fused GEMV: adds the tile's row sums (this lane's 8
+// columns) into acc.
 template <int TR>
-__global__ __launch_bounds__(kThreads) void k_gemv_fast(BlobDev b, const uint16_t* __restrict__ x,
-                                                        float* __restrict__ partial) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* tab = lds;
-  const uint32_t wave = threadIdx.x / kWave;
-  uint32_t* buf = lds + kTable + wave * b.buf_words;
+__device__ __forceinline__ void gemv_tile(const BlobDev& b, uint64_t ti, uint32_t tj, const uint16_t* __restrict__ x,
+                                          uint32_t* buf, const uint32_t* tab, float (&acc)[TR]) {
+  TileIn<TR> in;
+  in.load(b, ti, tj, buf);
+  const uint4 xv = *reinterpret_cast<const uint4*>(x + (in.active ? in.c0 : 0));
+  const uint32_t bit = in.start_bit();
+  wait_vmem();
+  wave_sync_lds();
+  if (in.active) {
+    // Rows past the matrix edge (last row block only) are decoded from
+    // whatever follows the chunk and multiplied too: raw loads were clamped to
+    // valid rows, each row keeps its own sum through the reduction, and rows
+    // past the edge are never stored.
+    Bits br;
+    br.init(buf, bit);
+#pragma unroll
+    for (int r = 0; r < TR; r++) {
+      float a = acc[r];
+      a = dot2(assemble(br.pair(tab, buf), in.raw[r].x, false), xv.x, a);
+      a = dot2(assemble(br.pair(tab, buf), in.raw[r].x, true), xv.y, a);
+      a = dot2(assemble(br.pair(tab, buf), in.raw[r].y, false), xv.z, a);
+      a = dot2(assemble(br.pair(tab, buf), in.raw[r].y, true), xv.w, a);
+      acc[r] = a;
+    }
+  }
+  wave_sync_lds();
+}
+
+// Fused decode-GEMV, batch 1, y written directly.
+// LDS: table | per-wavefront row sums [waves][TR] | stream buffers.
+template <int TR>
+__global__ __launch_bounds__(kMaxWaves * kWave) void k_gemv(BlobDev b, Split sp, const uint16_t* __restrict__ x,
+                                                            void* __restrict__ y, int y_f32) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
+  float* red = reinterpret_cast<float*>(lds);
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t lane = lane_id();
+  uint32_t* buf = lds + kMaxWaves * TR + wave * b.buf_words;
   load_table(tab, b.table);
   __syncthreads();
-  const uint32_t lane = lane_id();
-  const uint32_t limit = b.buf_words - 2;
-  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * kWavesPerBlock + wave; t < b.n_tiles;
-       t += static_cast<uint64_t>(gridDim.x) * kWavesPerBlock) {
-    const uint64_t ti = t / b.n_tc, tj = t % b.n_tc;
-    const uint64_t row0 = ti * TR;
-    const uint32_t nrows = static_cast<uint32_t>(umin64(TR, b.rows - row0));
-    const uint64_t c0 = tj * 512 + lane * 8;
-    const bool active = c0 < b.cols;
-    const uint32_t cb = b.chunk_bits[t * 64 + lane];
-    uint32_t q = wave_excl_scan(cb);
-    stage_tile(b, t, buf);
+  const uint32_t rbl = wave / sp.nw, wt = wave % sp.nw;
+  for (uint64_t item = blockIdx.x; item < sp.items; item += gridDim.x) {
+    const uint64_t ti = item * sp.rb + rbl;
     float acc[TR];
 #pragma unroll
     for (int r = 0; r < TR; r++) acc[r] = 0.0f;
-    if (active) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(x + c0);
-      uint2 rw[TR];
-#pragma unroll
-      for (int r = 0; r < TR; r++)
-        rw[r] = r < static_cast<int>(nrows)
-                    ? *reinterpret_cast<const uint2*>(b.raw + (row0 + r) * b.raw_ld + c0)
-                    : make_uint2(0, 0);
-#pragma unroll
-      for (int r = 0; r < TR; r++) {
-        if (r < static_cast<int>(nrows)) {
-          float a = 0.0f;
-          a = dot2(assemble(decode_pair(tab, buf, q, limit), rw[r].x, false), xv.x, a);
-          a = dot2(assemble(decode_pair(tab, buf, q, limit), rw[r].x, true), xv.y, a);
-          a = dot2(assemble(decode_pair(tab, buf, q, limit), rw[r].y, false), xv.z, a);
-          a = dot2(assemble(decode_pair(tab, buf, q, limit), rw[r].y, true), xv.w, a);
-          acc[r] = a;
-        }
-      }
+    if (ti < b.n_tr) {
+      for (uint32_t tj = wt; tj < b.n_tc; tj += sp.nw) gemv_tile<TR>(b, ti, tj, x, buf, tab, acc);
     }
     const float s = reduce_rows<TR>(acc);
     constexpr uint32_t lanes_per_row = kWave / TR;
-    if ((lane & (lanes_per_row - 1)) == 0) {
-      const uint32_t r = lane / lanes_per_row;
-      if (r < nrows) partial[tj * b.rows + row0 + r] = s;
+    if ((lane & (lanes_per_row - 1)) == 0) red[wave * TR + lane / lanes_per_row] = s;
+    __syncthreads();
+    if (threadIdx.x < sp.rb * TR) {
+      const uint32_t rl = threadIdx.x / TR, r = threadIdx.x % TR;
+      const uint64_t row = (item * sp.rb + rl) * TR + r;
+      if (row < b.rows) {
+        float sum = 0.0f;
+        for (uint32_t w = 0; w < sp.nw; w++) sum += red[(rl * sp.nw + w) * TR + r];
+        store_y(y, row, sum, y_f32);
+      }
     }
+    __syncthreads();
   }
 }
 
-// Generic path for any geometry; batch rows handled one after another.
+// Skinny decode-GEMM with MFMA, batch 2..16, TR = 16; one row block per work
+// item, its column tiles split across the workgroup's wavefronts.
+// LDS: table | per-wavefront D [waves][16][16] | stream buffers | decoded
+// tiles [waves][16][kMfmaRowPad].
+__global__ __launch_bounds__(kMaxWaves * kWave) void k_gemm_mfma(BlobDev b, Split sp, const uint16_t* __restrict__ X,
+                                                                 uint64_t ldx, int batch, void* __restrict__ Y,
+                                                                 uint64_t ldy, int y_f32) {
+  constexpr int TR = 16;
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
+  float* red = reinterpret_cast<float*>(lds);
+  const uint32_t nwaves = blockDim.x / kWave;
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t lane = lane_id();
+  uint32_t* buf = lds + nwaves * 256 + wave * b.buf_words;
+  uint16_t* wt_lds = reinterpret_cast<uint16_t*>(lds + nwaves * 256 + nwaves * b.buf_words) +
+                     wave * static_cast<size_t>(TR) * kMfmaRowPad;
+  load_table(tab, b.table);
+  __syncthreads();
+  const uint32_t mrow = lane % 16, kq = lane / 16;  // MFMA A: weight row, 8-column group
+  const uint32_t nb = lane % 16;                    // MFMA B: batch row
+  for (uint64_t ti = blockIdx.x; ti < b.n_tr; ti += gridDim.x) {
+    f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (uint32_t tj = wave; tj < b.n_tc; tj += nwaves) {
+      TileIn<TR> in;
+      in.load(b, ti, tj, buf);
+      uint4 xb[16];
+#pragma unroll
+      for (int kb = 0; kb < 16; kb++) {
+        const uint64_t gk = static_cast<uint64_t>(tj) * 512 + kb * 32 + kq * 8;
+        const bool ok = static_cast<int>(nb) < batch && gk < b.cols;
+        const uint4 v = *reinterpret_cast<const uint4*>(X + (ok ? nb * ldx + gk : 0));
+        xb[kb] = ok ? v : make_uint4(0, 0, 0, 0);
+      }
+      const uint32_t bit = in.start_bit();
+      wait_vmem();
+      wave_sync_lds();
+      Bits br;
+      if (in.active) br.init(buf, bit);
+#pragma unroll
+      for (int r = 0; r < TR; r++) {
+        uint4 o = make_uint4(0, 0, 0, 0);
+        if (in.active) {
+          o.x = assemble(br.pair(tab, buf), in.raw[r].x, false);
+          o.y = assemble(br.pair(tab, buf), in.raw[r].x, true);
+          o.z = assemble(br.pair(tab, buf), in.raw[r].y, false);
+          o.w = assemble(br.pair(tab, buf), in.raw[r].y, true);
+        }
+        // columns past the edge must be exact zeros (they meet zero X in the
+        // contraction); rows past the edge only reach rows that are not stored
+        *reinterpret_cast<uint4*>(wt_lds + r * kMfmaRowPad + lane * 8) = o;
+      }
+      wave_sync_lds();
+#pragma unroll
+      for (int kb = 0; kb < 16; kb++) {
+        const uint4 av = *reinterpret_cast<const uint4*>(wt_lds + mrow * kMfmaRowPad + kb * 32 + kq * 8);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                    __builtin_bit_cast(bf16x8_t, xb[kb]), d, 0, 0, 0);
+      }
+      wave_sync_lds();
+    }
+    // lane holds D[4 * (lane / 16) + i][lane % 16]: rows x batch
+#pragma unroll
+    for (int i = 0; i < 4; i++) red[wave * 256 + (4 * (lane / 16) + i) * 16 + nb] = d[i];
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
+      const uint32_t r = i / 16, beta = i % 16;
+      const uint64_t row = ti * TR + r;
+      if (static_cast<int>(beta) < batch && row < b.rows) {
+        float sum = 0.0f;
+        for (uint32_t w = 0; w < nwaves; w++) sum += red[w * 256 + i];
+        store_y(Y, beta * ldy + row, sum, y_f32);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Generic path for any geometry, batch rows one after another:
 // partial[(tj * batch + beta) * rows + n].
-__global__ __launch_bounds__(kThreads) void k_gemv_generic(BlobDev b, const uint16_t* __restrict__ X, uint64_t ldx,
-                                                           int batch, float* __restrict__ partial) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* tab = lds;
-  const uint32_t wave = threadIdx.x / kWave;
-  uint32_t* buf = lds + kTable + wave * b.buf_words;
-  float* rowsum = reinterpret_cast<float*>(lds + kTable + kWavesPerBlock * b.buf_words) +
-                  wave * static_cast<size_t>(b.tr) * b.s;
+__global__ __launch_bounds__(kGenericWaves * kWave) void k_gemv_generic(BlobDev b, const uint16_t* __restrict__ X,
+                                                                        uint64_t ldx, int batch,
+                                                                        float* __restrict__ partial) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
+  const uint32_t nw = blockDim.x / kWave;
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* buf = lds + wave * b.buf_words;
+  float* rowsum = reinterpret_cast<float*>(lds + nw * b.buf_words) + wave * static_cast<size_t>(b.tr) * b.s;
   load_table(tab, b.table);
   __syncthreads();
   const uint32_t lane = lane_id();
-  const uint32_t limit = b.buf_words - 2;
-  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * kWavesPerBlock + wave; t < b.n_tiles;
-       t += static_cast<uint64_t>(gridDim.x) * kWavesPerBlock) {
+  const uint64_t nwaves = static_cast<uint64_t>(gridDim.x) * nw;
+  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * nw + wave; t < b.n_tiles; t += nwaves) {
     const uint64_t ti = t / b.n_tc, tj = t % b.n_tc;
     const uint64_t row0 = ti * b.tr;
     const uint32_t nrows = static_cast<uint32_t>(umin64(b.tr, b.rows - row0));
     const uint64_t tile_c1 = umin64(b.cols, tj * b.tc + b.tc);
-    stage_tile(b, t, buf);
+    const uint32_t w0 = uniform(b.tile_words[t]);
+    const uint32_t w1 = uniform(b.tile_words[t + 1]);
+    const uint32_t a0 = w0 & ~3u;
+    stage_stream(b, a0, stage_blocks(b, a0, w1 < w0 ? w0 : w1), buf);
+    wait_vmem();
+    wave_sync_lds();
     for (int beta = 0; beta < batch; beta++) {
       const uint16_t* x = X + beta * ldx;
-      uint32_t base = 0;
+      uint32_t base = 128 + (w0 - a0) * 32;
       for (uint32_t c0i = 0; c0i < b.s; c0i += kWave) {
         const uint32_t c = c0i + lane;
         const uint32_t cb = c < b.s ? b.chunk_bits[t * b.s + c] : 0u;
         const uint32_t excl = wave_excl_scan(cb);
-        uint32_t q = base + excl;
-        base += __shfl(excl + cb, kWave - 1, kWave);
-        if (c >= b.s) continue;
-        const uint64_t cc0 = tj * b.tc + static_cast<uint64_t>(c) * b.v;
-        const uint64_t cc1 = cc0 < tile_c1 ? umin64(tile_c1, cc0 + b.v) : cc0;
-        for (uint32_t r = 0; r < nrows; r++) {
-          float a = 0.0f;
-          for (uint64_t k = cc0; k < cc1; k++) {
-            const uint32_t ent = tab[window_at(buf, q, limit) & 0xFFFu];
-            q += (ent >> 16) & 0xFu;
-            const uint32_t e = (ent >> 7) & 0xFFu;
-            const uint32_t rb = b.raw[(row0 + r) * b.raw_ld + k];
-            const uint32_t wbits = (((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu)) << 16;
-            const float xf = __builtin_bit_cast(float, static_cast<uint32_t>(x[k]) << 16);
-            a = __builtin_fmaf(__builtin_bit_cast(float, wbits), xf, a);
+        const uint32_t bit = base + excl;
+        base += __builtin_amdgcn_readlane(excl + cb, kWave - 1);
+        if (c < b.s) {
+          const uint64_t cc0 = tj * b.tc + static_cast<uint64_t>(c) * b.v;
+          const uint64_t cc1 = cc0 < tile_c1 ? umin64(tile_c1, cc0 + b.v) : cc0;
+          Bits br;
+          br.init(buf, bit);
+          for (uint32_t r = 0; r < nrows; r++) {
+            float a = 0.0f;
+            for (uint64_t k = cc0; k < cc1; k++) {
+              const uint32_t e = br.one(tab, buf);
+              const uint32_t rb = b.raw[(row0 + r) * b.raw_ld + k];
+              const uint32_t wbits = (((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu)) << 16;
+              const float xf = __builtin_bit_cast(float, static_cast<uint32_t>(x[k]) << 16);
+              a = __builtin_fmaf(__builtin_bit_cast(float, wbits), xf, a);
+            }
+            rowsum[r * b.s + c] = a;
           }
-          rowsum[r * b.s + c] = a;
         }
       }
       wave_sync_lds();
@@ -363,71 +622,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv_generic(BlobDev b, const uint
   }
 }
 
-// Skinny GEMM with MFMA, batch 2..16, TR = 16:
-// partial[(tj * batch + beta) * rows + n].
-__global__ __launch_bounds__(kThreads) void k_gemm_mfma(BlobDev b, const uint16_t* __restrict__ X, uint64_t ldx,
-                                                        int batch, float* __restrict__ partial) {
-  constexpr int TR = 16;
-  constexpr int kRowPad = 512 + 8;  // bf16 per LDS row (pad against bank conflicts)
-  extern __shared__ uint32_t lds[];
-  uint32_t* tab = lds;
-  const uint32_t wave = threadIdx.x / kWave;
-  uint32_t* buf = lds + kTable + wave * b.buf_words;
-  uint16_t* wt = reinterpret_cast<uint16_t*>(lds + kTable + kWavesPerBlock * b.buf_words) +
-                 wave * static_cast<size_t>(TR) * kRowPad;
-  load_table(tab, b.table);
-  __syncthreads();
-  const uint32_t lane = lane_id();
-  const uint32_t limit = b.buf_words - 2;
-  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * kWavesPerBlock + wave; t < b.n_tiles;
-       t += static_cast<uint64_t>(gridDim.x) * kWavesPerBlock) {
-    const uint64_t ti = t / b.n_tc, tj = t % b.n_tc;
-    const uint64_t row0 = ti * TR;
-    const uint32_t nrows = static_cast<uint32_t>(umin64(TR, b.rows - row0));
-    const uint64_t c0 = tj * 512 + lane * 8;
-    const bool active = c0 < b.cols;
-    const uint32_t cb = b.chunk_bits[t * 64 + lane];
-    uint32_t q = wave_excl_scan(cb);
-    stage_tile(b, t, buf);
-    // decode the tile into LDS, rows past the matrix (or columns past the
-    // edge) as zeros
-    for (int r = 0; r < TR; r++) {
-      uint4 o = make_uint4(0, 0, 0, 0);
-      if (active && r < static_cast<int>(nrows)) {
-        const uint2 rw = *reinterpret_cast<const uint2*>(b.raw + (row0 + r) * b.raw_ld + c0);
-        o.x = assemble(decode_pair(tab, buf, q, limit), rw.x, false);
-        o.y = assemble(decode_pair(tab, buf, q, limit), rw.x, true);
-        o.z = assemble(decode_pair(tab, buf, q, limit), rw.y, false);
-        o.w = assemble(decode_pair(tab, buf, q, limit), rw.y, true);
-      }
-      *reinterpret_cast<uint4*>(wt + r * kRowPad + lane * 8) = o;
-    }
-    wave_sync_lds();
-    // D[16 rows x 16 batch] += W[16 x 32] * X^T[32 x 16] over 16 column blocks
-    f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t mrow = lane % 16, kq = lane / 16;  // A: row, 8-column group
-    const uint32_t nb = lane % 16;                    // B: batch column
-#pragma unroll 4
-    for (int kb = 0; kb < 16; kb++) {
-      const uint32_t kcol = kb * 32 + kq * 8;
-      const uint4 av = *reinterpret_cast<const uint4*>(wt + mrow * kRowPad + kcol);
-      uint4 bv = make_uint4(0, 0, 0, 0);
-      const uint64_t gk = tj * 512 + kcol;
-      if (static_cast<int>(nb) < batch && gk < b.cols)
-        bv = *reinterpret_cast<const uint4*>(X + nb * ldx + gk);
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                  __builtin_bit_cast(bf16x8_t, bv), d, 0, 0, 0);
-    }
-    wave_sync_lds();
-    // lane holds D[4 * (lane / 16) + i][lane % 16]
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const uint32_t r = 4 * (lane / 16) + i;
-      if (static_cast<int>(nb) < batch && r < nrows) partial[(tj * batch + nb) * b.rows + row0 + r] = d[i];
-    }
-  }
-}
-
 // y[beta, n] = sum over column tiles of partial, in tile order.
 __global__ void k_reduce(const float* __restrict__ partial, uint64_t rows, uint32_t n_tc, int batch,
                          void* __restrict__ y, uint64_t ldy, int y_f32) {
@@ -436,53 +630,71 @@ __global__ void k_reduce(const float* __restrict__ partial, uint64_t rows, uint3
   const uint64_t beta = i / rows, n = i % rows;
   float s = 0.0f;
   for (uint32_t tj = 0; tj < n_tc; tj++) s += partial[(tj * static_cast<uint64_t>(batch) + beta) * rows + n];
-  if (y_f32)
-    static_cast<float*>(y)[beta * ldy + n] = s;
-  else
-    static_cast<uint16_t*>(y)[beta * ldy + n] = f32_to_bf16_rne(s);
+  store_y(y, beta * ldy + n, s, y_f32);
 }
 
 // ------------------------------------------------- uncompressed comparator
 
-// Same tiling and reduction as k_gemv_fast, reading BF16 weights directly.
+// Same tiling, split, loads-up-front and reductions as k_gemv, reading BF16
+// weights (16 bytes per lane per row) instead of decoding them.
 template <int TR>
-__global__ __launch_bounds__(kThreads) void k_gemv_bf16(const uint16_t* __restrict__ w, uint64_t rows,
-                                                        uint64_t cols, uint64_t ld, uint32_t n_tc,
-                                                        const uint16_t* __restrict__ x,
-                                                        float* __restrict__ partial) {
-  const uint32_t wave = threadIdx.x / kWave;
+__global__ __launch_bounds__(kMaxWaves * kWave) void k_gemv_bf16(const uint16_t* __restrict__ w, uint64_t rows,
+                                                                 uint64_t cols, uint64_t ld, uint32_t n_tc,
+                                                                 uint64_t n_tr, Split sp,
+                                                                 const uint16_t* __restrict__ x,
+                                                                 void* __restrict__ y, int y_f32) {
+  __shared__ float red[kMaxWaves * TR];
+  const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t lane = lane_id();
-  const uint64_t n_tiles = ((rows + TR - 1) / TR) * n_tc;
-  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * kWavesPerBlock + wave; t < n_tiles;
-       t += static_cast<uint64_t>(gridDim.x) * kWavesPerBlock) {
-    const uint64_t ti = t / n_tc, tj = t % n_tc;
-    const uint64_t row0 = ti * TR;
-    const uint32_t nrows = static_cast<uint32_t>(umin64(TR, rows - row0));
-    const uint64_t c0 = tj * 512 + lane * 8;
+  const uint32_t rbl = wave / sp.nw, wt = wave % sp.nw;
+  for (uint64_t item = blockIdx.x; item < sp.items; item += gridDim.x) {
+    const uint64_t ti = item * sp.rb + rbl;
     float acc[TR];
 #pragma unroll
     for (int r = 0; r < TR; r++) acc[r] = 0.0f;
-    if (c0 < cols) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(x + c0);
+    if (ti < n_tr) {
+      const uint64_t row0 = ti * TR;
+      const uint32_t nrows = static_cast<uint32_t>(umin64(TR, rows - row0));
+      for (uint32_t tj = wt; tj < n_tc; tj += sp.nw) {
+        const uint64_t c0 = static_cast<uint64_t>(tj) * 512 + lane * 8;
+        const bool active = c0 < cols;
+        const uint64_t cc = active ? c0 : 0;
+        const uint4 xv = *reinterpret_cast<const uint4*>(x + cc);
+        uint4 wv[TR];
 #pragma unroll
-      for (int r = 0; r < TR; r++) {
-        if (r < static_cast<int>(nrows)) {
-          const uint4 wv = *reinterpret_cast<const uint4*>(w + (row0 + r) * ld + c0);
-          float a = 0.0f;
-          a = dot2(wv.x, xv.x, a);
-          a = dot2(wv.y, xv.y, a);
-          a = dot2(wv.z, xv.z, a);
-          a = dot2(wv.w, xv.w, a);
-          acc[r] = a;
+        for (int r = 0; r < TR; r++) {
+          const uint64_t row = row0 + (static_cast<uint32_t>(r) < nrows ? r : nrows - 1);
+          wv[r] = *reinterpret_cast<const uint4*>(w + row * ld + cc);
+        }
+        if (active) {
+#pragma unroll
+          for (int r = 0; r < TR; r++) {
+            if (static_cast<uint32_t>(r) < nrows) {
+              float a = acc[r];
+              a = dot2(wv[r].x, xv.x, a);
+              a = dot2(wv[r].y, xv.y, a);
+              a = dot2(wv[r].z, xv.z, a);
+              a = dot2(wv[r].w, xv.w, a);
+              acc[r] = a;
+            }
+          }
         }
       }
     }
     const float s = reduce_rows<TR>(acc);
     constexpr uint32_t lanes_per_row = kWave / TR;
-    if ((lane & (lanes_per_row - 1)) == 0) {
-      const uint32_t r = lane / lanes_per_row;
-      if (r < nrows) partial[tj * rows + row0 + r] = s;
+    if ((lane & (lanes_per_row - 1)) == 0) red[wave * TR + lane / lanes_per_row] = s;
+    __syncthreads();
+    if (threadIdx.x < sp.rb * TR) {
+      const uint32_t rl = threadIdx.x / TR, r = threadIdx.x % TR;
+      const uint64_t row = (item * sp.rb + rl) * TR + r;
+      if (row < rows) {
+        float sum = 0.0f;
+        for (uint32_t wv2 = 0; wv2 < sp.nw; wv2++) sum += red[(rl * sp.nw + wv2) * TR + r];
+        store_y(y, row, sum, y_f32);
+      }
     }
+    __syncthreads();
   }
 }
 
@@ -490,18 +702,19 @@ __global__ __launch_bounds__(kThreads) void k_gemv_bf16(const uint16_t* __restri
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+constexpr size_t kMaxLds = 160 * 1024 - kTable * 4;  // dynamic LDS beside the static table
+constexpr int kCUs = 256;
+
 struct Launch {
   BlobDev b;
-  bool fast;       // S = 64, V = 8, TR in {8, 16, 32}, K % 8 == 0
-  size_t lds;      // dynamic LDS bytes (table + stream buffers)
-  unsigned grid;
+  bool fast;  // S = 64, V = 8, TR in {8, 16, 32}, K % 8 == 0
 };
 
 nwc_status prepare(const nwc_info* info, const void* blob_dev, Launch* L) {
   nwc::Geometry g;
   if (!info || !blob_dev || !nwc::info_geometry(info, &g)) return NWC_ERR_INVALID_ARG;
   if (!aligned(blob_dev, 256)) return NWC_ERR_ALIGNMENT;
-  if (info->max_tile_words > 3u * 65536u) return NWC_ERR_BAD_FORMAT;
+  if (info->max_tile_words > 65536u) return NWC_ERR_UNSUPPORTED;
   const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
   BlobDev& b = L->b;
   b.table = reinterpret_cast<const uint32_t*>(base + g.off_table);
@@ -513,32 +726,65 @@ nwc_status prepare(const nwc_info* info, const void* blob_dev, Launch* L) {
   b.cols = g.cols;
   b.raw_ld = g.raw_ld;
   b.n_tiles = g.n_tiles;
+  b.n_tr = g.n_tr;
   b.n_tc = static_cast<uint32_t>(g.n_tc);
   b.tr = g.tr;
   b.tc = g.tc;
   b.s = g.s;
   b.v = g.v;
   b.stream_words = static_cast<uint32_t>(g.stream_words);
-  b.buf_words = (info->max_tile_words + kGuardWords + 3) & ~3u;
+  // room for the largest tile starting 3 words into a 4-word block, plus the
+  // bit reader's two words of look-ahead, in whole 256-word blocks
+  b.buf_words = 4 + ((info->max_tile_words + 3 + 2 + 255) / 256) * 256;
   L->fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
-  L->lds = (kTable + static_cast<size_t>(kWavesPerBlock) * b.buf_words) * 4;
-  const uint64_t blocks = (g.n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-  L->grid = static_cast<unsigned>(std::min<uint64_t>(blocks, 256ull * 8));
   return NWC_OK;
+}
+
+// Split for the fused kernels: up to 16 wavefronts per workgroup; several row
+// blocks per work item when the matrix has few column tiles and many rows.
+Split make_split(uint64_t n_tr, uint32_t n_tc, uint32_t max_waves) {
+  Split sp;
+  sp.nw = std::min<uint32_t>(n_tc, max_waves);
+  const uint32_t fit = std::max<uint32_t>(1, max_waves / sp.nw);
+  const uint64_t want = (n_tr + 2 * kCUs - 1) / (2 * kCUs);  // keep >= 2 items per CU when possible
+  sp.rb = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(fit, want)));
+  sp.waves = sp.nw * sp.rb;
+  sp.items = (n_tr + sp.rb - 1) / sp.rb;
+  return sp;
 }
 
 template <typename K>
 hipError_t set_lds(K kernel, size_t lds) {
-  if (lds <= 65536) return hipSuccess;
+  if (lds + kTable * 4 <= 65536) return hipSuccess;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                              static_cast<int>(lds));
 }
 
-constexpr size_t kMaxLds = 160 * 1024;
-
 nwc_status launched() {
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   return e == hipSuccess ? NWC_OK : NWC_ERR_HIP;
+}
+
+// grid for a persistent loop over `items` work items of `waves` wavefronts
+unsigned grid_for(uint64_t items, uint32_t waves, size_t lds) {
+  const uint64_t by_waves = std::max<uint64_t>(1, 32 / waves);
+  const uint64_t by_lds = std::max<uint64_t>(1, (160 * 1024) / (lds + kTable * 4));
+  const uint64_t per_cu = std::min(by_waves, by_lds);
+  return static_cast<unsigned>(std::min<uint64_t>(items, kCUs * per_cu));
+}
+
+template <int TR>
+nwc_status launch_gemv(const Launch& L, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
+  const Split sp = make_split(L.b.n_tr, L.b.n_tc, kMaxWaves);
+  const size_t lds = (kMaxWaves * TR + static_cast<size_t>(sp.waves) * L.b.buf_words) * 4;
+  if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
+  if (set_lds(k_gemv<TR>, lds) != hipSuccess) return NWC_ERR_HIP;
+  k_gemv<TR><<<grid_for(sp.items, sp.waves, lds), sp.waves * kWave, lds, s>>>(L.b, sp, x, y, y_f32);
+  return launched();
+}
+
+size_t generic_ws_bytes(const nwc::Geometry& g, int batch) {
+  return static_cast<size_t>(g.n_tc) * batch * g.rows * sizeof(float);
 }
 
 }  // namespace
@@ -574,7 +820,9 @@ nwc_status nwc_inspect(const void* blob, size_t bytes, nwc_info* info) { return 
 nwc_status nwc_workspace_size(const nwc_info* info, int batch, size_t* bytes) {
   nwc::Geometry g;
   if (!info || !bytes || batch < 1 || batch > 16 || !nwc::info_geometry(info, &g)) return NWC_ERR_INVALID_ARG;
-  *bytes = static_cast<size_t>(g.n_tc) * batch * g.rows * sizeof(float);
+  const bool fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
+  const bool fused = fast && (batch == 1 || g.tr == 16);
+  *bytes = fused ? 0 : generic_ws_bytes(g, batch);
   return NWC_OK;
 }
 
@@ -584,86 +832,87 @@ nwc_status nwc_decode(const nwc_info* info, const void* blob_dev, uint16_t* w_de
   nwc_status st = prepare(info, blob_dev, &L);
   if (st) return st;
   if (ld < L.b.cols) return NWC_ERR_INVALID_ARG;
+  if (!aligned(w_dev, 2)) return NWC_ERR_ALIGNMENT;
   const bool vec = aligned(w_dev, 16) && ld % 8 == 0;
-  if (L.lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
+  const size_t lds = (static_cast<size_t>(kGenericWaves) * L.b.buf_words) * 4;
+  if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint64_t blocks = (L.b.n_tiles + kGenericWaves - 1) / kGenericWaves;
+  const unsigned grid = static_cast<unsigned>(std::min<uint64_t>(blocks, kCUs * 8));
+  const unsigned threads = kGenericWaves * kWave;
   if (L.fast && vec) {
     switch (L.b.tr) {
       case 8:
-        if (set_lds(k_decode_fast<8>, L.lds) != hipSuccess) return NWC_ERR_HIP;
-        k_decode_fast<8><<<L.grid, kThreads, L.lds, s>>>(L.b, w_dev, ld);
+        if (set_lds(k_decode_fast<8>, lds) != hipSuccess) return NWC_ERR_HIP;
+        k_decode_fast<8><<<grid, threads, lds, s>>>(L.b, w_dev, ld);
         break;
       case 16:
-        if (set_lds(k_decode_fast<16>, L.lds) != hipSuccess) return NWC_ERR_HIP;
-        k_decode_fast<16><<<L.grid, kThreads, L.lds, s>>>(L.b, w_dev, ld);
+        if (set_lds(k_decode_fast<16>, lds) != hipSuccess) return NWC_ERR_HIP;
+        k_decode_fast<16><<<grid, threads, lds, s>>>(L.b, w_dev, ld);
         break;
       default:
-        if (set_lds(k_decode_fast<32>, L.lds) != hipSuccess) return NWC_ERR_HIP;
-        k_decode_fast<32><<<L.grid, kThreads, L.lds, s>>>(L.b, w_dev, ld);
+        if (set_lds(k_decode_fast<32>, lds) != hipSuccess) return NWC_ERR_HIP;
+        k_decode_fast<32><<<grid, threads, lds, s>>>(L.b, w_dev, ld);
         break;
     }
   } else {
-    if (!aligned(w_dev, 2)) return NWC_ERR_ALIGNMENT;
-    if (set_lds(k_decode_generic, L.lds) != hipSuccess) return NWC_ERR_HIP;
-    k_decode_generic<<<L.grid, kThreads, L.lds, s>>>(L.b, w_dev, ld);
+    if (set_lds(k_decode_generic, lds) != hipSuccess) return NWC_ERR_HIP;
+    k_decode_generic<<<grid, threads, lds, s>>>(L.b, w_dev, ld);
   }
-  return launched();
-}
-
-static nwc_status launch_reduce(const float* ws, uint64_t rows, uint32_t n_tc, int batch, void* y, uint64_t ldy,
-                                nwc_out_type yt, hipStream_t s) {
-  const uint64_t n = rows * static_cast<uint64_t>(batch);
-  const unsigned threads = 256;
-  const unsigned blocks = static_cast<unsigned>((n + threads - 1) / threads);
-  k_reduce<<<blocks, threads, 0, s>>>(ws, rows, n_tc, batch, y, ldy, yt == NWC_OUT_F32 ? 1 : 0);
   return launched();
 }
 
 static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const uint16_t* X, uint64_t ldx, int batch,
                               void* Y, uint64_t ldy, nwc_out_type yt, void* ws, size_t ws_bytes, void* stream) {
-  if (!X || !Y || !ws) return NWC_ERR_INVALID_ARG;
+  if (!X || !Y) return NWC_ERR_INVALID_ARG;
   if (yt != NWC_OUT_BF16 && yt != NWC_OUT_F32) return NWC_ERR_INVALID_ARG;
   Launch L;
   nwc_status st = prepare(info, blob_dev, &L);
   if (st) return st;
   size_t need = 0;
   nwc_workspace_size(info, batch, &need);
+  if (need && !ws) return NWC_ERR_INVALID_ARG;
   if (ws_bytes < need) return NWC_ERR_BUFFER_TOO_SMALL;
   if (batch > 1 && (ldx < L.b.cols || ldy < L.b.rows)) return NWC_ERR_INVALID_ARG;
-  if (!aligned(ws, 16) || !aligned(Y, yt == NWC_OUT_F32 ? 4 : 2) || !aligned(X, 2)) return NWC_ERR_ALIGNMENT;
+  if (!aligned(Y, yt == NWC_OUT_F32 ? 4 : 2) || !aligned(X, 2)) return NWC_ERR_ALIGNMENT;
+  if (need && !aligned(ws, 16)) return NWC_ERR_ALIGNMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* part = static_cast<float*>(ws);
+  const int y_f32 = yt == NWC_OUT_F32 ? 1 : 0;
   const bool xvec = aligned(X, 16) && (batch == 1 || ldx % 8 == 0);
-  if (batch == 1 && L.fast && xvec) {
-    if (L.lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
+  if (need == 0 && !xvec) return NWC_ERR_ALIGNMENT;
+  if (need == 0 && batch == 1) {
     switch (L.b.tr) {
-      case 8:
-        if (set_lds(k_gemv_fast<8>, L.lds) != hipSuccess) return NWC_ERR_HIP;
-        k_gemv_fast<8><<<L.grid, kThreads, L.lds, s>>>(L.b, X, part);
-        break;
-      case 16:
-        if (set_lds(k_gemv_fast<16>, L.lds) != hipSuccess) return NWC_ERR_HIP;
-        k_gemv_fast<16><<<L.grid, kThreads, L.lds, s>>>(L.b, X, part);
-        break;
-      default:
-        if (set_lds(k_gemv_fast<32>, L.lds) != hipSuccess) return NWC_ERR_HIP;
-        k_gemv_fast<32><<<L.grid, kThreads, L.lds, s>>>(L.b, X, part);
-        break;
+      case 8: return launch_gemv<8>(L, X, Y, y_f32, s);
+      case 16: return launch_gemv<16>(L, X, Y, y_f32, s);
+      default: return launch_gemv<32>(L, X, Y, y_f32, s);
     }
-  } else if (batch > 1 && L.fast && L.b.tr == 16 && xvec) {
-    const size_t lds = L.lds + static_cast<size_t>(kWavesPerBlock) * 16 * (512 + 8) * 2;
+  }
+  if (need == 0) {
+    const uint32_t nw = std::min<uint32_t>(L.b.n_tc, 4);
+    const size_t lds = (nw * 256 + static_cast<size_t>(nw) * L.b.buf_words) * 4 +
+                       static_cast<size_t>(nw) * 16 * kMfmaRowPad * 2;
     if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
     if (set_lds(k_gemm_mfma, lds) != hipSuccess) return NWC_ERR_HIP;
-    k_gemm_mfma<<<L.grid, kThreads, lds, s>>>(L.b, X, ldx, batch, part);
-  } else {
-    const size_t lds = L.lds + static_cast<size_t>(kWavesPerBlock) * L.b.tr * L.b.s * 4;
-    if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
-    if (set_lds(k_gemv_generic, lds) != hipSuccess) return NWC_ERR_HIP;
-    k_gemv_generic<<<L.grid, kThreads, lds, s>>>(L.b, X, batch == 1 ? 0 : ldx, batch, part);
+    Split sp = make_split(L.b.n_tr, L.b.n_tc, nw);
+    const unsigned grid = static_cast<unsigned>(std::min<uint64_t>(L.b.n_tr, kCUs * 2));
+    k_gemm_mfma<<<grid, nw * kWave, lds, s>>>(L.b, sp, X, ldx, batch, Y, ldy, y_f32);
+    return launched();
   }
+  // generic path: partial sums per column tile, then a reduction
+  const size_t lds = (static_cast<size_t>(kGenericWaves) * L.b.buf_words) * 4 +
+                     static_cast<size_t>(kGenericWaves) * L.b.tr * L.b.s * 4;
+  if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
+  if (set_lds(k_gemv_generic, lds) != hipSuccess) return NWC_ERR_HIP;
+  float* part = static_cast<float*>(ws);
+  const uint64_t blocks = (L.b.n_tiles + kGenericWaves - 1) / kGenericWaves;
+  const unsigned grid = static_cast<unsigned>(std::min<uint64_t>(blocks, kCUs * 8));
+  k_gemv_generic<<<grid, kGenericWaves * kWave, lds, s>>>(L.b, X, batch == 1 ? 0 : ldx, batch, part);
   st = launched();
   if (st) return st;
-  return launch_reduce(part, L.b.rows, L.b.n_tc, batch, Y, batch == 1 ? 0 : ldy, yt, s);
+  const uint64_t n = L.b.rows * static_cast<uint64_t>(batch);
+  k_reduce<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(part, L.b.rows, L.b.n_tc, batch, Y,
+                                                                   batch == 1 ? 0 : ldy, y_f32);
+  return launched();
 }
 
 nwc_status nwc_gemv(const nwc_info* info, const void* blob_dev, const uint16_t* x_dev, void* y_dev,
@@ -679,28 +928,25 @@ nwc_status nwc_gemm_skinny(const nwc_info* info, const void* blob_dev, const uin
 
 nwc_status nwc_bf16_workspace_size(uint64_t rows, uint64_t cols, size_t* bytes) {
   if (!bytes || rows < 1 || cols < 1) return NWC_ERR_INVALID_ARG;
-  *bytes = ((cols + 511) / 512) * rows * sizeof(float);
+  *bytes = 0;
   return NWC_OK;
 }
 
 nwc_status nwc_gemv_bf16(const uint16_t* w_dev, uint64_t rows, uint64_t cols, uint64_t ld, const uint16_t* x_dev,
                          void* y_dev, nwc_out_type y_type, void* ws, size_t ws_bytes, void* stream) {
-  if (!w_dev || !x_dev || !y_dev || !ws || rows < 1 || cols < 1 || ld < cols) return NWC_ERR_INVALID_ARG;
+  (void)ws;
+  (void)ws_bytes;
+  if (!w_dev || !x_dev || !y_dev || rows < 1 || cols < 1 || ld < cols) return NWC_ERR_INVALID_ARG;
   if (y_type != NWC_OUT_BF16 && y_type != NWC_OUT_F32) return NWC_ERR_INVALID_ARG;
-  size_t need = 0;
-  nwc_bf16_workspace_size(rows, cols, &need);
-  if (ws_bytes < need) return NWC_ERR_BUFFER_TOO_SMALL;
-  if (cols % 8 || ld % 8 || !aligned(w_dev, 16) || !aligned(x_dev, 16) || !aligned(ws, 16)) return NWC_ERR_ALIGNMENT;
+  if (cols % 8 || ld % 8 || !aligned(w_dev, 16) || !aligned(x_dev, 16)) return NWC_ERR_ALIGNMENT;
   if (!aligned(y_dev, y_type == NWC_OUT_F32 ? 4 : 2)) return NWC_ERR_ALIGNMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint32_t n_tc = static_cast<uint32_t>((cols + 511) / 512);
-  const uint64_t tiles = ((rows + 15) / 16) * n_tc;
-  const unsigned grid = static_cast<unsigned>(std::min<uint64_t>((tiles + kWavesPerBlock - 1) / kWavesPerBlock, 256ull * 8));
-  float* part = static_cast<float*>(ws);
-  k_gemv_bf16<16><<<grid, kThreads, 0, s>>>(w_dev, rows, cols, ld, n_tc, x_dev, part);
-  nwc_status st = launched();
-  if (st) return st;
-  return launch_reduce(part, rows, n_tc, 1, y_dev, 0, y_type, s);
+  const uint64_t n_tr = (rows + 15) / 16;
+  const Split sp = make_split(n_tr, n_tc, kMaxWaves);
+  k_gemv_bf16<16><<<grid_for(sp.items, sp.waves, 4096), sp.waves * kWave, 0, s>>>(
+      w_dev, rows, cols, ld, n_tc, n_tr, sp, x_dev, y_dev, y_type == NWC_OUT_F32 ? 1 : 0);
+  return launched();
 }
 
 }  // extern "C"

@@ -131,17 +131,20 @@ nwc_status nwc_decode(const nwc_info *info, const void *blob_dev, uint16_t *w_de
                       uint64_t ld, void *stream);
 
 /* Workspace bytes needed by nwc_gemv (batch = 1) or nwc_gemm_skinny
- * (batch 2..16) for this blob: FP32 partial sums, one per (column tile,
- * batch row, output row). */
+ * (batch 2..16) for this blob.  0 on the fused paths (default geometry,
+ * cols % 8 == 0), which then accept ws = NULL; otherwise FP32 partial sums,
+ * one per (column tile, batch row, output row), for the one-symbol-at-a-time
+ * path, which runs a second reduction kernel. */
 nwc_status nwc_workspace_size(const nwc_info *info, int batch, size_t *bytes);
 
 /* Fused decode-GEMV (pages: "Fused kernel"; Unweight "Direct GPU
- * Decompression"): y = W x with x (device, cols BF16) and y (device, rows
- * entries of y_type).  Weights are decoded in registers and LDS and never
- * written to memory; products accumulate in FP32 in a fixed order.  ws is a
- * device workspace of at least nwc_workspace_size(info, 1) bytes whose
- * contents need not be initialised.  x and y must not alias.  Async.
- * Errors: INVALID_ARG, BUFFER_TOO_SMALL (ws), ALIGNMENT, HIP. */
+ * Decompression"): y = W x with x (device, cols BF16, 16-byte aligned) and y
+ * (device, rows entries of y_type).  Weights are decoded in registers and
+ * LDS and never written to memory; products accumulate in FP32 in a fixed
+ * order and y is written once.  ws is a device workspace of at least
+ * nwc_workspace_size(info, 1) bytes (NULL if that is 0) whose contents need
+ * not be initialised.  x and y must not alias.  Async.
+ * Errors: INVALID_ARG, BUFFER_TOO_SMALL (ws), ALIGNMENT, UNSUPPORTED, HIP. */
 nwc_status nwc_gemv(const nwc_info *info, const void *blob_dev, const uint16_t *x_dev,
                     void *y_dev, nwc_out_type y_type, void *ws, size_t ws_bytes,
                     void *stream);
@@ -155,9 +158,10 @@ nwc_status nwc_gemm_skinny(const nwc_info *info, const void *blob_dev, const uin
                            nwc_out_type y_type, void *ws, size_t ws_bytes, void *stream);
 
 /* Uncompressed comparator: the same GEMV on a plain BF16 matrix (device,
- * rows x cols, row stride ld), with the same tiling, summation order and
- * workspace layout (nwc_workspace_size of a blob of that shape with default
- * parameters, or nwc_bf16_workspace_size).  Async. */
+ * rows x cols, row stride ld, cols and ld multiples of 8), with the same
+ * tiling, work split, loads and summation order as the fused kernel, reading
+ * 2 bytes per weight instead of decoding.  nwc_bf16_workspace_size reports
+ * its workspace (currently 0: ws may be NULL).  Async. */
 nwc_status nwc_bf16_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
 nwc_status nwc_gemv_bf16(const uint16_t *w_dev, uint64_t rows, uint64_t cols, uint64_t ld,
                          const uint16_t *x_dev, void *y_dev, nwc_out_type y_type, void *ws,

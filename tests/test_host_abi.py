@@ -153,6 +153,7 @@ def test_encode_errors():
 
 
 def test_workspace_sizes():
+    # generic geometry (cols % 8 != 0): partial sums per column tile
     blob = nwc.nwc_encode(workloads.gaussian_bits((100, 1500), 0.02, 2))
     info = nwc.nwc_inspect(blob)
     assert nwc.nwc_workspace_size(info, 1) == 3 * 100 * 4
@@ -160,36 +161,52 @@ def test_workspace_sizes():
     for bad in (0, 17):
         with pytest.raises(nwc.NwcError):
             nwc.nwc_workspace_size(info, bad)
-    assert nwc.nwc_bf16_workspace_size(100, 1500) == 3 * 100 * 4
+    # fused paths need none
+    fast = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2)))
+    assert nwc.nwc_workspace_size(fast, 1) == 0 and nwc.nwc_workspace_size(fast, 8) == 0
+    tr8 = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2), dict(tile_rows=8)))
+    assert nwc.nwc_workspace_size(tr8, 1) == 0 and nwc.nwc_workspace_size(tr8, 8) == 3 * 8 * 100 * 4
+    assert nwc.nwc_bf16_workspace_size(100, 1500) == 0
 
 
 def test_device_calls_validate_before_launch():
-    # Every failure below is detected on the host, so these run without a GPU.
+    # Every call below fails on the host before any device work, so it is safe
+    # with fake device addresses (never dereferenced) and runs without a GPU.
+    # Do not add a call here that passes validation: it would launch a kernel
+    # on the fake addresses.
     blob = nwc.nwc_encode(workloads.gaussian_bits((64, 512), 0.02, 2))
     info = nwc.nwc_inspect(blob)
     L = nwc._lib
     ref = ctypes.byref(info)
-    A = 0x10000          # 256-aligned fake device addresses, never dereferenced
-    ws = nwc.nwc_workspace_size(info, 1)
-    assert L.nwc_gemv(None, A, A, A, 0, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, None, A, A, 0, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, A, None, A, 0, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, A, A, A, 0, None, ws, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, A, A, A, 7, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, A, A, A, 0, A, ws - 4, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
-    assert L.nwc_gemv(ref, A + 16, A, A, 0, A, ws, None) == nwc.NWC_ERR_ALIGNMENT
-    assert L.nwc_gemv(ref, A, A, A + 1, 0, A, ws, None) == nwc.NWC_ERR_ALIGNMENT
-    ws16 = nwc.nwc_workspace_size(info, 16)
+    A = 0x10000          # 256-aligned fake device address
+    assert L.nwc_gemv(None, A, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, None, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, None, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, A, None, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, A, A, 7, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A + 16, A, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv(ref, A, A, A + 1, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv(ref, A, A + 2, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT   # x must be 16-aligned
     for batch in (0, 1, 17):
-        assert L.nwc_gemm_skinny(ref, A, A, 512, batch, A, 64, 0, A, ws16, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemm_skinny(ref, A, A, 100, 4, A, 64, 0, A, ws16, None) == nwc.NWC_ERR_INVALID_ARG
+        assert L.nwc_gemm_skinny(ref, A, A, 512, batch, A, 64, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemm_skinny(ref, A, A, 100, 4, A, 64, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemm_skinny(ref, A, A, 512, 4, A, 63, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
     assert L.nwc_decode(ref, A, None, 512, None) == nwc.NWC_ERR_INVALID_ARG
     assert L.nwc_decode(ref, A, A, 100, None) == nwc.NWC_ERR_INVALID_ARG
     assert L.nwc_decode(ref, A + 8, A, 512, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_decode(ref, A, A + 1, 512, None) == nwc.NWC_ERR_ALIGNMENT
     bad = nwc.nwc_info.from_buffer_copy(info)
     bad.n_tiles += 1
-    assert L.nwc_gemv(ctypes.byref(bad), A, A, A, 0, A, ws, None) == nwc.NWC_ERR_INVALID_ARG
-    wsb = nwc.nwc_bf16_workspace_size(64, 512)
-    assert L.nwc_gemv_bf16(A, 64, 512, 500, A, A, 0, A, wsb, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv_bf16(A, 64, 500, 512, A, A, 0, A, wsb, None) == nwc.NWC_ERR_ALIGNMENT
-    assert L.nwc_gemv_bf16(A, 64, 512, 512, A, A, 0, A, wsb - 1, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
+    assert L.nwc_gemv(ctypes.byref(bad), A, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    # the one-symbol-at-a-time path needs its workspace
+    gblob = nwc.nwc_encode(workloads.gaussian_bits((64, 500), 0.02, 2))
+    ginfo = nwc.nwc_inspect(gblob)
+    gws = nwc.nwc_workspace_size(ginfo, 1)
+    assert gws > 0
+    gref = ctypes.byref(ginfo)
+    assert L.nwc_gemv(gref, A, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(gref, A, A, A, 0, A, gws - 4, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
+    assert L.nwc_gemv(gref, A, A, A, 0, A + 4, gws, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_bf16(A, 64, 512, 500, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_bf16(A, 64, 500, 512, A, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_bf16(A, 64, 512, 512, A + 8, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
