@@ -76,13 +76,16 @@ _lib.nwc_gemv.argtypes = [ctypes.POINTER(nwc_info), _vp, _vp, _vp, _i, _vp, _sz,
 _lib.nwc_gemm_skinny.argtypes = [ctypes.POINTER(nwc_info), _vp, _vp, _u64, _i, _vp, _u64, _i, _vp, _sz, _vp]
 _lib.nwc_bf16_workspace_size.argtypes = [_u64, _u64, ctypes.POINTER(_sz)]
 _lib.nwc_gemv_bf16.argtypes = [_vp, _u64, _u64, _u64, _vp, _vp, _i, _vp, _sz, _vp]
+_lib.nwc_gemv_batched.argtypes = [_i, ctypes.POINTER(nwc_info), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                  ctypes.POINTER(_vp), _i, _vp]
 for _f in ("nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode", "nwc_workspace_size", "nwc_gemv",
-           "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16"):
+           "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched"):
     getattr(_lib, _f).restype = _st
 
 # the exported C symbols, for checks against include/nwc.h
 EXPORTS = ("nwc_status_str", "nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode",
-           "nwc_workspace_size", "nwc_gemv", "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16")
+           "nwc_workspace_size", "nwc_gemv", "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16",
+           "nwc_gemv_batched")
 
 
 def _check(st: int, where: str):
@@ -201,6 +204,32 @@ def nwc_gemv(info: nwc_info, blob_dev, x_dev, y_dev, ws=None, stream=None):
     wp, wn = _ws(ws)
     _check(_lib.nwc_gemv(ctypes.byref(info), _dptr(blob_dev), _dptr(x_dev), _dptr(y_dev), _ytype(y_dev),
                          wp, wn, _stream(stream)), "nwc_gemv")
+
+
+class GemvBatch:
+    """Marshalled arguments of one nwc_gemv_batched call, built once and reusable
+    (e.g. inside a captured graph).  Keeps the tensors alive."""
+
+    def __init__(self, infos, blobs_dev, xs_dev, ys_dev):
+        n = len(infos)
+        if not (n == len(blobs_dev) == len(xs_dev) == len(ys_dev)) or n < 1:
+            raise ValueError("need equal, non-empty lists")
+        self.count = n
+        self.infos = (nwc_info * n)(*infos)
+        self.blobs = (_vp * n)(*[_dptr(t).value for t in blobs_dev])
+        self.xs = (_vp * n)(*[_dptr(t).value for t in xs_dev])
+        self.ys = (_vp * n)(*[_dptr(t).value for t in ys_dev])
+        ytypes = {_ytype(t) for t in ys_dev}
+        if len(ytypes) != 1:
+            raise ValueError("all outputs must have one dtype")
+        self.ytype = ytypes.pop()
+        self._keep = (list(blobs_dev), list(xs_dev), list(ys_dev))
+
+
+def nwc_gemv_batched(batch: GemvBatch, stream=None):
+    """Independent GEMVs y_i = W_i x_i in one launch (see GemvBatch)."""
+    _check(_lib.nwc_gemv_batched(batch.count, batch.infos, batch.blobs, batch.xs, batch.ys, batch.ytype,
+                                 _stream(stream)), "nwc_gemv_batched")
 
 
 def nwc_gemm_skinny(info: nwc_info, blob_dev, X_dev, Y_dev, ws=None, stream=None):

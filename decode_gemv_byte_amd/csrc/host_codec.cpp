@@ -189,7 +189,7 @@ void build_table(const uint8_t len[256], uint32_t table[4096]) {
 // ------------------------------------------------------------------ geometry
 
 bool params_resolve(const nwc_params* p, Geometry* g) {
-  g->tr = (p && p->tile_rows) ? p->tile_rows : 16;
+  g->tr = (p && p->tile_rows) ? p->tile_rows : 8;
   g->tc = (p && p->tile_cols) ? p->tile_cols : 512;
   g->s = (p && p->chunks_per_tile) ? p->chunks_per_tile : 64;
   g->lmax = (p && p->max_code_len) ? p->max_code_len : 12;

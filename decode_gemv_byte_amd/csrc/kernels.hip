@@ -78,6 +78,11 @@ struct Split {
 };
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+// Wave-uniform read through the constant address space (a scalar load).
+__device__ __forceinline__ uint32_t sload(const uint32_t* p, uint64_t i) {
+  typedef const __attribute__((address_space(4))) uint32_t cu32;
+  return ((cu32*)(reinterpret_cast<uintptr_t>(p)))[i];
+}
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -305,8 +310,8 @@ struct TileIn {
     c0 = static_cast<uint64_t>(tj) * 512 + lane * 8;
     active = c0 < b.cols;
     const uint64_t cc = active ? c0 : 0;
-    w0 = uniform(b.tile_words[t]);
-    const uint32_t w1 = uniform(b.tile_words[t + 1]);
+    w0 = sload(b.tile_words, t);
+    const uint32_t w1 = sload(b.tile_words, t + 1);
     a0 = w0 & ~3u;
     stage_stream(b, a0, stage_blocks(b, a0, w1 < w0 ? w0 : w1), buf);
     cb = b.chunk_bits[t * 64 + lane];
@@ -376,8 +381,8 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDe
     const uint64_t row0 = ti * b.tr;
     const uint64_t r1 = umin64(b.rows, row0 + b.tr);
     const uint64_t tile_c1 = umin64(b.cols, tj * b.tc + b.tc);
-    const uint32_t w0 = uniform(b.tile_words[t]);
-    const uint32_t w1 = uniform(b.tile_words[t + 1]);
+    const uint32_t w0 = sload(b.tile_words, t);
+    const uint32_t w1 = sload(b.tile_words, t + 1);
     const uint32_t a0 = w0 & ~3u;
     stage_stream(b, a0, stage_blocks(b, a0, w1 < w0 ? w0 : w1), buf);
     wait_vmem();
@@ -410,17 +415,33 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDe
 
 // -------------------------------------------------------------------- GEMV
 
-// One tile of the fused GEMV: adds the tile's row sums (this lane's 8
-// columns) into acc.
+// One matrix of a grouped fused-GEMV launch.  A work item is `rb` row blocks
+// with all their column tiles (rb * n_tc tiles, numbered row block by row
+// block); the workgroup's wavefronts take the item's tiles round robin.
+struct GemvJob {
+  BlobDev b;
+  const uint16_t* x;
+  void* y;
+  uint32_t rb;
+  uint64_t item0;  // first work item of this matrix in the launch
+};
+constexpr int kMaxJobs = 8;
+constexpr int kGemvWaves = 8;        // wavefronts per workgroup
+constexpr int kMaxItemTiles = 64;    // LDS slots for per-tile row sums
+struct GemvGroup {
+  GemvJob job[kMaxJobs];
+  uint32_t count;
+  uint64_t items;
+  int y_f32;
+};
+
+// Decode one tile already staged (stream in LDS, raw bytes and x in
+// registers) and return this lane's TR row sums over its 8 columns.
 template <int TR>
-__device__ __forceinline__ void gemv_tile(const BlobDev& b, uint64_t ti, uint32_t tj, const uint16_t* __restrict__ x,
-                                          uint32_t* buf, const uint32_t* tab, float (&acc)[TR]) {
-  TileIn<TR> in;
-  in.load(b, ti, tj, buf);
-  const uint4 xv = *reinterpret_cast<const uint4*>(x + (in.active ? in.c0 : 0));
-  const uint32_t bit = in.start_bit();
-  wait_vmem();
-  wave_sync_lds();
+__device__ __forceinline__ void gemv_tile_sums(const TileIn<TR>& in, const uint4& xv, uint32_t bit,
+                                               const uint32_t* tab, const uint32_t* buf, float (&acc)[TR]) {
+#pragma unroll
+  for (int r = 0; r < TR; r++) acc[r] = 0.0f;
   if (in.active) {
     // Rows past the matrix edge (last row block only) are decoded from
     // whatever follows the chunk and multiplied too: raw loads were clamped to
@@ -430,7 +451,7 @@ __device__ __forceinline__ void gemv_tile(const BlobDev& b, uint64_t ti, uint32_
     br.init(buf, bit);
 #pragma unroll
     for (int r = 0; r < TR; r++) {
-      float a = acc[r];
+      float a = 0.0f;
       a = dot2(assemble(br.pair(tab, buf), in.raw[r].x, false), xv.x, a);
       a = dot2(assemble(br.pair(tab, buf), in.raw[r].x, true), xv.y, a);
       a = dot2(assemble(br.pair(tab, buf), in.raw[r].y, false), xv.z, a);
@@ -438,56 +459,95 @@ __device__ __forceinline__ void gemv_tile(const BlobDev& b, uint64_t ti, uint32_
       acc[r] = a;
     }
   }
-  wave_sync_lds();
 }
 
-// Fused decode-GEMV, batch 1, y written directly.
-// LDS: table | per-wavefront row sums [waves][TR] | stream buffers.
+// Grouped fused decode-GEMV, batch 1: y_j = W_j x_j for every job j.
+// LDS: per-tile row sums [kMaxItemTiles][TR] | stream buffers [waves][2][buf_words].
 template <int TR>
-__global__ __launch_bounds__(kMaxWaves * kWave) void k_gemv(BlobDev b, Split sp, const uint16_t* __restrict__ x,
-                                                            void* __restrict__ y, int y_f32) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+__global__ __launch_bounds__(kGemvWaves * kWave) void k_gemv_group(const GemvGroup g, uint32_t buf_words) {
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
-  float* red = reinterpret_cast<float*>(lds);
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  float* sums = reinterpret_cast<float*>(lds);
+  const uint32_t nwaves = blockDim.x / kWave;
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t lane = lane_id();
-  uint32_t* buf = lds + kMaxWaves * TR + wave * b.buf_words;
-  load_table(tab, b.table);
-  __syncthreads();
-  const uint32_t rbl = wave / sp.nw, wt = wave % sp.nw;
-  for (uint64_t item = blockIdx.x; item < sp.items; item += gridDim.x) {
-    const uint64_t ti = item * sp.rb + rbl;
-    float acc[TR];
+  uint32_t* bufs = lds + kMaxItemTiles * TR + wave * 2 * buf_words;
+  int cur = -1;
+  for (uint64_t item = blockIdx.x; item < g.items; item += gridDim.x) {
+    int j = 0;
+    while (j + 1 < static_cast<int>(g.count) && item >= g.job[j + 1].item0) j++;
+    // select the job with compile-time indices (no dynamic indexing of the
+    // kernel-argument struct, which would copy it to scratch)
+    GemvJob job = g.job[0];
 #pragma unroll
-    for (int r = 0; r < TR; r++) acc[r] = 0.0f;
-    if (ti < b.n_tr) {
-      for (uint32_t tj = wt; tj < b.n_tc; tj += sp.nw) gemv_tile<TR>(b, ti, tj, x, buf, tab, acc);
+    for (int jj = 1; jj < kMaxJobs; jj++)
+      if (jj == j) job = g.job[jj];
+    const BlobDev& b = job.b;
+    if (j != cur) {  // a new matrix: its decode table
+      __syncthreads();
+      load_table(tab, b.table);
+      __syncthreads();
+      cur = j;
     }
-    const float s = reduce_rows<TR>(acc);
-    constexpr uint32_t lanes_per_row = kWave / TR;
-    if ((lane & (lanes_per_row - 1)) == 0) red[wave * TR + lane / lanes_per_row] = s;
+    const uint64_t tb0 = (item - job.item0) * job.rb;           // first row block of the item
+    const uint64_t nrb = umin64(job.rb, b.n_tr - tb0);           // row blocks in this item
+    const uint32_t ntiles = static_cast<uint32_t>(nrb) * b.n_tc;
+    // tiles of this wavefront: wave, wave + nwaves, ...; the next tile's loads
+    // are in flight while the current one decodes
+    uint32_t k = wave;
+    int slot = 0;
+    TileIn<TR> in;
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    if (k < ntiles) {
+      in.load(b, tb0 + k / b.n_tc, k % b.n_tc, bufs);
+      xv = *reinterpret_cast<const uint4*>(job.x + (in.active ? in.c0 : 0));
+    }
+    while (k < ntiles) {
+      const uint32_t bit = in.start_bit();
+      wait_vmem();
+      wave_sync_lds();
+      const uint32_t kn = k + nwaves;
+      TileIn<TR> nx;
+      uint4 xn = make_uint4(0, 0, 0, 0);
+      if (kn < ntiles) {
+        nx.load(b, tb0 + kn / b.n_tc, kn % b.n_tc, bufs + (slot ^ 1) * buf_words);
+        xn = *reinterpret_cast<const uint4*>(job.x + (nx.active ? nx.c0 : 0));
+      }
+      float acc[TR];
+      gemv_tile_sums<TR>(in, xv, bit, tab, bufs + slot * buf_words, acc);
+      const float s = reduce_rows<TR>(acc);
+      constexpr uint32_t lanes_per_row = kWave / TR;
+      if ((lane & (lanes_per_row - 1)) == 0) sums[k * TR + lane / lanes_per_row] = s;
+      wave_sync_lds();
+      in = nx;
+      xv = xn;
+      k = kn;
+      slot ^= 1;
+    }
     __syncthreads();
-    if (threadIdx.x < sp.rb * TR) {
-      const uint32_t rl = threadIdx.x / TR, r = threadIdx.x % TR;
-      const uint64_t row = (item * sp.rb + rl) * TR + r;
+    // row r of the item's row block i: add its column tiles in order
+    for (uint32_t t = threadIdx.x; t < nrb * TR; t += blockDim.x) {
+      const uint32_t i = t / TR, r = t % TR;
+      const uint64_t row = (tb0 + i) * TR + r;
       if (row < b.rows) {
         float sum = 0.0f;
-        for (uint32_t w = 0; w < sp.nw; w++) sum += red[(rl * sp.nw + w) * TR + r];
-        store_y(y, row, sum, y_f32);
+        for (uint32_t tj = 0; tj < b.n_tc; tj++) sum += sums[(i * b.n_tc + tj) * TR + r];
+        store_y(job.y, row, sum, g.y_f32);
       }
     }
     __syncthreads();
   }
 }
 
-// Skinny decode-GEMM with MFMA, batch 2..16, TR = 16; one row block per work
-// item, its column tiles split across the workgroup's wavefronts.
+// Skinny decode-GEMM with MFMA, batch 2..16, TR = 8 or 16 (the 16-row MFMA
+// operand is padded with zero rows for TR = 8); one row block per work item,
+// its column tiles split across the workgroup's wavefronts.
 // LDS: table | per-wavefront D [waves][16][16] | stream buffers | decoded
 // tiles [waves][16][kMfmaRowPad].
-__global__ __launch_bounds__(kMaxWaves * kWave) void k_gemm_mfma(BlobDev b, Split sp, const uint16_t* __restrict__ X,
+template <int TR>
+__global__ __launch_bounds__(kMaxWaves * kWave) void k_gemm_mfma(BlobDev b, const uint16_t* __restrict__ X,
                                                                  uint64_t ldx, int batch, void* __restrict__ Y,
                                                                  uint64_t ldy, int y_f32) {
-  constexpr int TR = 16;
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
   float* red = reinterpret_cast<float*>(lds);
@@ -496,7 +556,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void k_gemm_mfma(BlobDev b, Spli
   const uint32_t lane = lane_id();
   uint32_t* buf = lds + nwaves * 256 + wave * b.buf_words;
   uint16_t* wt_lds = reinterpret_cast<uint16_t*>(lds + nwaves * 256 + nwaves * b.buf_words) +
-                     wave * static_cast<size_t>(TR) * kMfmaRowPad;
+                     wave * static_cast<size_t>(16) * kMfmaRowPad;
   load_table(tab, b.table);
   __syncthreads();
   const uint32_t mrow = lane % 16, kq = lane / 16;  // MFMA A: weight row, 8-column group
@@ -532,6 +592,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void k_gemm_mfma(BlobDev b, Spli
         // contraction); rows past the edge only reach rows that are not stored
         *reinterpret_cast<uint4*>(wt_lds + r * kMfmaRowPad + lane * 8) = o;
       }
+#pragma unroll
+      for (int r = TR; r < 16; r++)  // padding rows of the 16-row operand
+        *reinterpret_cast<uint4*>(wt_lds + r * kMfmaRowPad + lane * 8) = make_uint4(0, 0, 0, 0);
       wave_sync_lds();
 #pragma unroll
       for (int kb = 0; kb < 16; kb++) {
@@ -548,7 +611,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void k_gemm_mfma(BlobDev b, Spli
     for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
       const uint32_t r = i / 16, beta = i % 16;
       const uint64_t row = ti * TR + r;
-      if (static_cast<int>(beta) < batch && row < b.rows) {
+      if (static_cast<int>(beta) < batch && r < TR && row < b.rows) {
         float sum = 0.0f;
         for (uint32_t w = 0; w < nwaves; w++) sum += red[w * 256 + i];
         store_y(Y, beta * ldy + row, sum, y_f32);
@@ -578,8 +641,8 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_gemv_generic(BlobDev 
     const uint64_t row0 = ti * b.tr;
     const uint32_t nrows = static_cast<uint32_t>(umin64(b.tr, b.rows - row0));
     const uint64_t tile_c1 = umin64(b.cols, tj * b.tc + b.tc);
-    const uint32_t w0 = uniform(b.tile_words[t]);
-    const uint32_t w1 = uniform(b.tile_words[t + 1]);
+    const uint32_t w0 = sload(b.tile_words, t);
+    const uint32_t w1 = sload(b.tile_words, t + 1);
     const uint32_t a0 = w0 & ~3u;
     stage_stream(b, a0, stage_blocks(b, a0, w1 < w0 ? w0 : w1), buf);
     wait_vmem();
@@ -773,13 +836,43 @@ unsigned grid_for(uint64_t items, uint32_t waves, size_t lds) {
   return static_cast<unsigned>(std::min<uint64_t>(items, kCUs * per_cu));
 }
 
+// Row blocks per work item: about two tiles per wavefront, within the LDS
+// slots for per-tile sums.
+uint32_t rows_per_item(uint32_t n_tc) {
+  uint32_t rb = std::max<uint32_t>(1, (2 * kGemvWaves + n_tc / 2) / n_tc);
+  while (rb > 1 && rb * n_tc > kMaxItemTiles) rb--;
+  return rb;
+}
+
 template <int TR>
-nwc_status launch_gemv(const Launch& L, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
-  const Split sp = make_split(L.b.n_tr, L.b.n_tc, kMaxWaves);
-  const size_t lds = (kMaxWaves * TR + static_cast<size_t>(sp.waves) * L.b.buf_words) * 4;
+nwc_status launch_gemv_group(const Launch* L, const uint16_t* const* x, void* const* y, int count, int y_f32,
+                             hipStream_t s) {
+  GemvGroup g;
+  std::memset(&g, 0, sizeof(g));
+  uint32_t buf_words = 0;
+  uint64_t items = 0;
+  for (int j = 0; j < count; j++) {
+    if (L[j].b.n_tc > kMaxItemTiles) return NWC_ERR_UNSUPPORTED;
+    buf_words = std::max(buf_words, L[j].b.buf_words);
+  }
+  for (int j = 0; j < count; j++) {
+    GemvJob& job = g.job[j];
+    job.b = L[j].b;
+    job.b.buf_words = buf_words;
+    job.x = x[j];
+    job.y = y[j];
+    job.rb = rows_per_item(job.b.n_tc);
+    job.item0 = items;
+    items += (job.b.n_tr + job.rb - 1) / job.rb;
+  }
+  g.count = static_cast<uint32_t>(count);
+  g.items = items;
+  g.y_f32 = y_f32;
+  const size_t lds = (static_cast<size_t>(kMaxItemTiles) * TR + 2ull * kGemvWaves * buf_words) * 4;
   if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
-  if (set_lds(k_gemv<TR>, lds) != hipSuccess) return NWC_ERR_HIP;
-  k_gemv<TR><<<grid_for(sp.items, sp.waves, lds), sp.waves * kWave, lds, s>>>(L.b, sp, x, y, y_f32);
+  if (set_lds(k_gemv_group<TR>, lds) != hipSuccess) return NWC_ERR_HIP;
+  const unsigned grid = grid_for(items, kGemvWaves, lds);
+  k_gemv_group<TR><<<grid, kGemvWaves * kWave, lds, s>>>(g, buf_words);
   return launched();
 }
 
@@ -821,7 +914,7 @@ nwc_status nwc_workspace_size(const nwc_info* info, int batch, size_t* bytes) {
   nwc::Geometry g;
   if (!info || !bytes || batch < 1 || batch > 16 || !nwc::info_geometry(info, &g)) return NWC_ERR_INVALID_ARG;
   const bool fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
-  const bool fused = fast && (batch == 1 || g.tr == 16);
+  const bool fused = fast && (batch == 1 || g.tr == 8 || g.tr == 16);
   *bytes = fused ? 0 : generic_ws_bytes(g, batch);
   return NWC_OK;
 }
@@ -881,10 +974,11 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
   const bool xvec = aligned(X, 16) && (batch == 1 || ldx % 8 == 0);
   if (need == 0 && !xvec) return NWC_ERR_ALIGNMENT;
   if (need == 0 && batch == 1) {
+    void* yy = Y;
     switch (L.b.tr) {
-      case 8: return launch_gemv<8>(L, X, Y, y_f32, s);
-      case 16: return launch_gemv<16>(L, X, Y, y_f32, s);
-      default: return launch_gemv<32>(L, X, Y, y_f32, s);
+      case 8: return launch_gemv_group<8>(&L, &X, &yy, 1, y_f32, s);
+      case 16: return launch_gemv_group<16>(&L, &X, &yy, 1, y_f32, s);
+      default: return launch_gemv_group<32>(&L, &X, &yy, 1, y_f32, s);
     }
   }
   if (need == 0) {
@@ -892,10 +986,14 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
     const size_t lds = (nw * 256 + static_cast<size_t>(nw) * L.b.buf_words) * 4 +
                        static_cast<size_t>(nw) * 16 * kMfmaRowPad * 2;
     if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
-    if (set_lds(k_gemm_mfma, lds) != hipSuccess) return NWC_ERR_HIP;
-    Split sp = make_split(L.b.n_tr, L.b.n_tc, nw);
     const unsigned grid = static_cast<unsigned>(std::min<uint64_t>(L.b.n_tr, kCUs * 2));
-    k_gemm_mfma<<<grid, nw * kWave, lds, s>>>(L.b, sp, X, ldx, batch, Y, ldy, y_f32);
+    if (L.b.tr == 8) {
+      if (set_lds(k_gemm_mfma<8>, lds) != hipSuccess) return NWC_ERR_HIP;
+      k_gemm_mfma<8><<<grid, nw * kWave, lds, s>>>(L.b, X, ldx, batch, Y, ldy, y_f32);
+    } else {
+      if (set_lds(k_gemm_mfma<16>, lds) != hipSuccess) return NWC_ERR_HIP;
+      k_gemm_mfma<16><<<grid, nw * kWave, lds, s>>>(L.b, X, ldx, batch, Y, ldy, y_f32);
+    }
     return launched();
   }
   // generic path: partial sums per column tile, then a reduction
@@ -918,6 +1016,27 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
 nwc_status nwc_gemv(const nwc_info* info, const void* blob_dev, const uint16_t* x_dev, void* y_dev,
                     nwc_out_type y_type, void* ws, size_t ws_bytes, void* stream) {
   return gemm_common(info, blob_dev, x_dev, 0, 1, y_dev, 0, y_type, ws, ws_bytes, stream);
+}
+
+nwc_status nwc_gemv_batched(int count, const nwc_info* infos, const void* const* blobs_dev,
+                            const uint16_t* const* x_dev, void* const* y_dev, nwc_out_type y_type, void* stream) {
+  if (count < 1 || count > kMaxJobs || !infos || !blobs_dev || !x_dev || !y_dev) return NWC_ERR_INVALID_ARG;
+  if (y_type != NWC_OUT_BF16 && y_type != NWC_OUT_F32) return NWC_ERR_INVALID_ARG;
+  Launch L[kMaxJobs];
+  for (int j = 0; j < count; j++) {
+    if (!x_dev[j] || !y_dev[j]) return NWC_ERR_INVALID_ARG;
+    nwc_status st = prepare(&infos[j], blobs_dev[j], &L[j]);
+    if (st) return st;
+    if (!L[j].fast || L[j].b.tr != L[0].b.tr) return NWC_ERR_UNSUPPORTED;
+    if (!aligned(x_dev[j], 16) || !aligned(y_dev[j], y_type == NWC_OUT_F32 ? 4 : 2)) return NWC_ERR_ALIGNMENT;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int y_f32 = y_type == NWC_OUT_F32 ? 1 : 0;
+  switch (L[0].b.tr) {
+    case 8: return launch_gemv_group<8>(L, x_dev, y_dev, count, y_f32, s);
+    case 16: return launch_gemv_group<16>(L, x_dev, y_dev, count, y_f32, s);
+    default: return launch_gemv_group<32>(L, x_dev, y_dev, count, y_f32, s);
+  }
 }
 
 nwc_status nwc_gemm_skinny(const nwc_info* info, const void* blob_dev, const uint16_t* X_dev, uint64_t ldx, int batch,

@@ -74,7 +74,7 @@ typedef enum {
  * Constraints: tile_cols % chunks_per_tile == 0, 8 <= max_code_len <= 12,
  * tile_rows * (tile_cols / chunks_per_tile) * max_code_len <= 65535. */
 typedef struct {
-  uint32_t tile_rows;       /* TR rows per tile [16] */
+  uint32_t tile_rows;       /* TR rows per tile [8] */
   uint32_t tile_cols;       /* TC columns per tile [512] */
   uint32_t chunks_per_tile; /* S column-strip chunks per tile [64] */
   uint32_t max_code_len;    /* L, longest code in bits [12] */
@@ -148,6 +148,19 @@ nwc_status nwc_workspace_size(const nwc_info *info, int batch, size_t *bytes);
 nwc_status nwc_gemv(const nwc_info *info, const void *blob_dev, const uint16_t *x_dev,
                     void *y_dev, nwc_out_type y_type, void *ws, size_t ws_bytes,
                     void *stream);
+
+/* Several independent fused decode-GEMVs in one launch (count <= 8):
+ * y_i = W_i x_i with blob i described by infos[i] and stored at blobs_dev[i],
+ * x_dev[i] / y_dev[i] as for nwc_gemv, all outputs of y_type.  For the GEMVs
+ * of one decode step that need no result of each other (q/k/v from the same
+ * activations, gate/up), one launch keeps the whole GPU busy where separate
+ * small launches each pay a start-up and a tail.  Every blob must be on the
+ * fused path (nwc_workspace_size 0) and all must share tile_rows; each y_i is
+ * bitwise identical to what nwc_gemv computes for it.  Async.
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, HIP. */
+nwc_status nwc_gemv_batched(int count, const nwc_info *infos, const void *const *blobs_dev,
+                            const uint16_t *const *x_dev, void *const *y_dev, nwc_out_type y_type,
+                            void *stream);
 
 /* Skinny decode-GEMM for batch 2..16: Y[b, n] = sum_k X[b, k] W[n, k] with X
  * (device, batch x cols, row stride ldx) and Y (device, batch x rows, row

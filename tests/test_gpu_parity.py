@@ -96,7 +96,7 @@ def _special(name):
     }[name]()
 
 
-DECODE_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=8)), ("cfg1", dict(tile_rows=32)),
+DECODE_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=16)), ("cfg1", dict(tile_rows=32)),
                 ("cfg1", dict(tile_rows=5, tile_cols=24, chunks_per_tile=3, max_code_len=11)),
                 ("all_patterns", None), ("127x1001", None), ("1x1", None), ("1000x256", None),
                 ("nan_payloads", None), ("subnormal", None), ("one_symbol", None), ("random_bits", None),
@@ -131,7 +131,7 @@ def test_decode_padded_leading_dimension():
 def test_decode_oracle_written_blob():
     # the GPU decoder follows the format, not just the library's encoder
     w = _w(1, "w")
-    host = oracle.encode(w, 16, 512, 64, 12)
+    host = oracle.encode(w, 8, 512, 64, 12)
     info = nwc.nwc_inspect(host)
     out = torch.empty(w.shape, dtype=torch.int16, device="cuda")
     nwc.nwc_decode(info, dev(host), out)
@@ -141,7 +141,7 @@ def test_decode_oracle_written_blob():
 
 # ------------------------------------------------------------------- GEMV --
 
-GEMV_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=8)), ("cfg1", dict(tile_rows=32)),
+GEMV_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=16)), ("cfg1", dict(tile_rows=32)),
               ("cfg1", dict(tile_rows=5, tile_cols=24, chunks_per_tile=3, max_code_len=11)),
               ("127x1001", None), ("1x1", None), ("1000x256", None), ("subnormal", None),
               ("one_symbol", None), ("wide_odd", None)]
@@ -223,6 +223,40 @@ def test_gemv_lm_head_sampled():
         assert np.all(np.isfinite(y))
 
 
+def test_gemv_batched_equals_single_calls():
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    blobs = [Blob(_w(2, n)) for n in names]
+    xs = [dev(workloads.activations(2, n)[0]) for n in names]
+    for out_f32 in (False, True):
+        dt = torch.float32 if out_f32 else torch.bfloat16
+        ys = [torch.empty(b.info.rows, dtype=dt, device="cuda") for b in blobs]
+        batch = nwc.GemvBatch([b.info for b in blobs], [b.dev for b in blobs], xs, ys)
+        _say("gemv_batched 7 matrices f32=%s" % out_f32)
+        nwc.nwc_gemv_batched(batch)
+        torch.cuda.synchronize()
+        for b, x, y, n in zip(blobs, xs, ys, names):
+            y1 = torch.empty_like(y)
+            nwc.nwc_gemv(b.info, b.dev, x, y1)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16) if not out_f32 else y.view(torch.int32),
+                               y1.view(torch.int16) if not out_f32 else y1.view(torch.int32)), n
+            y_ref, a_ref = oracle.gemv(b.w, x.cpu().numpy())
+            _check_y(_to_f64(y), y_ref, a_ref, out_f32, n)
+
+
+def test_gemv_batched_mixed_shapes_and_edges():
+    ws = [workloads.gaussian_bits((1000, 256), 0.02, 1), workloads.gaussian_bits((37, 1024), 0.05, 2),
+          workloads.gaussian_bits((300, 2048), 0.01, 3)]
+    blobs = [Blob(w) for w in ws]
+    xs = [dev(workloads.gaussian_bits((w.shape[1],), 1.0, 5 + i)) for i, w in enumerate(ws)]
+    ys = [torch.empty(w.shape[0], dtype=torch.float32, device="cuda") for w in ws]
+    nwc.nwc_gemv_batched(nwc.GemvBatch([b.info for b in blobs], [b.dev for b in blobs], xs, ys))
+    torch.cuda.synchronize()
+    for w, x, y in zip(ws, xs, ys):
+        y_ref, a_ref = oracle.gemv(w, x.cpu().numpy())
+        _check_y(_to_f64(y), y_ref, a_ref, True, str(w.shape))
+
+
 # ------------------------------------------------------------ skinny GEMM --
 
 def _gemm(blob: Blob, X: np.ndarray, out_f32: bool):
@@ -236,7 +270,8 @@ def _gemm(blob: Blob, X: np.ndarray, out_f32: bool):
 
 @pytest.mark.parametrize("batch", [2, 3, 4, 8, 16])
 @pytest.mark.parametrize("name,params", [("cfg1", None), ("127x1001", None), ("1000x256", None),
-                                         ("cfg1", dict(tile_rows=8)), ("wide_odd", None)])
+                                         ("cfg1", dict(tile_rows=16)), ("1000x256", dict(tile_rows=16)),
+                                         ("cfg1", dict(tile_rows=32)), ("wide_odd", None)])
 def test_gemm_small(name, params, batch):
     w = _special(name)
     X = workloads.gaussian_bits((batch, w.shape[1]), 1.0, 12)

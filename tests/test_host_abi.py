@@ -16,7 +16,7 @@ import workloads
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nwc.h")
 
-DEFAULT = dict(tile_rows=16, tile_cols=512, chunks_per_tile=64, max_code_len=12)
+DEFAULT = dict(tile_rows=8, tile_cols=512, chunks_per_tile=64, max_code_len=12)
 
 
 def _declared_functions():
@@ -49,7 +49,7 @@ def _oracle_blob(w, p):
     return oracle.encode(w, q["tile_rows"], q["tile_cols"], q["chunks_per_tile"], q["max_code_len"])
 
 
-GEOMS = [None, dict(tile_rows=8), dict(tile_rows=32), dict(tile_rows=5, tile_cols=24, chunks_per_tile=3,
+GEOMS = [None, dict(tile_rows=16), dict(tile_rows=32), dict(tile_rows=5, tile_cols=24, chunks_per_tile=3,
                                                               max_code_len=11),
          dict(tile_rows=3, tile_cols=7, chunks_per_tile=7, max_code_len=10), dict(max_code_len=8)]
 
@@ -163,9 +163,13 @@ def test_workspace_sizes():
             nwc.nwc_workspace_size(info, bad)
     # fused paths need none
     fast = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2)))
-    assert nwc.nwc_workspace_size(fast, 1) == 0 and nwc.nwc_workspace_size(fast, 8) == 0
-    tr8 = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2), dict(tile_rows=8)))
-    assert nwc.nwc_workspace_size(tr8, 1) == 0 and nwc.nwc_workspace_size(tr8, 8) == 3 * 8 * 100 * 4
+    assert nwc.nwc_workspace_size(fast, 1) == 0
+    tr16 = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2), dict(tile_rows=16)))
+    assert nwc.nwc_workspace_size(tr16, 1) == 0 and nwc.nwc_workspace_size(tr16, 8) == 0
+    assert nwc.nwc_workspace_size(fast, 8) == 0
+    # batch > 1 with tile_rows 32 takes the generic path
+    tr32 = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2), dict(tile_rows=32)))
+    assert nwc.nwc_workspace_size(tr32, 1) == 0 and nwc.nwc_workspace_size(tr32, 8) == 3 * 8 * 100 * 4
     assert nwc.nwc_bf16_workspace_size(100, 1500) == 0
 
 
@@ -210,3 +214,19 @@ def test_device_calls_validate_before_launch():
     assert L.nwc_gemv_bf16(A, 64, 512, 500, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
     assert L.nwc_gemv_bf16(A, 64, 500, 512, A, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
     assert L.nwc_gemv_bf16(A, 64, 512, 512, A + 8, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    # grouped launch: count, NULL arrays, per-entry checks, geometry mix
+    infos = (nwc.nwc_info * 2)(info, info)
+    V2 = ctypes.c_void_p * 2
+    ok = V2(A, A)
+    for count in (0, 9):
+        assert L.nwc_gemv_batched(count, infos, ok, ok, ok, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_batched(2, None, ok, ok, ok, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_batched(2, infos, ok, ok, ok, 5, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_batched(2, infos, ok, V2(A, None), ok, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_batched(2, infos, V2(A, A + 16), ok, ok, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_batched(2, infos, ok, V2(A, A + 4), ok, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    mixed = (nwc.nwc_info * 2)(info, nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((64, 512), 0.02, 2),
+                                                                      dict(tile_rows=16))))
+    assert L.nwc_gemv_batched(2, mixed, ok, ok, ok, 0, None) == nwc.NWC_ERR_UNSUPPORTED
+    gen = (nwc.nwc_info * 2)(info, ginfo)
+    assert L.nwc_gemv_batched(2, gen, ok, ok, ok, 0, None) == nwc.NWC_ERR_UNSUPPORTED
