@@ -77,7 +77,7 @@ _lib.nwc_gemm_skinny.argtypes = [ctypes.POINTER(nwc_info), _vp, _vp, _u64, _i, _
 _lib.nwc_bf16_workspace_size.argtypes = [_u64, _u64, ctypes.POINTER(_sz)]
 _lib.nwc_gemv_bf16.argtypes = [_vp, _u64, _u64, _u64, _vp, _vp, _i, _vp, _sz, _vp]
 _lib.nwc_gemv_batched.argtypes = [_i, ctypes.POINTER(nwc_info), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
-                                  ctypes.POINTER(_vp), _i, _vp]
+                                  ctypes.POINTER(_vp), _i, _vp, _sz, _vp]
 for _f in ("nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode", "nwc_workspace_size", "nwc_gemv",
            "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched"):
     getattr(_lib, _f).restype = _st
@@ -200,17 +200,26 @@ def _ws(ws):
 
 def nwc_gemv(info: nwc_info, blob_dev, x_dev, y_dev, ws=None, stream=None):
     """y = W x; y_dev float32 or bfloat16 (rows); ws a device byte tensor of
-    nwc_workspace_size(info, 1) bytes, or None when that size is 0."""
+    nwc_workspace_size(info, 1) bytes (zero-filled before its first use on the
+    fused path), or None when that size is 0."""
     wp, wn = _ws(ws)
     _check(_lib.nwc_gemv(ctypes.byref(info), _dptr(blob_dev), _dptr(x_dev), _dptr(y_dev), _ytype(y_dev),
                          wp, wn, _stream(stream)), "nwc_gemv")
 
 
+def gemv_batched_workspace_size(infos) -> int:
+    """Workspace bytes of one nwc_gemv_batched call over these blobs: the sum
+    of their batch-1 workspace sizes."""
+    return sum(nwc_workspace_size(i, 1) for i in infos)
+
+
 class GemvBatch:
     """Marshalled arguments of one nwc_gemv_batched call, built once and reusable
-    (e.g. inside a captured graph).  Keeps the tensors alive."""
+    (e.g. inside a captured graph).  ws is a device byte tensor of at least
+    gemv_batched_workspace_size(infos) bytes, zero-filled before its first use.
+    Keeps the tensors alive."""
 
-    def __init__(self, infos, blobs_dev, xs_dev, ys_dev):
+    def __init__(self, infos, blobs_dev, xs_dev, ys_dev, ws):
         n = len(infos)
         if not (n == len(blobs_dev) == len(xs_dev) == len(ys_dev)) or n < 1:
             raise ValueError("need equal, non-empty lists")
@@ -223,13 +232,14 @@ class GemvBatch:
         if len(ytypes) != 1:
             raise ValueError("all outputs must have one dtype")
         self.ytype = ytypes.pop()
-        self._keep = (list(blobs_dev), list(xs_dev), list(ys_dev))
+        self.ws, self.ws_bytes = _ws(ws)
+        self._keep = (list(blobs_dev), list(xs_dev), list(ys_dev), ws)
 
 
 def nwc_gemv_batched(batch: GemvBatch, stream=None):
     """Independent GEMVs y_i = W_i x_i in one launch (see GemvBatch)."""
     _check(_lib.nwc_gemv_batched(batch.count, batch.infos, batch.blobs, batch.xs, batch.ys, batch.ytype,
-                                 _stream(stream)), "nwc_gemv_batched")
+                                 batch.ws, batch.ws_bytes, _stream(stream)), "nwc_gemv_batched")
 
 
 def nwc_gemm_skinny(info: nwc_info, blob_dev, X_dev, Y_dev, ws=None, stream=None):

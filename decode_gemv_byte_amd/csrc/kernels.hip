@@ -145,26 +145,28 @@ __device__ __forceinline__ void load_table(uint32_t* lds_table, const uint32_t* 
   wait_vmem();
 }
 
-// Issue the loads that bring tile t's stream words [a0, a0 + 256 * n) into
-// this wavefront's LDS buffer (a0 = first word rounded down to 4 words).
-// Sources past the stream's guard words are redirected to its start; those
-// LDS words are never read for a well-formed blob.
+// Issue the loads that bring stream words [a0, a0 + n) of a tile into this
+// wavefront's LDS buffer (a0 = the tile's first word rounded down to 4 words,
+// n a multiple of 4), 16 bytes per lane.  Sources past the stream's guard
+// words are redirected to its start; those LDS words are never read for a
+// well-formed blob.
 __device__ __forceinline__ void stage_stream(const BlobDev& b, uint32_t a0, uint32_t n, uint32_t* buf) {
   const uint32_t lane = lane_id();
   if (lane < 4) buf[lane] = 0u;  // guard words before the stream
   buf += 4;
-  for (uint32_t j = 0; j < n; j++) {
-    uint32_t g = a0 + 256 * j + 4 * lane;
+  for (uint32_t j = 0; j < n; j += 4 * kWave) {
+    const uint32_t o = j + 4 * lane;
+    uint32_t g = a0 + o;
     g = g + 4 <= b.stream_words + 4 ? g : 0u;
-    __builtin_amdgcn_global_load_lds(b.stream + g, buf + 256 * j, 16, 0, 0);
+    if (o < n) __builtin_amdgcn_global_load_lds(b.stream + g, buf + j, 16, 0, 0);
   }
 }
 
-// Number of 256-word blocks to stage for a tile [w0, w1): covers the bit
-// buffer's two words of look-ahead, capped by the buffer.
+// Words to stage for a tile [w0, w1): through the bit reader's two words of
+// look-ahead, in whole 16-byte pieces, capped by the buffer.
 __device__ __forceinline__ uint32_t stage_blocks(const BlobDev& b, uint32_t a0, uint32_t w1) {
-  uint32_t need = (w1 - a0 + 2 + 255) / 256;
-  const uint32_t cap = (b.buf_words - 4) / 256;
+  const uint32_t need = (w1 - a0 + 2 + 3) & ~3u;
+  const uint32_t cap = b.buf_words - 8;
   return need > cap ? cap : need;
 }
 
@@ -415,23 +417,28 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDe
 
 // -------------------------------------------------------------------- GEMV
 
-// One matrix of a grouped fused-GEMV launch.  A work item is `rb` row blocks
-// with all their column tiles (rb * n_tc tiles, numbered row block by row
-// block); the workgroup's wavefronts take the item's tiles round robin.
+// One matrix of a fused batch-1 launch.  Its tiles, numbered row block by row
+// block (t = i * n_tc + j), are cut into equal contiguous ranges (sizes differ
+// by at most one), one per wavefront of the matrix's `groups` workgroups.  A
+// row block whose tiles all fall in one range is summed in registers.  A row
+// block cut between ranges leaves one sum per tile and row in `part`; the
+// wavefront that completes the row block's last range (counted on `count`)
+// adds them and sets the counter and the sums back to zero, so the workspace
+// is all zero between launches.  Both add a row's tile sums in column order
+// starting from zero, so y does not depend on the cut.
 struct GemvJob {
   BlobDev b;
   const uint16_t* x;
   void* y;
-  uint32_t rb;
-  uint64_t item0;  // first work item of this matrix in the launch
+  float* part;      // [n_tiles][TR] tile sums of cut row blocks
+  uint32_t* count;  // [n_tr] ranges finished per row block
+  uint32_t g0;      // first workgroup of this matrix
+  uint32_t groups;  // workgroups of this matrix
 };
 constexpr int kMaxJobs = 8;
-constexpr int kGemvWaves = 8;        // wavefronts per workgroup
-constexpr int kMaxItemTiles = 64;    // LDS slots for per-tile row sums
 struct GemvGroup {
   GemvJob job[kMaxJobs];
   uint32_t count;
-  uint64_t items;
   int y_f32;
 };
 
@@ -452,90 +459,160 @@ __device__ __forceinline__ void gemv_tile_sums(const TileIn<TR>& in, const uint4
 #pragma unroll
     for (int r = 0; r < TR; r++) {
       float a = 0.0f;
+      // each product is pinned next to its decode step: left alone, the
+      // compiler defers all of them to the end of the tile and keeps every
+      // decoded pair live, which costs occupancy
       a = dot2(assemble(br.pair(tab, buf), in.raw[r].x, false), xv.x, a);
+      asm volatile("" : "+v"(a));
       a = dot2(assemble(br.pair(tab, buf), in.raw[r].x, true), xv.y, a);
+      asm volatile("" : "+v"(a));
       a = dot2(assemble(br.pair(tab, buf), in.raw[r].y, false), xv.z, a);
+      asm volatile("" : "+v"(a));
       a = dot2(assemble(br.pair(tab, buf), in.raw[r].y, true), xv.w, a);
+      asm volatile("" : "+v"(a));
       acc[r] = a;
     }
   }
 }
 
-// Grouped fused decode-GEMV, batch 1: y_j = W_j x_j for every job j.
-// LDS: per-tile row sums [kMaxItemTiles][TR] | stream buffers [waves][2][buf_words].
-template <int TR>
-__global__ __launch_bounds__(kGemvWaves * kWave) void k_gemv_group(const GemvGroup g, uint32_t buf_words) {
+// Data handed between workgroups.  On this chip each XCD has its own L2, and
+// an agent-scope fence writes back or invalidates the whole L2, which is far
+// too slow to do once per wavefront.  The partial sums instead go through
+// agent-scope atomic stores and loads, which write and read through to the
+// level shared by all XCDs, and ordering needs only a wait for this
+// wavefront's own memory operations: the stores are complete before the
+// counter is incremented, and the loads are issued after its result returns.
+__device__ __forceinline__ void put_shared(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_shared(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_done() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  wait_vmem();
+}
+__device__ __forceinline__ void wait_loads_after_atomic() {
+  wait_vmem();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// wavefront whose range holds tile t, for ranges [w T / W, (w + 1) T / W)
+__device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W) { return ((t + 1) * W - 1) / T; }
+
+// Fused decode-GEMV, batch 1, for up to kMaxJobs matrices: y_j = W_j x_j.
+// LDS: static decode table | stream buffers [waves][2][buf_words].
+template <int TR, int MAXW>
+__global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g, uint32_t buf_words) {
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  float* sums = reinterpret_cast<float*>(lds);
-  const uint32_t nwaves = blockDim.x / kWave;
+  const uint32_t nw = blockDim.x / kWave;
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t lane = lane_id();
-  uint32_t* bufs = lds + kMaxItemTiles * TR + wave * 2 * buf_words;
-  int cur = -1;
-  for (uint64_t item = blockIdx.x; item < g.items; item += gridDim.x) {
-    int j = 0;
-    while (j + 1 < static_cast<int>(g.count) && item >= g.job[j + 1].item0) j++;
-    // select the job with compile-time indices (no dynamic indexing of the
-    // kernel-argument struct, which would copy it to scratch)
-    GemvJob job = g.job[0];
+  int j = 0;
+  while (j + 1 < static_cast<int>(g.count) && blockIdx.x >= g.job[j + 1].g0) j++;
+  // select the job with compile-time indices (no dynamic indexing of the
+  // kernel-argument struct, which would copy it to scratch)
+  GemvJob job = g.job[0];
 #pragma unroll
-    for (int jj = 1; jj < kMaxJobs; jj++)
-      if (jj == j) job = g.job[jj];
-    const BlobDev& b = job.b;
-    if (j != cur) {  // a new matrix: its decode table
-      __syncthreads();
-      load_table(tab, b.table);
-      __syncthreads();
-      cur = j;
+  for (int jj = 1; jj < kMaxJobs; jj++)
+    if (jj == j) job = g.job[jj];
+  const BlobDev& b = job.b;
+  uint32_t* bufs = lds + wave * 2 * buf_words;
+  // W <= T ranges, none empty; wavefronts past the last range idle
+  const uint64_t T = b.n_tiles;
+  const uint64_t W = umin64(static_cast<uint64_t>(job.groups) * nw, T);
+  const uint64_t w = static_cast<uint64_t>(blockIdx.x - job.g0) * nw + wave;
+  const uint64_t t0 = w < W ? w * T / W : T, t1 = w < W ? (w + 1) * T / W : T;
+  const uint32_t n_tc = b.n_tc;
+
+  // the decode table and the first tile are loaded together
+  for (uint32_t base = wave * kWave * 4; base < kTable; base += nw * kWave * 4)
+    __builtin_amdgcn_global_load_lds(b.table + base + lane * 4, tab + base, 16, 0, 0);
+  uint64_t ti = t0 / n_tc;  // row block and column tile of tile t
+  uint32_t tj = static_cast<uint32_t>(t0 - ti * n_tc);
+  TileIn<TR> in;
+  uint4 xv = make_uint4(0, 0, 0, 0);
+  if (t0 < t1) {
+    in.load(b, ti, tj, bufs);
+    xv = *reinterpret_cast<const uint4*>(job.x + (in.active ? in.c0 : 0));
+  }
+  wait_vmem();
+  __syncthreads();
+
+  constexpr uint32_t lanes_per_row = kWave / TR;
+  const bool row_lane = (lane & (lanes_per_row - 1)) == 0;
+  const uint32_t r = lane / lanes_per_row;  // row of the reduced sum this lane holds
+  // a row block is whole when this range holds all of its tiles
+  bool whole = tj == 0 && ti * n_tc + n_tc <= t1;
+  float run = 0.0f;
+  int slot = 0;
+  for (uint64_t t = t0; t < t1; t++) {
+    const uint32_t bit = in.start_bit();
+    wait_vmem();
+    wave_sync_lds();
+    uint64_t ni = ti;
+    uint32_t nj = tj + 1;
+    if (nj == n_tc) {
+      nj = 0;
+      ni++;
     }
-    const uint64_t tb0 = (item - job.item0) * job.rb;           // first row block of the item
-    const uint64_t nrb = umin64(job.rb, b.n_tr - tb0);           // row blocks in this item
-    const uint32_t ntiles = static_cast<uint32_t>(nrb) * b.n_tc;
-    // tiles of this wavefront: wave, wave + nwaves, ...; the next tile's loads
-    // are in flight while the current one decodes
-    uint32_t k = wave;
-    int slot = 0;
-    TileIn<TR> in;
-    uint4 xv = make_uint4(0, 0, 0, 0);
-    if (k < ntiles) {
-      in.load(b, tb0 + k / b.n_tc, k % b.n_tc, bufs);
-      xv = *reinterpret_cast<const uint4*>(job.x + (in.active ? in.c0 : 0));
+    TileIn<TR> nx;
+    uint4 xn = make_uint4(0, 0, 0, 0);
+    if (t + 1 < t1) {
+      nx.load(b, ni, nj, bufs + (slot ^ 1) * buf_words);
+      xn = *reinterpret_cast<const uint4*>(job.x + (nx.active ? nx.c0 : 0));
     }
-    while (k < ntiles) {
-      const uint32_t bit = in.start_bit();
-      wait_vmem();
-      wave_sync_lds();
-      const uint32_t kn = k + nwaves;
-      TileIn<TR> nx;
-      uint4 xn = make_uint4(0, 0, 0, 0);
-      if (kn < ntiles) {
-        nx.load(b, tb0 + kn / b.n_tc, kn % b.n_tc, bufs + (slot ^ 1) * buf_words);
-        xn = *reinterpret_cast<const uint4*>(job.x + (nx.active ? nx.c0 : 0));
+    float acc[TR];
+    gemv_tile_sums<TR>(in, xv, bit, tab, bufs + slot * buf_words, acc);
+    const float s = reduce_rows<TR>(acc);
+    const uint64_t row = ti * TR + r;
+    if (whole) {
+      run += s;
+      if (tj + 1 == n_tc) {
+        if (row_lane && row < b.rows) store_y(job.y, row, run, g.y_f32);
+        run = 0.0f;
       }
-      float acc[TR];
-      gemv_tile_sums<TR>(in, xv, bit, tab, bufs + slot * buf_words, acc);
-      const float s = reduce_rows<TR>(acc);
-      constexpr uint32_t lanes_per_row = kWave / TR;
-      if ((lane & (lanes_per_row - 1)) == 0) sums[k * TR + lane / lanes_per_row] = s;
-      wave_sync_lds();
-      in = nx;
-      xv = xn;
-      k = kn;
-      slot ^= 1;
-    }
-    __syncthreads();
-    // row r of the item's row block i: add its column tiles in order
-    for (uint32_t t = threadIdx.x; t < nrb * TR; t += blockDim.x) {
-      const uint32_t i = t / TR, r = t % TR;
-      const uint64_t row = (tb0 + i) * TR + r;
-      if (row < b.rows) {
-        float sum = 0.0f;
-        for (uint32_t tj = 0; tj < b.n_tc; tj++) sum += sums[(i * b.n_tc + tj) * TR + r];
-        store_y(job.y, row, sum, g.y_f32);
+    } else {
+      if (row_lane && row < b.rows) put_shared(job.part + t * TR + r, s);
+      if (tj + 1 == n_tc || t + 1 == t1) {
+        // this range's share of a cut row block is stored: count it; the
+        // range that completes the row block adds all its tile sums
+        const uint64_t first = ti * n_tc;
+        const uint32_t ranges = static_cast<uint32_t>(range_of(first + n_tc - 1, T, W) - range_of(first, T, W) + 1);
+        wait_stores_done();
+        uint32_t done = 0;
+        if (lane == 0) done = __hip_atomic_fetch_add(job.count + ti, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+        done = __builtin_amdgcn_readlane(done, 0);
+        if (done == ranges) {
+          wait_loads_after_atomic();
+          if (row_lane && row < b.rows) {
+            // loads issued eight at a time, added in column order; the sums
+            // are zeroed behind, so the workspace is all zero again at the end
+            float sum = 0.0f;
+            for (uint32_t k = 0; k < n_tc; k += 8) {
+              float v[8];
+#pragma unroll
+              for (uint32_t u = 0; u < 8; u++) v[u] = k + u < n_tc ? get_shared(job.part + (first + k + u) * TR + r) : 0.0f;
+#pragma unroll
+              for (uint32_t u = 0; u < 8; u++)
+                if (k + u < n_tc) {
+                  sum += v[u];
+                  put_shared(job.part + (first + k + u) * TR + r, 0.0f);
+                }
+            }
+            store_y(job.y, row, sum, g.y_f32);
+          }
+          if (lane == 0) __hip_atomic_store(job.count + ti, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
-    __syncthreads();
+    ti = ni;
+    tj = nj;
+    if (tj == 0) whole = ti * n_tc + n_tc <= t1;
+    in = nx;
+    xv = xn;
+    slot ^= 1;
   }
 }
 
@@ -796,9 +873,10 @@ nwc_status prepare(const nwc_info* info, const void* blob_dev, Launch* L) {
   b.s = g.s;
   b.v = g.v;
   b.stream_words = static_cast<uint32_t>(g.stream_words);
-  // room for the largest tile starting 3 words into a 4-word block, plus the
-  // bit reader's two words of look-ahead, in whole 256-word blocks
-  b.buf_words = 4 + ((info->max_tile_words + 3 + 2 + 255) / 256) * 256;
+  // 4 zero guard words, room for the largest tile starting 3 words into a
+  // 4-word block plus the bit reader's two words of look-ahead (in 16-byte
+  // pieces), and 4 spare words that the reader may fetch past the end
+  b.buf_words = 4 + ((info->max_tile_words + 3 + 2 + 3) / 4) * 4 + 4;
   L->fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
   return NWC_OK;
 }
@@ -836,43 +914,73 @@ unsigned grid_for(uint64_t items, uint32_t waves, size_t lds) {
   return static_cast<unsigned>(std::min<uint64_t>(items, kCUs * per_cu));
 }
 
-// Row blocks per work item: about two tiles per wavefront, within the LDS
-// slots for per-tile sums.
-uint32_t rows_per_item(uint32_t n_tc) {
-  uint32_t rb = std::max<uint32_t>(1, (2 * kGemvWaves + n_tc / 2) / n_tc);
-  while (rb > 1 && rb * n_tc > kMaxItemTiles) rb--;
-  return rb;
+// Workspace of the fused batch-1 path: row-block counters, then tile sums.
+size_t fused_ws_bytes(const nwc::Geometry& g) {
+  auto up = [](uint64_t v) { return (v + 255) / 256 * 256; };
+  return up(g.n_tr * 4) + up(g.n_tiles * static_cast<uint64_t>(g.tr) * 4);
 }
 
-template <int TR>
-nwc_status launch_gemv_group(const Launch* L, const uint16_t* const* x, void* const* y, int count, int y_f32,
-                             hipStream_t s) {
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return kCUs;
+  return n;
+}
+
+// Batch-1 fused launch over `count` matrices with the same tile height.
+// Workgroups are shared out in proportion to each matrix's tiles, no more
+// than the chip holds at once, so every range runs in one pass.
+template <int TR, int MAXW>
+nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y, uint8_t* const* ws, int count,
+                       int y_f32, hipStream_t s) {
   GemvGroup g;
   std::memset(&g, 0, sizeof(g));
   uint32_t buf_words = 0;
-  uint64_t items = 0;
+  uint64_t total = 0;
   for (int j = 0; j < count; j++) {
-    if (L[j].b.n_tc > kMaxItemTiles) return NWC_ERR_UNSUPPORTED;
     buf_words = std::max(buf_words, L[j].b.buf_words);
+    total += L[j].b.n_tiles;
   }
+  // wavefronts per workgroup: the size with the most resident wavefronts
+  // per CU (registers and LDS both count), the larger size on a tie
+  const size_t per_wave = 2ull * buf_words * 4;
+  uint32_t nw = 0;
+  int per_cu = 0;
+  for (uint32_t n = MAXW; n >= 1; n /= 2) {
+    const size_t l = n * per_wave;
+    if (l > kMaxLds) continue;
+    if (set_lds(k_gemv<TR, MAXW>, l) != hipSuccess) return NWC_ERR_HIP;
+    int k = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&k, k_gemv<TR, MAXW>, n * kWave, l) != hipSuccess)
+      return NWC_ERR_HIP;
+    if (static_cast<uint64_t>(k) * n > static_cast<uint64_t>(per_cu) * nw) {
+      nw = n;
+      per_cu = k;
+    }
+  }
+  if (nw == 0 || per_cu < 1) return NWC_ERR_UNSUPPORTED;
+  const size_t lds = nw * per_wave;
+  if (set_lds(k_gemv<TR, MAXW>, lds) != hipSuccess) return NWC_ERR_HIP;
+  const uint64_t cap = static_cast<uint64_t>(cu_count()) * per_cu;
+  uint32_t groups = 0;
   for (int j = 0; j < count; j++) {
     GemvJob& job = g.job[j];
     job.b = L[j].b;
     job.b.buf_words = buf_words;
     job.x = x[j];
     job.y = y[j];
-    job.rb = rows_per_item(job.b.n_tc);
-    job.item0 = items;
-    items += (job.b.n_tr + job.rb - 1) / job.rb;
+    job.count = reinterpret_cast<uint32_t*>(ws[j]);
+    job.part = reinterpret_cast<float*>(ws[j] + (job.b.n_tr * 4 + 255) / 256 * 256);
+    const uint64_t T = job.b.n_tiles;
+    const uint64_t share = 1 + (cap - count) * T / total;
+    job.groups = static_cast<uint32_t>(std::min<uint64_t>((T + nw - 1) / nw, share));
+    job.g0 = groups;
+    groups += job.groups;
   }
   g.count = static_cast<uint32_t>(count);
-  g.items = items;
   g.y_f32 = y_f32;
-  const size_t lds = (static_cast<size_t>(kMaxItemTiles) * TR + 2ull * kGemvWaves * buf_words) * 4;
-  if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
-  if (set_lds(k_gemv_group<TR>, lds) != hipSuccess) return NWC_ERR_HIP;
-  const unsigned grid = grid_for(items, kGemvWaves, lds);
-  k_gemv_group<TR><<<grid, kGemvWaves * kWave, lds, s>>>(g, buf_words);
+  k_gemv<TR, MAXW><<<groups, nw * kWave, lds, s>>>(g, buf_words);
   return launched();
 }
 
@@ -914,8 +1022,12 @@ nwc_status nwc_workspace_size(const nwc_info* info, int batch, size_t* bytes) {
   nwc::Geometry g;
   if (!info || !bytes || batch < 1 || batch > 16 || !nwc::info_geometry(info, &g)) return NWC_ERR_INVALID_ARG;
   const bool fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
-  const bool fused = fast && (batch == 1 || g.tr == 8 || g.tr == 16);
-  *bytes = fused ? 0 : generic_ws_bytes(g, batch);
+  if (fast && batch == 1)
+    *bytes = fused_ws_bytes(g);
+  else if (fast && (g.tr == 8 || g.tr == 16))
+    *bytes = 0;
+  else
+    *bytes = generic_ws_bytes(g, batch);
   return NWC_OK;
 }
 
@@ -968,17 +1080,19 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
   if (ws_bytes < need) return NWC_ERR_BUFFER_TOO_SMALL;
   if (batch > 1 && (ldx < L.b.cols || ldy < L.b.rows)) return NWC_ERR_INVALID_ARG;
   if (!aligned(Y, yt == NWC_OUT_F32 ? 4 : 2) || !aligned(X, 2)) return NWC_ERR_ALIGNMENT;
-  if (need && !aligned(ws, 16)) return NWC_ERR_ALIGNMENT;
+  if (need && !aligned(ws, L.fast && batch == 1 ? 256 : 16)) return NWC_ERR_ALIGNMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int y_f32 = yt == NWC_OUT_F32 ? 1 : 0;
   const bool xvec = aligned(X, 16) && (batch == 1 || ldx % 8 == 0);
   if (need == 0 && !xvec) return NWC_ERR_ALIGNMENT;
-  if (need == 0 && batch == 1) {
+  if (L.fast && batch == 1) {
+    if (!xvec) return NWC_ERR_ALIGNMENT;
     void* yy = Y;
+    uint8_t* w8 = static_cast<uint8_t*>(ws);
     switch (L.b.tr) {
-      case 8: return launch_gemv_group<8>(&L, &X, &yy, 1, y_f32, s);
-      case 16: return launch_gemv_group<16>(&L, &X, &yy, 1, y_f32, s);
-      default: return launch_gemv_group<32>(&L, &X, &yy, 1, y_f32, s);
+      case 8: return launch_gemv<8, 16>(&L, &X, &yy, &w8, 1, y_f32, s);
+      case 16: return launch_gemv<16, 8>(&L, &X, &yy, &w8, 1, y_f32, s);
+      default: return launch_gemv<32, 4>(&L, &X, &yy, &w8, 1, y_f32, s);
     }
   }
   if (need == 0) {
@@ -1019,23 +1133,32 @@ nwc_status nwc_gemv(const nwc_info* info, const void* blob_dev, const uint16_t* 
 }
 
 nwc_status nwc_gemv_batched(int count, const nwc_info* infos, const void* const* blobs_dev,
-                            const uint16_t* const* x_dev, void* const* y_dev, nwc_out_type y_type, void* stream) {
-  if (count < 1 || count > kMaxJobs || !infos || !blobs_dev || !x_dev || !y_dev) return NWC_ERR_INVALID_ARG;
+                            const uint16_t* const* x_dev, void* const* y_dev, nwc_out_type y_type, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (count < 1 || count > kMaxJobs || !infos || !blobs_dev || !x_dev || !y_dev || !ws) return NWC_ERR_INVALID_ARG;
   if (y_type != NWC_OUT_BF16 && y_type != NWC_OUT_F32) return NWC_ERR_INVALID_ARG;
+  if (!aligned(ws, 256)) return NWC_ERR_ALIGNMENT;
   Launch L[kMaxJobs];
+  uint8_t* w8[kMaxJobs];
+  size_t used = 0;
   for (int j = 0; j < count; j++) {
     if (!x_dev[j] || !y_dev[j]) return NWC_ERR_INVALID_ARG;
     nwc_status st = prepare(&infos[j], blobs_dev[j], &L[j]);
     if (st) return st;
     if (!L[j].fast || L[j].b.tr != L[0].b.tr) return NWC_ERR_UNSUPPORTED;
     if (!aligned(x_dev[j], 16) || !aligned(y_dev[j], y_type == NWC_OUT_F32 ? 4 : 2)) return NWC_ERR_ALIGNMENT;
+    nwc::Geometry g;
+    nwc::info_geometry(&infos[j], &g);
+    w8[j] = static_cast<uint8_t*>(ws) + used;
+    used += fused_ws_bytes(g);
   }
+  if (ws_bytes < used) return NWC_ERR_BUFFER_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int y_f32 = y_type == NWC_OUT_F32 ? 1 : 0;
   switch (L[0].b.tr) {
-    case 8: return launch_gemv_group<8>(L, x_dev, y_dev, count, y_f32, s);
-    case 16: return launch_gemv_group<16>(L, x_dev, y_dev, count, y_f32, s);
-    default: return launch_gemv_group<32>(L, x_dev, y_dev, count, y_f32, s);
+    case 8: return launch_gemv<8, 16>(L, x_dev, y_dev, w8, count, y_f32, s);
+    case 16: return launch_gemv<16, 8>(L, x_dev, y_dev, w8, count, y_f32, s);
+    default: return launch_gemv<32, 4>(L, x_dev, y_dev, w8, count, y_f32, s);
   }
 }
 

@@ -131,19 +131,29 @@ nwc_status nwc_decode(const nwc_info *info, const void *blob_dev, uint16_t *w_de
                       uint64_t ld, void *stream);
 
 /* Workspace bytes needed by nwc_gemv (batch = 1) or nwc_gemm_skinny
- * (batch 2..16) for this blob.  0 on the fused paths (default geometry,
- * cols % 8 == 0), which then accept ws = NULL; otherwise FP32 partial sums,
- * one per (column tile, batch row, output row), for the one-symbol-at-a-time
- * path, which runs a second reduction kernel. */
+ * (batch 2..16) for this blob.
+ *  - Fused batch-1 path (default geometry, cols % 8 == 0): one counter per
+ *    row block and one FP32 partial sum per (tile, row), 256-byte aligned
+ *    sections.  The kernel splits the tiles evenly over the GPU, so a row
+ *    block can be shared by several wavefronts; the counters tell the last
+ *    one to finish that it adds the partial sums.  The workspace must be
+ *    zero-filled before its first use; every call leaves it zero-filled.
+ *  - Fused skinny path (tile_rows 8 or 16, batch 2..16): 0 (ws may be NULL).
+ *  - Otherwise FP32 partial sums, one per (column tile, batch row, output
+ *    row), for the one-symbol-at-a-time path, which runs a second reduction
+ *    kernel; contents need not be initialised. */
 nwc_status nwc_workspace_size(const nwc_info *info, int batch, size_t *bytes);
 
 /* Fused decode-GEMV (pages: "Fused kernel"; Unweight "Direct GPU
  * Decompression"): y = W x with x (device, cols BF16, 16-byte aligned) and y
  * (device, rows entries of y_type).  Weights are decoded in registers and
- * LDS and never written to memory; products accumulate in FP32 in a fixed
- * order and y is written once.  ws is a device workspace of at least
- * nwc_workspace_size(info, 1) bytes (NULL if that is 0) whose contents need
- * not be initialised.  x and y must not alias.  Async.
+ * LDS and never written to memory; each output row adds its per-tile FP32
+ * sums in column order, so y does not depend on how the tiles were shared
+ * out, and each y entry is written once.  ws is a device workspace of at
+ * least nwc_workspace_size(info, 1) bytes, 256-byte aligned, used as that
+ * function describes (zero-filled before first use on the fused path).
+ * Calls that share a workspace must not run concurrently (same stream, or
+ * ordered by events).  x and y must not alias.  Async.
  * Errors: INVALID_ARG, BUFFER_TOO_SMALL (ws), ALIGNMENT, UNSUPPORTED, HIP. */
 nwc_status nwc_gemv(const nwc_info *info, const void *blob_dev, const uint16_t *x_dev,
                     void *y_dev, nwc_out_type y_type, void *ws, size_t ws_bytes,
@@ -155,12 +165,15 @@ nwc_status nwc_gemv(const nwc_info *info, const void *blob_dev, const uint16_t *
  * of one decode step that need no result of each other (q/k/v from the same
  * activations, gate/up), one launch keeps the whole GPU busy where separate
  * small launches each pay a start-up and a tail.  Every blob must be on the
- * fused path (nwc_workspace_size 0) and all must share tile_rows; each y_i is
- * bitwise identical to what nwc_gemv computes for it.  Async.
- * Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, HIP. */
+ * fused batch-1 path and all must share tile_rows.  ws (256-byte aligned,
+ * zero-filled before first use, left zero-filled) holds the workspaces of
+ * all blobs back to back: at least the sum over i of
+ * nwc_workspace_size(&infos[i], 1).  Each y_i is bitwise identical to what
+ * nwc_gemv computes for it.  Same concurrency rule as nwc_gemv.  Async.
+ * Errors: INVALID_ARG, BUFFER_TOO_SMALL (ws), UNSUPPORTED, ALIGNMENT, HIP. */
 nwc_status nwc_gemv_batched(int count, const nwc_info *infos, const void *const *blobs_dev,
-                            const uint16_t *const *x_dev, void *const *y_dev, nwc_out_type y_type,
-                            void *stream);
+                            const uint16_t *const *x_dev, void *const *y_dev,
+                            nwc_out_type y_type, void *ws, size_t ws_bytes, void *stream);
 
 /* Skinny decode-GEMM for batch 2..16: Y[b, n] = sum_k X[b, k] W[n, k] with X
  * (device, batch x cols, row stride ldx) and Y (device, batch x rows, row

@@ -44,7 +44,8 @@ class Blob:
         self.dev = dev(self.host)
 
     def ws(self, batch=1):
-        return torch.empty(nwc.nwc_workspace_size(self.info, batch), dtype=torch.uint8, device="cuda")
+        # zero-filled: the fused batch-1 path keeps counters there
+        return torch.zeros(nwc.nwc_workspace_size(self.info, batch), dtype=torch.uint8, device="cuda")
 
 
 @functools.lru_cache(maxsize=None)
@@ -93,6 +94,9 @@ def _special(name):
         "one_symbol": lambda: (0x3C00 | rng.integers(0, 128, (50, 64))).astype(np.uint16),
         "random_bits": lambda: workloads.random_bits((300, 264), 6),
         "wide_odd": lambda: workloads.gaussian_bits((40, 3000), 0.05, 8),
+        "8x512": lambda: workloads.gaussian_bits((8, 512), 0.02, 9),
+        "3000x512": lambda: workloads.gaussian_bits((3000, 512), 0.02, 10),
+        "20x40960": lambda: workloads.gaussian_bits((20, 40960), 0.02, 12),
     }[name]()
 
 
@@ -144,7 +148,8 @@ def test_decode_oracle_written_blob():
 GEMV_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=16)), ("cfg1", dict(tile_rows=32)),
               ("cfg1", dict(tile_rows=5, tile_cols=24, chunks_per_tile=3, max_code_len=11)),
               ("127x1001", None), ("1x1", None), ("1000x256", None), ("subnormal", None),
-              ("one_symbol", None), ("wide_odd", None)]
+              ("one_symbol", None), ("wide_odd", None), ("8x512", None), ("3000x512", None),
+              ("20x40960", None), ("20x40960", dict(tile_rows=16))]
 
 
 @pytest.mark.parametrize("out_f32", [False, True])
@@ -169,6 +174,23 @@ def test_gemv_subnormal_products_kept():
     y_ref, a_ref = oracle.gemv(w, x)
     assert np.all(y_ref > 0)
     _check_y(_to_f64(y), y_ref, a_ref, True, "subnormal")
+
+
+def test_gemv_workspace_reused_across_shapes():
+    # one workspace, sized for the largest call, serves calls of any size in
+    # stream order: each call leaves its counters at zero for the next
+    big, small = Blob(_special("3000x512")), Blob(_special("20x40960"))
+    ws = torch.zeros(max(nwc.nwc_workspace_size(big.info, 1), nwc.nwc_workspace_size(small.info, 1)),
+                     dtype=torch.uint8, device="cuda")
+    for b in (big, small, big, small):
+        x = workloads.gaussian_bits((b.info.cols,), 1.0, 13)
+        y = torch.empty(b.info.rows, dtype=torch.float32, device="cuda")
+        _say("gemv reuse %dx%d" % (b.info.rows, b.info.cols))
+        nwc.nwc_gemv(b.info, b.dev, dev(x), y, ws)
+        torch.cuda.synchronize()
+        y_ref, a_ref = oracle.gemv(b.w, x)
+        _check_y(_to_f64(y), y_ref, a_ref, True, "reuse")
+        assert _counters_zero([b], ws)
 
 
 def test_gemv_deterministic():
@@ -223,6 +245,16 @@ def test_gemv_lm_head_sampled():
         assert np.all(np.isfinite(y))
 
 
+def _batched_ws(blobs):
+    return torch.zeros(nwc.gemv_batched_workspace_size([b.info for b in blobs]), dtype=torch.uint8, device="cuda")
+
+
+def _counters_zero(blobs, ws):
+    """Every call leaves its workspace (counters and partial sums) all zero."""
+    n = sum(nwc.nwc_workspace_size(b.info, 1) for b in blobs)
+    return int(ws[:n].count_nonzero()) == 0
+
+
 def test_gemv_batched_equals_single_calls():
     names = ["q", "k", "v", "o", "gate", "up", "down"]
     blobs = [Blob(_w(2, n)) for n in names]
@@ -230,13 +262,15 @@ def test_gemv_batched_equals_single_calls():
     for out_f32 in (False, True):
         dt = torch.float32 if out_f32 else torch.bfloat16
         ys = [torch.empty(b.info.rows, dtype=dt, device="cuda") for b in blobs]
-        batch = nwc.GemvBatch([b.info for b in blobs], [b.dev for b in blobs], xs, ys)
+        ws = _batched_ws(blobs)
+        batch = nwc.GemvBatch([b.info for b in blobs], [b.dev for b in blobs], xs, ys, ws)
         _say("gemv_batched 7 matrices f32=%s" % out_f32)
         nwc.nwc_gemv_batched(batch)
         torch.cuda.synchronize()
+        assert _counters_zero(blobs, ws)
         for b, x, y, n in zip(blobs, xs, ys, names):
             y1 = torch.empty_like(y)
-            nwc.nwc_gemv(b.info, b.dev, x, y1)
+            nwc.nwc_gemv(b.info, b.dev, x, y1, b.ws())
             torch.cuda.synchronize()
             assert torch.equal(y.view(torch.int16) if not out_f32 else y.view(torch.int32),
                                y1.view(torch.int16) if not out_f32 else y1.view(torch.int32)), n
@@ -250,8 +284,10 @@ def test_gemv_batched_mixed_shapes_and_edges():
     blobs = [Blob(w) for w in ws]
     xs = [dev(workloads.gaussian_bits((w.shape[1],), 1.0, 5 + i)) for i, w in enumerate(ws)]
     ys = [torch.empty(w.shape[0], dtype=torch.float32, device="cuda") for w in ws]
-    nwc.nwc_gemv_batched(nwc.GemvBatch([b.info for b in blobs], [b.dev for b in blobs], xs, ys))
+    wsp = _batched_ws(blobs)
+    nwc.nwc_gemv_batched(nwc.GemvBatch([b.info for b in blobs], [b.dev for b in blobs], xs, ys, wsp))
     torch.cuda.synchronize()
+    assert _counters_zero(blobs, wsp)
     for w, x, y in zip(ws, xs, ys):
         y_ref, a_ref = oracle.gemv(w, x.cpu().numpy())
         _check_y(_to_f64(y), y_ref, a_ref, True, str(w.shape))

@@ -161,15 +161,21 @@ def test_workspace_sizes():
     for bad in (0, 17):
         with pytest.raises(nwc.NwcError):
             nwc.nwc_workspace_size(info, bad)
-    # fused paths need none
+    # fused batch 1: row-block counters, then one sum per (tile, row), each
+    # section rounded up to 256 bytes; the fused skinny path needs none
+    up = lambda v: -(-v // 256) * 256
     fast = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2)))
-    assert nwc.nwc_workspace_size(fast, 1) == 0
+    assert nwc.nwc_workspace_size(fast, 1) == up(13 * 4) + up(13 * 3 * 8 * 4)
     tr16 = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2), dict(tile_rows=16)))
-    assert nwc.nwc_workspace_size(tr16, 1) == 0 and nwc.nwc_workspace_size(tr16, 8) == 0
+    assert nwc.nwc_workspace_size(tr16, 1) == up(7 * 4) + up(7 * 3 * 16 * 4)
+    assert nwc.nwc_workspace_size(tr16, 8) == 0
     assert nwc.nwc_workspace_size(fast, 8) == 0
+    assert nwc.gemv_batched_workspace_size([fast, tr16]) == (nwc.nwc_workspace_size(fast, 1) +
+                                                             nwc.nwc_workspace_size(tr16, 1))
     # batch > 1 with tile_rows 32 takes the generic path
     tr32 = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2), dict(tile_rows=32)))
-    assert nwc.nwc_workspace_size(tr32, 1) == 0 and nwc.nwc_workspace_size(tr32, 8) == 3 * 8 * 100 * 4
+    assert nwc.nwc_workspace_size(tr32, 1) == up(4 * 4) + up(4 * 3 * 32 * 4)
+    assert nwc.nwc_workspace_size(tr32, 8) == 3 * 8 * 100 * 4
     assert nwc.nwc_bf16_workspace_size(100, 1500) == 0
 
 
@@ -183,14 +189,20 @@ def test_device_calls_validate_before_launch():
     L = nwc._lib
     ref = ctypes.byref(info)
     A = 0x10000          # 256-aligned fake device address
-    assert L.nwc_gemv(None, A, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, None, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, A, None, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, A, A, None, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, A, A, A, 7, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv(ref, A + 16, A, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
-    assert L.nwc_gemv(ref, A, A, A + 1, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
-    assert L.nwc_gemv(ref, A, A + 2, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT   # x must be 16-aligned
+    W = nwc.nwc_workspace_size(info, 1)
+    assert W > 0
+    assert L.nwc_gemv(None, A, A, A, 0, A, W, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, None, A, A, 0, A, W, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, None, A, 0, A, W, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, A, None, 0, A, W, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, A, A, 7, A, W, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A + 16, A, A, 0, A, W, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv(ref, A, A, A + 1, 0, A, W, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv(ref, A, A + 2, A, 0, A, W, None) == nwc.NWC_ERR_ALIGNMENT   # x must be 16-aligned
+    # the fused path's workspace: present, large enough, 256-byte aligned
+    assert L.nwc_gemv(ref, A, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ref, A, A, A, 0, A, W - 4, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
+    assert L.nwc_gemv(ref, A, A, A, 0, A + 16, W, None) == nwc.NWC_ERR_ALIGNMENT
     for batch in (0, 1, 17):
         assert L.nwc_gemm_skinny(ref, A, A, 512, batch, A, 64, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
     assert L.nwc_gemm_skinny(ref, A, A, 100, 4, A, 64, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
@@ -201,7 +213,7 @@ def test_device_calls_validate_before_launch():
     assert L.nwc_decode(ref, A, A + 1, 512, None) == nwc.NWC_ERR_ALIGNMENT
     bad = nwc.nwc_info.from_buffer_copy(info)
     bad.n_tiles += 1
-    assert L.nwc_gemv(ctypes.byref(bad), A, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv(ctypes.byref(bad), A, A, A, 0, A, W, None) == nwc.NWC_ERR_INVALID_ARG
     # the one-symbol-at-a-time path needs its workspace
     gblob = nwc.nwc_encode(workloads.gaussian_bits((64, 500), 0.02, 2))
     ginfo = nwc.nwc_inspect(gblob)
@@ -218,15 +230,19 @@ def test_device_calls_validate_before_launch():
     infos = (nwc.nwc_info * 2)(info, info)
     V2 = ctypes.c_void_p * 2
     ok = V2(A, A)
+    B = 2 * W
     for count in (0, 9):
-        assert L.nwc_gemv_batched(count, infos, ok, ok, ok, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv_batched(2, None, ok, ok, ok, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv_batched(2, infos, ok, ok, ok, 5, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv_batched(2, infos, ok, V2(A, None), ok, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv_batched(2, infos, V2(A, A + 16), ok, ok, 0, None) == nwc.NWC_ERR_ALIGNMENT
-    assert L.nwc_gemv_batched(2, infos, ok, V2(A, A + 4), ok, 0, None) == nwc.NWC_ERR_ALIGNMENT
+        assert L.nwc_gemv_batched(count, infos, ok, ok, ok, 0, A, B, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_batched(2, None, ok, ok, ok, 0, A, B, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_batched(2, infos, ok, ok, ok, 5, A, B, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_batched(2, infos, ok, V2(A, None), ok, 0, A, B, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_batched(2, infos, ok, ok, ok, 0, None, B, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_batched(2, infos, V2(A, A + 16), ok, ok, 0, A, B, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_batched(2, infos, ok, V2(A, A + 4), ok, 0, A, B, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_batched(2, infos, ok, ok, ok, 0, A + 16, B, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_batched(2, infos, ok, ok, ok, 0, A, B - 4, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
     mixed = (nwc.nwc_info * 2)(info, nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((64, 512), 0.02, 2),
                                                                       dict(tile_rows=16))))
-    assert L.nwc_gemv_batched(2, mixed, ok, ok, ok, 0, None) == nwc.NWC_ERR_UNSUPPORTED
+    assert L.nwc_gemv_batched(2, mixed, ok, ok, ok, 0, A, 1 << 20, None) == nwc.NWC_ERR_UNSUPPORTED
     gen = (nwc.nwc_info * 2)(info, ginfo)
-    assert L.nwc_gemv_batched(2, gen, ok, ok, ok, 0, None) == nwc.NWC_ERR_UNSUPPORTED
+    assert L.nwc_gemv_batched(2, gen, ok, ok, ok, 0, A, 1 << 20, None) == nwc.NWC_ERR_UNSUPPORTED
