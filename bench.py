@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--roofline-reps", type=int, default=200)
     ap.add_argument("--skip-bf16", action="store_true")
     ap.add_argument("--tile-rows", type=int, default=0, help="encoder tile rows (0 = library default)")
+    ap.add_argument("--max-code-len", type=int, default=0, help="encoder code length limit (0 = library default)")
     return ap.parse_args()
 
 
@@ -70,7 +71,8 @@ def main():
     host = {}
     for m in mats:
         w = workloads.weights(wl.cid, m.name, layer=0)
-        blob = nwc.nwc_encode(w, dict(tile_rows=args.tile_rows) if args.tile_rows else None)
+        params = {k: v for k, v in (("tile_rows", args.tile_rows), ("max_code_len", args.max_code_len)) if v}
+        blob = nwc.nwc_encode(w, params or None)
         host[m.name] = (w, blob, nwc.nwc_inspect(blob))
     enc_s = time.time() - t0
     bytes_c = sum(host[n][1].size + 2 * host[n][2].cols + 2 * host[n][2].rows for n in order)

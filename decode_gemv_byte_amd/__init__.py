@@ -49,7 +49,8 @@ class nwc_info(ctypes.Structure):
                 ("off_table", ctypes.c_uint64), ("off_tile_words", ctypes.c_uint64),
                 ("off_chunk_bits", ctypes.c_uint64), ("off_raw", ctypes.c_uint64),
                 ("off_stream", ctypes.c_uint64), ("max_tile_words", ctypes.c_uint32),
-                ("n_symbols", ctypes.c_uint32), ("payload_bits", ctypes.c_uint64),
+                ("n_symbols", ctypes.c_uint32), ("max_chunk_bits", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32), ("payload_bits", ctypes.c_uint64),
                 ("code_len", ctypes.c_uint8 * 256)]
 
 

@@ -428,6 +428,7 @@ nwc_status inspect(const void* blob_v, size_t bytes, nwc_info* info) {
 
   uint64_t payload = 0;
   uint32_t max_tw = 0;
+  uint64_t max_cb = 0;
   if (load_le<uint32_t>(b + g.off_tile_words) != 0) return NWC_ERR_BAD_FORMAT;
   for (uint64_t t = 0; t < g.n_tiles; t++) {
     uint64_t bits = 0;
@@ -441,6 +442,7 @@ nwc_status inspect(const void* blob_v, size_t bytes, nwc_info* info) {
       const uint64_t nc = c0 < tile_c1 ? std::min<uint64_t>(tile_c1, c0 + g.v) - c0 : 0;
       if (cb < nr * nc || cb > nr * nc * g.lmax) return NWC_ERR_BAD_FORMAT;
       bits += cb;
+      max_cb = std::max<uint64_t>(max_cb, cb);
     }
     const uint32_t a = load_le<uint32_t>(b + g.off_tile_words + 4 * t);
     const uint32_t e = load_le<uint32_t>(b + g.off_tile_words + 4 * (t + 1));
@@ -470,6 +472,7 @@ nwc_status inspect(const void* blob_v, size_t bytes, nwc_info* info) {
   info->off_stream = g.off_stream;
   info->max_tile_words = max_tw;
   info->n_symbols = nsym;
+  info->max_chunk_bits = static_cast<uint32_t>(max_cb);
   info->payload_bits = payload;
   std::memcpy(info->code_len, len, 256);
   return NWC_OK;

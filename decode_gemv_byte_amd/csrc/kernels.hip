@@ -170,69 +170,95 @@ __device__ __forceinline__ uint32_t stage_blocks(const BlobDev& b, uint32_t a0, 
   return need > cap ? cap : need;
 }
 
+// LDS access by byte address (a 32-bit offset into the workgroup's LDS).
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u32*)p));
+}
+__device__ __forceinline__ uint32_t lds_word(uint32_t byte_addr) {
+  return *(lds_u32*)(static_cast<uintptr_t>(byte_addr));
+}
+typedef __attribute__((address_space(3))) uint32_t lds_u32w;
+__device__ __forceinline__ void lds_put(uint32_t byte_addr, uint32_t v) {
+  *(lds_u32w*)(static_cast<uintptr_t>(byte_addr)) = v;
+}
+
+// Raw buffer resource over [base, base + bytes) (bytes capped at 4 GiB - 1):
+// loads past the end return zero instead of faulting.  Built from
+// wave-uniform values, so it lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(n),
+                                           0x00020000);
+}
+
 // Bit reader over a wavefront's LDS stream buffer.  The buffer keeps 4 zero
-// guard words before the staged stream, so every start bit b >= 128.  State:
-// a 64-bit window (lo = word wi, hi = word wi + 1), the following word nxt,
-// and qm = (bit offset in lo) - 2, kept in [0, 32): the funnel shift by qm
-// then leaves the next 12 stream bits at bits 2..13, i.e. already scaled to a
-// byte address into the 4-byte-entry decode table at LDS address 0.
+// guard words before the staged stream, so every start bit b >= 128.  The
+// whole state is p = (LDS bit address of the next code) - 2: a step reads the
+// word holding bit p and the next one (one ds_read2), and a funnel shift by
+// p (mod 32) leaves the next 12 stream bits at bits 2..13, already a byte
+// address into the 4-byte-entry decode table.  Six VALU operations per step
+// besides the table lookup; the stream words are re-read from LDS instead of
+// being shifted through registers.
 struct Bits {
-  uint32_t lo, hi, nxt, qm, wi;
-  __device__ __forceinline__ void init(const uint32_t* buf, uint32_t bit) {
-    const uint32_t b2 = bit - 2;
-    wi = b2 >> 5;
-    qm = b2 & 31u;
-    lo = buf[wi];
-    hi = buf[wi + 1];
-    nxt = buf[wi + 2];
-  }
-  // window for the current qm, which may have run up to 55: both funnel
-  // shifts are computed next to the compare, so the select is the only step
-  // between the new position and the next table address
+  uint32_t p;
+  __device__ __forceinline__ void init(const uint32_t* buf, uint32_t bit) { p = lds_addr(buf) * 8u + bit - 2u; }
   __device__ __forceinline__ uint32_t window() const {
-    const uint32_t a = __builtin_amdgcn_alignbit(hi, lo, qm);
-    const uint32_t b = __builtin_amdgcn_alignbit(nxt, hi, qm);
-    return qm >= 32 ? b : a;
+    const uint32_t a = (p >> 3) & ~3u;
+    return __builtin_amdgcn_alignbit(lds_word(a + 4), lds_word(a), p);
   }
-  // commit a position that may have crossed into the next word
-  __device__ __forceinline__ void settle(const uint32_t* buf) {
-    const bool c = qm >= 32;
-    lo = c ? hi : lo;
-    hi = c ? nxt : hi;
-    wi += c ? 1u : 0u;
-    qm &= 31u;
-    nxt = buf[wi + 2];
-  }
-  // Decode the next two exponents: returns a dword with exponent 0 at bits
-  // 7..14 and exponent 1 at bits 23..30.
-  __device__ __forceinline__ uint32_t pair(const uint32_t* tab, const uint32_t* buf) {
-    const uint32_t win = window();
-    settle(buf);
-    uint32_t ent = tab[(win & 0x3FFCu) >> 2];
-    // Rarely the second code does not fit in the 12-bit window.  The test is
-    // made for the whole wavefront, and inside the branch every lane does the
-    // second lookup and keeps it only if it needs it, so the common path has
-    // no exec-mask changes.
-    const bool single = static_cast<int32_t>(ent) < 0;
-    if (__builtin_amdgcn_ballot_w64(single)) {
-      const uint32_t l0 = ent & 0xFu;
-      const uint32_t ent2 = tab[((win >> l0) & 0x3FFCu) >> 2];
-      // merged advance l0 + l1 may reach 24: it occupies bits 0..4
-      const uint32_t merged = (ent & 0x7F80u) | ((ent2 & 0x7F80u) << 16) | (l0 + ((ent2 >> 16) & 0xFu));
-      ent = single ? merged : ent;
-    }
-    qm += ent & 0x1Fu;
-    return ent;
-  }
+  __device__ __forceinline__ void advance(uint32_t n) { p += n; }
+  __device__ __forceinline__ uint32_t pair(const uint32_t* tab);
   // One exponent (generic paths): returns it and advances.
-  __device__ __forceinline__ uint32_t one(const uint32_t* tab, const uint32_t* buf) {
-    const uint32_t win = window();
-    settle(buf);
-    const uint32_t ent = tab[(win & 0x3FFCu) >> 2];
-    qm += (ent >> 16) & 0xFu;
+  __device__ __forceinline__ uint32_t one(const uint32_t* tab) {
+    const uint32_t ent = tab[(window() & 0x3FFCu) >> 2];
+    p += (ent >> 16) & 0xFu;
     return (ent >> 7) & 0xFFu;
   }
 };
+
+// Bit reader over a lane-interleaved LDS stream buffer: word j of this lane's
+// staged words is LDS word 64 j + lane of the slot, so at every step the 64
+// lanes read 64 different banks.  q = (bit position in the staged words) - 2.
+// The slot starts on a 256-byte boundary, so q carries the slot's base (as
+// 32 * base / 256 added to the bit position): the word address is then
+// ((q >> 5) << 8) | (4 * lane), one shift and one and-or.
+struct LaneBits {
+  uint32_t lane4, q;
+  __device__ __forceinline__ void init(const uint32_t* slot, uint32_t q0) {
+    lane4 = lane_id() * 4u;
+    q = q0 + (lds_addr(slot) >> 3);
+  }
+  __device__ __forceinline__ uint32_t window() const {
+    const uint32_t a = ((q << 3) & ~0xFFu) | lane4;
+    return __builtin_amdgcn_alignbit(lds_word(a + 256), lds_word(a), q);
+  }
+  __device__ __forceinline__ void advance(uint32_t n) { q += n; }
+};
+
+// Decode the next two exponents with either reader: returns a dword with
+// exponent 0 at bits 7..14 and exponent 1 at bits 23..30.
+template <class R>
+__device__ __forceinline__ uint32_t decode_pair(R& rd, const uint32_t* tab) {
+  const uint32_t win = rd.window();
+  uint32_t ent = tab[(win & 0x3FFCu) >> 2];
+  // Rarely the second code does not fit in the 12-bit window.  The test is
+  // made for the whole wavefront, and inside the branch every lane does the
+  // second lookup and keeps it only if it needs it, so the common path has no
+  // exec-mask changes.  The window holds 30 bits past the first code's start,
+  // so the second code (<= 12 bits after <= 12) is inside it.
+  const bool single = static_cast<int32_t>(ent) < 0;
+  if (__builtin_amdgcn_ballot_w64(single)) {
+    const uint32_t l0 = ent & 0xFu;
+    const uint32_t ent2 = tab[((win >> l0) & 0x3FFCu) >> 2];
+    // merged advance l0 + l1 may reach 24: it occupies bits 0..4
+    const uint32_t merged = (ent & 0x7F80u) | ((ent2 & 0x7F80u) << 16) | (l0 + ((ent2 >> 16) & 0xFu));
+    ent = single ? merged : ent;
+  }
+  rd.advance(ent & 0x1Fu);
+  return ent;
+}
+__device__ __forceinline__ uint32_t Bits::pair(const uint32_t* tab) { return decode_pair(*this, tab); }
 
 // Two BF16 weights from a pair entry and 4 raw bytes; `hi` selects raw bytes
 // 2,3 instead of 0,1.
@@ -265,14 +291,26 @@ __device__ __forceinline__ void store_y(void* y, uint64_t i, float v, int y_f32)
 // the lower half.  Indices are compile-time, so no dynamic register indexing.
 // Partners differ in bit M and hold sums over disjoint lane sets, so after
 // all levels every row's sum covers all 64 lanes exactly once.
+// For M = 32 and M = 16 one lane-swap instruction moves exactly the two
+// halves that change hands (v[i] from the upper lanes down, v[HALF + i] from
+// the lower lanes up), so a level costs a swap and an add; the sums are the
+// same two operands as the select form (addition commutes).
 template <int R, int HALF, int M>
 __device__ __forceinline__ void butterfly(float (&v)[R], uint32_t lane) {
   const bool up = (lane & M) != 0;
 #pragma unroll
   for (int i = 0; i < HALF; i++) {
-    const float keep = up ? v[HALF + i] : v[i];
-    const float send = up ? v[i] : v[HALF + i];
-    v[i] = keep + partner<M>(send);
+    if constexpr (M == 32 || M == 16) {
+      const uint32_t lo = __builtin_bit_cast(uint32_t, v[i]), hi = __builtin_bit_cast(uint32_t, v[HALF + i]);
+      const auto p = M == 32 ? __builtin_amdgcn_permlane32_swap(lo, hi, false, false)
+                             : __builtin_amdgcn_permlane16_swap(lo, hi, false, false);
+      v[i] = __builtin_bit_cast(float, static_cast<uint32_t>(p[0])) +
+             __builtin_bit_cast(float, static_cast<uint32_t>(p[1]));
+    } else {
+      const float keep = up ? v[HALF + i] : v[i];
+      const float send = up ? v[i] : v[HALF + i];
+      v[i] = keep + partner<M>(send);
+    }
   }
   if constexpr (HALF > 1) butterfly<R, HALF / 2, M / 2>(v, lane);
 }
@@ -356,10 +394,10 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_fast(BlobDev b
 #pragma unroll
       for (int r = 0; r < TR; r++) {
         uint4 o;
-        o.x = assemble(br.pair(tab, buf), in.raw[r].x, false);
-        o.y = assemble(br.pair(tab, buf), in.raw[r].x, true);
-        o.z = assemble(br.pair(tab, buf), in.raw[r].y, false);
-        o.w = assemble(br.pair(tab, buf), in.raw[r].y, true);
+        o.x = assemble(br.pair(tab), in.raw[r].x, false);
+        o.y = assemble(br.pair(tab), in.raw[r].x, true);
+        o.z = assemble(br.pair(tab), in.raw[r].y, false);
+        o.w = assemble(br.pair(tab), in.raw[r].y, true);
         if (static_cast<uint32_t>(r) < in.nrows) *reinterpret_cast<uint4*>(out + (row0 + r) * ld + in.c0) = o;
       }
     }
@@ -404,7 +442,7 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDe
           br.init(buf, bit);
           for (uint64_t r = row0; r < r1; r++)
             for (uint64_t k = cc0; k < cc1; k++) {
-              const uint32_t e = br.one(tab, buf);
+              const uint32_t e = br.one(tab);
               const uint32_t rb = b.raw[r * b.raw_ld + k];
               out[r * ld + k] = static_cast<uint16_t>(((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu));
             }
@@ -440,35 +478,116 @@ struct GemvGroup {
   GemvJob job[kMaxJobs];
   uint32_t count;
   int y_f32;
+  uint32_t lane_words;  // stream words per lane in the interleaved slot (J, even)
+  uint32_t buf_words;   // linear staging buffer per wavefront
 };
 
-// Decode one tile already staged (stream in LDS, raw bytes and x in
-// registers) and return this lane's TR row sums over its 8 columns.
+// Registers of one tile for the batch-1 kernel: raw bytes of this lane's
+// 8 columns in every row, x for those columns, this lane's chunk length, and
+// where the tile's stream starts.  Every load goes through a buffer resource
+// built from wave-uniform addresses (row offsets in scalar registers, one
+// constant lane offset), so issuing a tile costs almost no vector ALU work.
+// The tile's word offsets (tw0, tw1) come in from a vector load issued one
+// tile earlier: a scalar load would share its wait counter with the LDS
+// reads of the decode loop and stall it for a full memory round trip.
 template <int TR>
-__device__ __forceinline__ void gemv_tile_sums(const TileIn<TR>& in, const uint4& xv, uint32_t bit,
-                                               const uint32_t* tab, const uint32_t* buf, float (&acc)[TR]) {
-#pragma unroll
-  for (int r = 0; r < TR; r++) acc[r] = 0.0f;
-  if (in.active) {
-    // Rows past the matrix edge (last row block only) are decoded from
-    // whatever follows the chunk and multiplied too: raw loads were clamped to
-    // valid rows, each row keeps its own sum through the reduction, and rows
-    // past the edge are never stored.
-    Bits br;
-    br.init(buf, bit);
+struct TileRegs {
+  uint2 raw[TR];
+  uint4 x;
+  uint32_t cb, w0, a0, nrows;
+  bool active;
+  __device__ __forceinline__ void load(const BlobDev& b, const uint16_t* xp, uint64_t ti, uint32_t tj,
+                                       uint32_t tw0, uint32_t tw1, uint32_t* buf) {
+    const uint32_t lane = lane_id();
+    const uint64_t t = ti * b.n_tc + tj;
+    const uint64_t row0 = ti * TR;
+    nrows = static_cast<uint32_t>(umin64(TR, b.rows - row0));
+    active = static_cast<uint64_t>(tj) * 512 + lane * 8 < b.cols;
+    // raw plane: rows past the matrix edge re-read the last valid row
+    const uint64_t col0 = static_cast<uint64_t>(tj) * 512;
+    const __amdgpu_buffer_rsrc_t rr =
+        buf_rsrc(b.raw + row0 * b.raw_ld + col0, (b.rows - row0) * b.raw_ld - col0);
 #pragma unroll
     for (int r = 0; r < TR; r++) {
+      const uint32_t rr_off = static_cast<uint32_t>((static_cast<uint32_t>(r) < nrows ? r : nrows - 1) * b.raw_ld);
+      raw[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rr, lane * 8, rr_off, 0));
+    }
+    x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(xp + col0, (b.cols - col0) * 2),
+                                                                         lane * 16, 0, 0));
+    cb = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(b.chunk_bits + t * 64, 128), lane * 2, 0, 0);
+    // the tile's stream words [w0 & ~3, w1 + 2) in 16-byte pieces, behind
+    // 4 zero guard words
+    w0 = tw0;
+    const uint32_t w1 = tw1;
+    a0 = w0 & ~3u;
+    const uint32_t n = stage_blocks(b, a0, w1 < w0 ? w0 : w1);
+    if (lane < 4) buf[lane] = 0u;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(b.stream + a0, (static_cast<uint64_t>(b.stream_words) + 4 - a0) * 4);
+    for (uint32_t j = 0; j < n; j += 4 * kWave)
+      if (j + 4 * lane < n)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + 4 + j), 16,
+                                                 lane * 16, j * 4, 0, 0);
+  }
+};
+
+// Lanes 0 and 1 fetch tile_words[t] and [t + 1] (0 elsewhere, or past t1).
+__device__ __forceinline__ uint32_t fetch_tile_words(const BlobDev& b, uint64_t t, uint64_t t1) {
+  const uint32_t lane = lane_id();
+  return t < t1 && lane < 2 ? b.tile_words[t + lane] : 0u;
+}
+
+// Copy this lane's words of the linearly staged stream into the lane-
+// interleaved slot (word j of lane l at slot word 64 j + l, so the decode
+// steps of the 64 lanes always hit 64 different banks).  A lane takes J
+// words starting with the one that holds bit (chunk start - 2); returns the
+// reader's start position within them.
+__device__ __forceinline__ uint32_t interleave(const uint32_t* buf, uint32_t w0, uint32_t a0, uint32_t cb,
+                                               uint32_t J, uint32_t* slot) {
+  const uint32_t sb = 128u + (w0 - a0) * 32u + wave_excl_scan(cb) - 2u;
+  const uint32_t src = lds_addr(buf) + (sb >> 5) * 4u;
+  const uint32_t dst = lds_addr(slot) + lane_id() * 4u;
+  // four words read before any is written (the compiler cannot reorder LDS
+  // reads and writes through computed addresses itself); J is even
+  for (uint32_t j = 0; j < J; j += 4) {
+    const bool two = j + 2 < J;
+    const uint32_t w0 = lds_word(src + 4 * j), w1 = lds_word(src + 4 * j + 4);
+    uint32_t w2 = 0, w3 = 0;
+    if (two) {
+      w2 = lds_word(src + 4 * j + 8);
+      w3 = lds_word(src + 4 * j + 12);
+    }
+    lds_put(dst + 256 * j, w0);
+    lds_put(dst + 256 * j + 256, w1);
+    if (two) {
+      lds_put(dst + 256 * j + 512, w2);
+      lds_put(dst + 256 * j + 768, w3);
+    }
+  }
+  return sb & 31u;
+}
+
+// Decode rows [R0, R1) of a staged tile (stream in the lane-interleaved
+// slot, raw bytes and x in registers) into this lane's row sums over its 8
+// columns.  Rows past the matrix edge (last row block only; a wave-uniform
+// test) are not decoded and keep their zero sums.
+template <int TR, int R0, int R1>
+__device__ __forceinline__ void gemv_rows(const TileRegs<TR>& in, LaneBits& br, const uint32_t* tab,
+                                          float (&acc)[TR]) {
+  const uint4& xv = in.x;
+#pragma unroll
+  for (int r = R0; r < R1; r++) {
+    if (static_cast<uint32_t>(r) < in.nrows) {
       float a = 0.0f;
       // each product is pinned next to its decode step: left alone, the
       // compiler defers all of them to the end of the tile and keeps every
       // decoded pair live, which costs occupancy
-      a = dot2(assemble(br.pair(tab, buf), in.raw[r].x, false), xv.x, a);
+      a = dot2(assemble(decode_pair(br, tab), in.raw[r].x, false), xv.x, a);
       asm volatile("" : "+v"(a));
-      a = dot2(assemble(br.pair(tab, buf), in.raw[r].x, true), xv.y, a);
+      a = dot2(assemble(decode_pair(br, tab), in.raw[r].x, true), xv.y, a);
       asm volatile("" : "+v"(a));
-      a = dot2(assemble(br.pair(tab, buf), in.raw[r].y, false), xv.z, a);
+      a = dot2(assemble(decode_pair(br, tab), in.raw[r].y, false), xv.z, a);
       asm volatile("" : "+v"(a));
-      a = dot2(assemble(br.pair(tab, buf), in.raw[r].y, true), xv.w, a);
+      a = dot2(assemble(decode_pair(br, tab), in.raw[r].y, true), xv.w, a);
       asm volatile("" : "+v"(a));
       acc[r] = a;
     }
@@ -501,9 +620,11 @@ __device__ __forceinline__ void wait_loads_after_atomic() {
 __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W) { return ((t + 1) * W - 1) / T; }
 
 // Fused decode-GEMV, batch 1, for up to kMaxJobs matrices: y_j = W_j x_j.
-// LDS: static decode table | stream buffers [waves][2][buf_words].
+// LDS: static decode table | per wavefront: linear staging buffer
+// (buf_words) | lane-interleaved slot (64 J words).  While tile t decodes from
+// the slot, tile t + 1's stream lands in the linear buffer.
 template <int TR, int MAXW>
-__global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g, uint32_t buf_words) {
+__global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const uint32_t nw = blockDim.x / kWave;
@@ -518,7 +639,9 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g, uint32
   for (int jj = 1; jj < kMaxJobs; jj++)
     if (jj == j) job = g.job[jj];
   const BlobDev& b = job.b;
-  uint32_t* bufs = lds + wave * 2 * buf_words;
+  const uint32_t J = g.lane_words;
+  uint32_t* buf = lds + wave * (g.buf_words + kWave * J);
+  uint32_t* slot = buf + g.buf_words;
   // W <= T ranges, none empty; wavefronts past the last range idle
   const uint64_t T = b.n_tiles;
   const uint64_t W = umin64(static_cast<uint64_t>(job.groups) * nw, T);
@@ -531,11 +654,13 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g, uint32
     __builtin_amdgcn_global_load_lds(b.table + base + lane * 4, tab + base, 16, 0, 0);
   uint64_t ti = t0 / n_tc;  // row block and column tile of tile t
   uint32_t tj = static_cast<uint32_t>(t0 - ti * n_tc);
-  TileIn<TR> in;
-  uint4 xv = make_uint4(0, 0, 0, 0);
+  TileRegs<TR> in;
+  uint32_t twn = 0;  // (lanes 0, 1) word offsets of tile t + 1
   if (t0 < t1) {
-    in.load(b, ti, tj, bufs);
-    xv = *reinterpret_cast<const uint4*>(job.x + (in.active ? in.c0 : 0));
+    const uint32_t tw = fetch_tile_words(b, t0, t1);
+    twn = fetch_tile_words(b, t0 + 1, t1);
+    wait_vmem();
+    in.load(b, job.x, ti, tj, __builtin_amdgcn_readlane(tw, 0), __builtin_amdgcn_readlane(tw, 1), buf);
   }
   wait_vmem();
   __syncthreads();
@@ -546,10 +671,15 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g, uint32
   // a row block is whole when this range holds all of its tiles
   bool whole = tj == 0 && ti * n_tc + n_tc <= t1;
   float run = 0.0f;
-  int slot = 0;
+  uint64_t pend[2] = {0, 0};  // cut row blocks whose share this range holds
+  uint32_t npend = 0;
   for (uint64_t t = t0; t < t1; t++) {
-    const uint32_t bit = in.start_bit();
     wait_vmem();
+    wave_sync_lds();
+    // this tile's stream into the slot; the linear buffer is then free for
+    // the next tile
+    const uint32_t q0 = interleave(buf, in.w0, in.a0, in.cb, J, slot);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the copy's reads are done
     wave_sync_lds();
     uint64_t ni = ti;
     uint32_t nj = tj + 1;
@@ -557,14 +687,23 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g, uint32
       nj = 0;
       ni++;
     }
-    TileIn<TR> nx;
-    uint4 xn = make_uint4(0, 0, 0, 0);
-    if (t + 1 < t1) {
-      nx.load(b, ni, nj, bufs + (slot ^ 1) * buf_words);
-      xn = *reinterpret_cast<const uint4*>(job.x + (nx.active ? nx.c0 : 0));
-    }
     float acc[TR];
-    gemv_tile_sums<TR>(in, xv, bit, tab, bufs + slot * buf_words, acc);
+#pragma unroll
+    for (int k = 0; k < TR; k++) acc[k] = 0.0f;
+    LaneBits br;
+    br.init(slot, q0);
+    if (in.active) gemv_rows<TR, 0, TR / 2>(in, br, tab, acc);
+    // the next tile's loads go out halfway through this one: at the start of
+    // a launch every wavefront is loading at once and issuing more loads
+    // stalls until the memory queues drain
+    asm volatile("" ::: "memory");
+    TileRegs<TR> nx;
+    uint32_t twnn = 0;
+    if (t + 1 < t1) {
+      nx.load(b, job.x, ni, nj, __builtin_amdgcn_readlane(twn, 0), __builtin_amdgcn_readlane(twn, 1), buf);
+      twnn = fetch_tile_words(b, t + 2, t1);
+    }
+    if (in.active) gemv_rows<TR, TR / 2, TR>(in, br, tab, acc);
     const float s = reduce_rows<TR>(acc);
     const uint64_t row = ti * TR + r;
     if (whole) {
@@ -575,44 +714,51 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g, uint32
       }
     } else {
       if (row_lane && row < b.rows) put_shared(job.part + t * TR + r, s);
-      if (tj + 1 == n_tc || t + 1 == t1) {
-        // this range's share of a cut row block is stored: count it; the
-        // range that completes the row block adds all its tile sums
-        const uint64_t first = ti * n_tc;
-        const uint32_t ranges = static_cast<uint32_t>(range_of(first + n_tc - 1, T, W) - range_of(first, T, W) + 1);
-        wait_stores_done();
-        uint32_t done = 0;
-        if (lane == 0) done = __hip_atomic_fetch_add(job.count + ti, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-        done = __builtin_amdgcn_readlane(done, 0);
-        if (done == ranges) {
-          wait_loads_after_atomic();
-          if (row_lane && row < b.rows) {
-            // loads issued eight at a time, added in column order; the sums
-            // are zeroed behind, so the workspace is all zero again at the end
-            float sum = 0.0f;
-            for (uint32_t k = 0; k < n_tc; k += 8) {
-              float v[8];
-#pragma unroll
-              for (uint32_t u = 0; u < 8; u++) v[u] = k + u < n_tc ? get_shared(job.part + (first + k + u) * TR + r) : 0.0f;
-#pragma unroll
-              for (uint32_t u = 0; u < 8; u++)
-                if (k + u < n_tc) {
-                  sum += v[u];
-                  put_shared(job.part + (first + k + u) * TR + r, 0.0f);
-                }
-            }
-            store_y(job.y, row, sum, g.y_f32);
-          }
-          if (lane == 0) __hip_atomic_store(job.count + ti, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+      // a cut row block's share ends here: counted at the end of the range
+      // (a range cuts at most its first and its last row block)
+      if (tj + 1 == n_tc || t + 1 == t1) pend[npend++] = ti;
     }
     ti = ni;
     tj = nj;
     if (tj == 0) whole = ti * n_tc + n_tc <= t1;
     in = nx;
-    xv = xn;
-    slot ^= 1;
+    twn = twnn;
+  }
+  if (npend == 0) return;
+  // count this range's shares of its cut row blocks (lanes 0 and 1 each do
+  // one increment); the range that completes a row block adds all its tile
+  // sums in column order and zeroes them behind
+  wait_stores_done();
+  uint32_t done = 0;
+  if (lane < npend) {
+    const uint64_t rb = lane == 0 ? pend[0] : pend[1];
+    done = __hip_atomic_fetch_add(job.count + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+  }
+  const uint32_t done0 = __builtin_amdgcn_readlane(done, 0), done1 = __builtin_amdgcn_readlane(done, 1);
+  for (uint32_t k = 0; k < npend; k++) {
+    const uint64_t rb = k == 0 ? pend[0] : pend[1];
+    const uint64_t first = rb * n_tc;
+    const uint32_t ranges = static_cast<uint32_t>(range_of(first + n_tc - 1, T, W) - range_of(first, T, W) + 1);
+    if ((k == 0 ? done0 : done1) != ranges) continue;
+    wait_loads_after_atomic();
+    const uint64_t row = rb * TR + r;
+    if (row_lane && row < b.rows) {
+      // loads issued eight at a time, added in column order
+      float sum = 0.0f;
+      for (uint32_t c = 0; c < n_tc; c += 8) {
+        float v[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8; u++) v[u] = c + u < n_tc ? get_shared(job.part + (first + c + u) * TR + r) : 0.0f;
+#pragma unroll
+        for (uint32_t u = 0; u < 8; u++)
+          if (c + u < n_tc) {
+            sum += v[u];
+            put_shared(job.part + (first + c + u) * TR + r, 0.0f);
+          }
+      }
+      store_y(job.y, row, sum, g.y_f32);
+    }
+    if (lane == 0) __hip_atomic_store(job.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -660,10 +806,10 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void k_gemm_mfma(BlobDev b, cons
       for (int r = 0; r < TR; r++) {
         uint4 o = make_uint4(0, 0, 0, 0);
         if (in.active) {
-          o.x = assemble(br.pair(tab, buf), in.raw[r].x, false);
-          o.y = assemble(br.pair(tab, buf), in.raw[r].x, true);
-          o.z = assemble(br.pair(tab, buf), in.raw[r].y, false);
-          o.w = assemble(br.pair(tab, buf), in.raw[r].y, true);
+          o.x = assemble(br.pair(tab), in.raw[r].x, false);
+          o.y = assemble(br.pair(tab), in.raw[r].x, true);
+          o.z = assemble(br.pair(tab), in.raw[r].y, false);
+          o.w = assemble(br.pair(tab), in.raw[r].y, true);
         }
         // columns past the edge must be exact zeros (they meet zero X in the
         // contraction); rows past the edge only reach rows that are not stored
@@ -741,7 +887,7 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_gemv_generic(BlobDev 
           for (uint32_t r = 0; r < nrows; r++) {
             float a = 0.0f;
             for (uint64_t k = cc0; k < cc1; k++) {
-              const uint32_t e = br.one(tab, buf);
+              const uint32_t e = br.one(tab);
               const uint32_t rb = b.raw[(row0 + r) * b.raw_ld + k];
               const uint32_t wbits = (((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu)) << 16;
               const float xf = __builtin_bit_cast(float, static_cast<uint32_t>(x[k]) << 16);
@@ -848,6 +994,7 @@ constexpr int kCUs = 256;
 struct Launch {
   BlobDev b;
   bool fast;  // S = 64, V = 8, TR in {8, 16, 32}, K % 8 == 0
+  uint32_t max_chunk_bits;
 };
 
 nwc_status prepare(const nwc_info* info, const void* blob_dev, Launch* L) {
@@ -855,6 +1002,8 @@ nwc_status prepare(const nwc_info* info, const void* blob_dev, Launch* L) {
   if (!info || !blob_dev || !nwc::info_geometry(info, &g)) return NWC_ERR_INVALID_ARG;
   if (!aligned(blob_dev, 256)) return NWC_ERR_ALIGNMENT;
   if (info->max_tile_words > 65536u) return NWC_ERR_UNSUPPORTED;
+  if (info->max_chunk_bits > static_cast<uint64_t>(g.tr) * g.v * g.lmax) return NWC_ERR_INVALID_ARG;
+  L->max_chunk_bits = info->max_chunk_bits;
   const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
   BlobDev& b = L->b;
   b.table = reinterpret_cast<const uint32_t*>(base + g.off_table);
@@ -936,18 +1085,27 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
                        int y_f32, hipStream_t s) {
   GemvGroup g;
   std::memset(&g, 0, sizeof(g));
-  uint32_t buf_words = 0;
+  uint32_t lane_words = 0, buf_words = 0;
   uint64_t total = 0;
   for (int j = 0; j < count; j++) {
+    // a lane's words start with the one holding bit (chunk start - 2), so
+    // the reader starts at bit <= 31 and its last window (at most chunk
+    // bits - 1 further) reads one word of look-ahead; rounded up to even
+    lane_words = std::max(lane_words, (((30 + L[j].max_chunk_bits) >> 5) + 2 + 1) & ~1u);
     buf_words = std::max(buf_words, L[j].b.buf_words);
     total += L[j].b.n_tiles;
   }
+  // the interleaving copy reads up to lane_words past the last chunk start;
+  // whole 256-byte units keep every slot 256-byte aligned
+  buf_words = (buf_words + lane_words + 63) & ~63u;
   // wavefronts per workgroup: the size with the most resident wavefronts
   // per CU (registers and LDS both count), the larger size on a tie
-  const size_t per_wave = 2ull * buf_words * 4;
+  const size_t per_wave = (static_cast<size_t>(kWave) * lane_words + buf_words) * 4;
   uint32_t nw = 0;
   int per_cu = 0;
-  for (uint32_t n = MAXW; n >= 1; n /= 2) {
+  const uint32_t sizes[] = {16, 12, 8, 4, 2, 1};
+  for (uint32_t n : sizes) {
+    if (n > MAXW) continue;
     const size_t l = n * per_wave;
     if (l > kMaxLds) continue;
     if (set_lds(k_gemv<TR, MAXW>, l) != hipSuccess) return NWC_ERR_HIP;
@@ -967,7 +1125,6 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   for (int j = 0; j < count; j++) {
     GemvJob& job = g.job[j];
     job.b = L[j].b;
-    job.b.buf_words = buf_words;
     job.x = x[j];
     job.y = y[j];
     job.count = reinterpret_cast<uint32_t*>(ws[j]);
@@ -980,7 +1137,9 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   }
   g.count = static_cast<uint32_t>(count);
   g.y_f32 = y_f32;
-  k_gemv<TR, MAXW><<<groups, nw * kWave, lds, s>>>(g, buf_words);
+  g.lane_words = lane_words;
+  g.buf_words = buf_words;
+  k_gemv<TR, MAXW><<<groups, nw * kWave, lds, s>>>(g);
   return launched();
 }
 

@@ -91,6 +91,8 @@ typedef struct {
   uint64_t off_code_len, off_table, off_tile_words, off_chunk_bits, off_raw, off_stream;
   uint32_t max_tile_words;         /* largest single-tile stream, in words */
   uint32_t n_symbols;              /* distinct exponent values present */
+  uint32_t max_chunk_bits;         /* longest single chunk, in bits */
+  uint32_t reserved;               /* 0 */
   uint64_t payload_bits;           /* sum of all chunk lengths */
   uint8_t code_len[256];           /* code length per exponent value */
 } nwc_info;

@@ -97,6 +97,7 @@ def test_inspect_matches_oracle_header():
     sec = oracle.sections(blob)
     assert info.max_tile_words == int(np.diff(sec["tile_words"].astype(np.int64)).max())
     assert info.payload_bits == int(sec["chunk_bits"].astype(np.int64).sum())
+    assert info.max_chunk_bits == int(sec["chunk_bits"].max())
     assert bytes(info.code_len) == bytes(sec["code_len"])
     e, _ = oracle.split(w)
     assert info.n_symbols == int((oracle.histogram(e) > 0).sum())
