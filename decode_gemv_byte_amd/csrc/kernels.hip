@@ -743,14 +743,15 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     wait_loads_after_atomic();
     const uint64_t row = rb * TR + r;
     if (row_lane && row < b.rows) {
-      // loads issued eight at a time, added in column order
+      // the loads for up to 32 column tiles are all issued before the first
+      // add, so a row block costs one memory round trip; added in column order
       float sum = 0.0f;
-      for (uint32_t c = 0; c < n_tc; c += 8) {
-        float v[8];
+      for (uint32_t c = 0; c < n_tc; c += 32) {
+        float v[32];
 #pragma unroll
-        for (uint32_t u = 0; u < 8; u++) v[u] = c + u < n_tc ? get_shared(job.part + (first + c + u) * TR + r) : 0.0f;
+        for (uint32_t u = 0; u < 32; u++) v[u] = c + u < n_tc ? get_shared(job.part + (first + c + u) * TR + r) : 0.0f;
 #pragma unroll
-        for (uint32_t u = 0; u < 8; u++)
+        for (uint32_t u = 0; u < 32; u++)
           if (c + u < n_tc) {
             sum += v[u];
             put_shared(job.part + (first + c + u) * TR + r, 0.0f);
