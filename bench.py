@@ -1,21 +1,32 @@
 #!/usr/bin/env python3
-"""Benchmark: fused decode-GEMV on compressed BF16 weights, batch 1, one MI355X.
+"""Benchmark: fused decode-GEMV on compressed BF16 weights, one MI355X.
 
-One step = the batch-1 GEMVs of one Qwen3-4B-shaped decoder layer (q, k, v,
-o, gate, up, down; seeded synthetic weights, x ~ N(0, 1)), run in the order a
-decode step needs them.  Inputs are resident in HBM before timing starts.
-To measure HBM rather than the 256 MB Infinity Cache, steps cycle through
-several device copies of the layer (>= 1 GB in total).  Each copy's step is
-captured once as a HIP graph and replayed.
+Default workload (2): one batch-1 decode step of a Qwen3-4B-shaped decoder
+layer (q, k, v, o, gate, up, down; seeded synthetic weights, x ~ N(0, 1)),
+launched in the order a decode step needs them, GEMVs that read the same
+activations sharing a launch.  Other workloads:
+  1  one 1024x1024 matrix, batch 1
+  3  a Llama-3.1-8B-shaped full step: 32 layers, 128 launches in one graph
+  4  skinny decode-GEMM, 4096x14336 and 14336x4096, --batch 2..16
+  5  LM head 128256x4096, --batch 1 or 8
 
-Prints ONE JSON line.  `value` is compressed GB/s (blob + x + y bytes per
-step / step time); the uncompressed-equivalent rate, % of HBM peak, the same
-GEMV reading plain BF16, the roofline figure of the dominant kernel and the
-CPU oracle's rate on a bounded sample are reported beside it.
+Inputs are resident in HBM before timing starts.  To measure HBM rather than
+the 256 MB Infinity Cache, steps cycle through device copies of the
+compressed weights (>= 1 GB in total).  Each copy's step is captured once as
+a HIP graph and replayed.
+
+Prints ONE JSON line.  `value` is compressed GB/s (blob + x + y bytes per step
+/ step time); the uncompressed-equivalent rate, % of HBM peak, the same GEMVs
+reading plain BF16 (our kernel and torch's), the roofline figure of the
+dominant kernel and the CPU oracle's rate on a bounded sample sit beside it.
+
+--roofline-only runs just the dominant launch (warm-up + timed repetitions),
+so that a profiler's per-kernel statistics cover exactly that launch.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +38,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+STREAM_BYTES = 1.0e9          # device copies cycled per pass, well above the Infinity Cache
+CHECK_ROWS = 256              # rows per matrix checked against an FP64 product
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemv_qwen3_4b_gate_up_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "decode_gemv_byte_amd", "csrc", "kernels.hip")
 
 
 def parse():
@@ -34,23 +49,62 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, help="workload id (1..5); 2 = Qwen3-4B-shaped layer")
+    ap.add_argument("--workload", type=int, default=2, help="1..5; 2 = Qwen3-4B-shaped layer (default)")
+    ap.add_argument("--batch", type=int, default=0, help="batch size (0 = the workload's first)")
     ap.add_argument("--copies", type=int, default=0, help="device copies cycled (0 = enough for >= 1 GB)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--roofline-reps", type=int, default=200)
-    ap.add_argument("--skip-bf16", action="store_true")
+    ap.add_argument("--roofline-only", action="store_true", help="time only the dominant launch")
+    ap.add_argument("--skip-bf16", action="store_true", help="skip the plain-BF16 comparators")
     ap.add_argument("--tile-rows", type=int, default=0, help="encoder tile rows (0 = library default)")
     ap.add_argument("--max-code-len", type=int, default=0, help="encoder code length limit (0 = library default)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB, 5 times (scales HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy of known size: what FETCH_SIZE and WRITE_SIZE read for it
+    gives the factors that turn those counters into HBM bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    for i in range(5):
+        dst[i % 2].copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "reps": 5}))
+
+
+def traffic_from_profile():
+    """Measured HBM bytes per dominant launch (FETCH_SIZE + WRITE_SIZE, each
+    scaled by a copy kernel of known size), if the kernels have not changed
+    since the counters were taken; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines() if ":" in l and not l.startswith("#"))
+    digest = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if fields.get("kernels.hip sha256", "").strip() != digest:
+        return None
+    try:
+        return int(float(fields["hbm bytes per launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(row-sharding across GPUs is described in DESIGN.md but not built)", file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(row sharding across GPUs is described in DESIGN.md but not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -59,66 +113,124 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
     wl = workloads.WORKLOADS[args.workload]
-    if wl.layers != 1 and args.workload != 3:
-        pass
-    layer_ids = [0]
-    mats = list(wl.matrices)
-    order = [m for g in wl.groups for m in g] if wl.groups else [m.name for m in mats]
+    batch = args.batch or wl.batches[0]
+    if not 1 <= batch <= 16:
+        sys.exit("batch must be 1..16")
+    params = {k: v for k, v in (("tile_rows", args.tile_rows), ("max_code_len", args.max_code_len)) if v}
+    groups_named = [list(g) for g in wl.groups] if wl.groups else [[m.name] for m in wl.matrices]
+    # the step: every layer's groups in order; a key is (layer, matrix name)
+    groups = [[(l, n) for n in g] for l in range(wl.layers) for g in groups_named]
+    keys = [k for g in groups for k in g]
+    rng = np.random.default_rng(1)
+    want_bf16 = not args.skip_bf16 and not args.roofline_only
 
     # ---------------------------------------------------------------- setup
     t0 = time.time()
-    host = {}
-    for m in mats:
-        w = workloads.weights(wl.cid, m.name, layer=0)
-        params = {k: v for k, v in (("tile_rows", args.tile_rows), ("max_code_len", args.max_code_len)) if v}
+    host_blob, info, check, wbf = {}, {}, {}, {}
+    for (l, n) in keys:
+        w = workloads.weights(wl.cid, n, layer=l)
         blob = nwc.nwc_encode(w, params or None)
-        host[m.name] = (w, blob, nwc.nwc_inspect(blob))
+        host_blob[(l, n)] = blob
+        info[(l, n)] = nwc.nwc_inspect(blob)
+        rows = np.unique(np.concatenate([rng.choice(w.shape[0], min(CHECK_ROWS, w.shape[0]), replace=False),
+                                         [0, w.shape[0] - 1]]))
+        check[(l, n)] = (rows, w[rows].copy())
+        if want_bf16:
+            wbf[(l, n)] = torch.from_numpy(w.view(np.int16)).to(dev)
+        del w
     enc_s = time.time() - t0
-    bytes_c = sum(host[n][1].size + 2 * host[n][2].cols + 2 * host[n][2].rows for n in order)
-    bytes_u = sum(2 * host[n][2].rows * host[n][2].cols + 2 * host[n][2].cols + 2 * host[n][2].rows
-                  for n in order)
-    blob_bytes = sum(host[n][1].size for n in order)
-    copies = args.copies or max(1, int(np.ceil(1.0e9 / blob_bytes)))
 
-    dev = torch.device("cuda", 0)
-    blobs = [{n: torch.from_numpy(host[n][1]).to(dev) for n in order} for _ in range(copies)]
-    xs = {n: torch.from_numpy(workloads.activations(wl.cid, n)[0]).to(dev) for n in order}
-    ys = {n: torch.empty(host[n][2].rows, dtype=torch.bfloat16, device=dev) for n in order}
-    infos = {n: host[n][2] for n in order}
+    def cbytes(k):  # compressed bytes of one GEMV / GEMM: blob + x + y
+        return host_blob[k].size + 2 * batch * (info[k].cols + info[k].rows)
+
+    def ubytes(k):
+        return 2 * info[k].rows * info[k].cols + 2 * batch * (info[k].cols + info[k].rows)
+
+    bytes_c = sum(cbytes(k) for k in keys)
+    bytes_u = sum(ubytes(k) for k in keys)
+    gbytes = [sum(cbytes(k) for k in g) for g in groups]
+    blob_total = sum(host_blob[k].size for k in keys)
+    # (a workload far smaller than the cache, like the 1024x1024 matrix, is
+    # launch-bound anyway; 64 copies bound the graphs it needs)
+    copies = args.copies or min(64, max(1, int(np.ceil(STREAM_BYTES / blob_total))))
+
+    blobs = [{k: torch.from_numpy(host_blob[k]).to(dev) for k in keys} for _ in range(copies)]
+    del host_blob
+    xs = {k: torch.from_numpy(workloads.activations(wl.cid, k[1], batch=batch, layer=k[0])).to(dev) for k in keys}
+    ys = {k: torch.empty((batch, info[k].rows) if batch > 1 else (info[k].rows,), dtype=torch.bfloat16, device=dev)
+          for k in keys}
     stream = torch.cuda.Stream()
 
-    def zeroed_ws(names):
-        # the fused path's workspace: zero-filled once, left zero by every call
-        return torch.zeros(nwc.gemv_batched_workspace_size([infos[n] for n in names]), dtype=torch.uint8,
-                           device=dev)
+    def zeroed(nbytes):
+        # workspaces are zero-filled once; every call leaves them zero
+        return torch.zeros(max(1, nbytes), dtype=torch.uint8, device=dev)
 
-    # one launch per dependency group (GEMVs that read the same activations);
-    # launches are stream-ordered, so each group's workspace serves every copy
-    groups = [list(g) for g in wl.groups] if wl.groups else [[n] for n in order]
-    gws = [zeroed_ws(g) for g in groups]
-    batches = [[nwc.GemvBatch([infos[n] for n in g], [blobs[c][n] for n in g], [xs[n] for n in g],
-                              [ys[n] for n in g], gws[k]) for k, g in enumerate(groups)] for c in range(copies)]
+    if batch == 1:
+        gws = [zeroed(nwc.gemv_batched_workspace_size([info[k] for k in g])) for g in groups]
+        launches = [[nwc.GemvBatch([info[k] for k in g], [blobs[c][k] for k in g], [xs[k][0] for k in g],
+                                   [ys[k] for k in g], gws[i]) for i, g in enumerate(groups)] for c in range(copies)]
+
+        def launch(c, i):
+            nwc.nwc_gemv_batched(launches[c][i], stream=stream)
+    else:
+        kws = {k: zeroed(nwc.nwc_workspace_size(info[k], batch)) for k in keys}
+
+        def launch(c, i):
+            for k in groups[i]:
+                nwc.nwc_gemm_skinny(info[k], blobs[c][k], xs[k], ys[k], kws[k], stream=stream)
 
     def step(c):
-        for bt in batches[c]:
-            nwc.nwc_gemv_batched(bt, stream=stream)
+        for i in range(len(groups)):
+            launch(c, i)
 
-    # correctness guard: one eager step, compared with an FP64 reference of
-    # the BF16 values computed by torch on the host (not timed)
+    # the dominant launch: the one that moves the most bytes
+    gi = int(np.argmax(gbytes))
+    reps = args.roofline_reps
+
+    def time_dominant():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            for i in range(10):
+                launch(i % copies, gi)
+            e0.record(stream)
+            for i in range(reps):
+                launch(i % copies, gi)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    dom_name = "+".join("%s%s" % (n, "@%d" % l if wl.layers > 1 else "") for (l, n) in groups[gi])
+    kernel = "k_gemv via nwc_gemv_batched" if batch == 1 else "k_gemm_mfma via nwc_gemm_skinny"
+
+    def roofline(us):
+        a = gbytes[gi] / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_from_profile() if (args.workload == 2 and batch == 1) else None,
+                "kernel": "%s (%s)" % (kernel, dom_name), "bytes_per_launch": int(gbytes[gi]),
+                "avg_launch_us": round(us, 3)}
+
+    if args.roofline_only:
+        us = time_dominant()
+        print(json.dumps({"roofline": roofline(us), "config": {"workload": wl.name, "batch": batch}}))
+        return
+
+    # correctness guard (not timed): one eager step, sampled rows against an
+    # FP64 product of the same BF16 values
     with torch.cuda.stream(stream):
         step(0)
     torch.cuda.synchronize()
-    for n in order:
-        w = host[n][0]
-        wf = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).double()
-        xf = xs[n].cpu().view(torch.bfloat16).double()
-        ref = (wf @ xf).numpy()
-        a = (wf.abs() @ xf.abs()).numpy()
-        got = ys[n].cpu().double().numpy()
-        ok = np.all(np.abs(got - ref) <= 2.0 ** -10 * a + 2.0 ** -8 * np.abs(ref))
-        if not ok:
-            print("bench: GEMV %s outside tolerance" % n, file=sys.stderr)
+    for k in keys:
+        rows, wr = check[k]
+        wf = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).double()
+        xf = xs[k].cpu().view(torch.bfloat16).double()                      # [batch, K]
+        ref = (xf @ wf.T).numpy()
+        a = (xf.abs() @ wf.abs().T).numpy()
+        got = ys[k].reshape(batch, -1).cpu().double().numpy()[:, rows]
+        if not np.all(np.abs(got - ref) <= 2.0 ** -10 * a + 2.0 ** -8 * np.abs(ref)):
+            print("bench: %s outside tolerance" % (k,), file=sys.stderr)
             sys.exit(1)
 
     graphs = None
@@ -131,141 +243,92 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
 
-    def run(k, start):
-        for i in range(k):
+    def run(n, start):
+        for i in range(n):
             c = (start + i) % copies
-            if graphs is not None:
-                with torch.cuda.stream(stream):
+            with torch.cuda.stream(stream):
+                if graphs is not None:
                     graphs[c].replay()
-            else:
-                with torch.cuda.stream(stream):
+                else:
                     step(c)
 
     # --------------------------------------------------------------- timed
     run(args.warmup, 0)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
-    ev0.record(stream)
+    e0.record(stream)
     run(args.steps, args.warmup)
-    ev1.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_start
-    ms_gpu = ev0.elapsed_time(ev1)
-    ms_per_step = ms_gpu / args.steps
-    value = bytes_c * args.steps / (ms_gpu * 1e-3) / 1e9
-    value_u = bytes_u * args.steps / (ms_gpu * 1e-3) / 1e9
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = bytes_c / (ms_per_step * 1e-3) / 1e9
+    value_u = bytes_u / (ms_per_step * 1e-3) / 1e9
+    dom_us = time_dominant()
 
-    # ------------------------------------------- dominant kernel, roofline
-    # the dominant kernel is the launch that moves the most bytes; its average
-    # duration is measured with events on the launch stream over back-to-back
-    # launches cycling the device copies
-    gbytes = [sum(host[n][1].size + 2 * infos[n].cols + 2 * infos[n].rows for n in g) for g in groups]
-    gi = int(np.argmax(gbytes))
-    dom_bytes = gbytes[gi]
-    reps = args.roofline_reps
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        for i in range(10):
-            nwc.nwc_gemv_batched(batches[i % copies][gi], stream=stream)
-        e0.record(stream)
-        for i in range(reps):
-            nwc.nwc_gemv_batched(batches[i % copies][gi], stream=stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    dom_us = e0.elapsed_time(e1) * 1e3 / reps
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-
-    # all seven GEMVs in one launch: they read independent activations here
-    iws = zeroed_ws(order)
-    indep = [nwc.GemvBatch([infos[n] for n in order], [blobs[c][n] for n in order], [xs[n] for n in order],
-                           [ys[n] for n in order], iws) for c in range(copies)]
-    with torch.cuda.stream(stream):
-        for i in range(10):
-            nwc.nwc_gemv_batched(indep[i % copies], stream=stream)
-        e0.record(stream)
-        for i in range(reps):
-            nwc.nwc_gemv_batched(indep[i % copies], stream=stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    indep_us = e0.elapsed_time(e1) * 1e3 / reps
-
-    # ------------------------------------------------ plain BF16 comparator
-    bf16 = None
-    if not args.skip_bf16:
-        wdev = {n: [torch.from_numpy(host[n][0].view(np.int16)).to(dev) for _ in range(copies)] for n in order}
-        wsb = {n: torch.empty(nwc.nwc_bf16_workspace_size(infos[n].rows, infos[n].cols), dtype=torch.uint8,
-                              device=dev) for n in order}
-        yb = {n: torch.empty(infos[n].rows, dtype=torch.bfloat16, device=dev) for n in order}
-
-        def step_bf16(c):
-            for n in order:
-                nwc.nwc_gemv_bf16(wdev[n][c], xs[n], yb[n], wsb[n], stream=stream)
-
-        gb = []
-        for c in range(copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                step_bf16(c)
-            gb.append(g)
-        torch.cuda.synchronize()
-        for i in range(args.warmup):
-            with torch.cuda.stream(stream):
-                gb[i % copies].replay()
-        torch.cuda.synchronize()
-        b0 = torch.cuda.Event(enable_timing=True)
-        b1 = torch.cuda.Event(enable_timing=True)
-        b0.record(stream)
-        for i in range(args.steps):
-            with torch.cuda.stream(stream):
-                gb[i % copies].replay()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        ms_b = b0.elapsed_time(b1) / args.steps
-        bf16 = dict(ms_per_step=round(ms_b, 5), GBps=round(bytes_u / (ms_b * 1e-3) / 1e9, 1),
-                    speedup_fused_vs_bf16=round(ms_b / ms_per_step, 3))
-
-        # the vendor library's BF16 GEMV (torch.mv), same matrices, same launch
-        # order, also graph-captured: an outside reference
-        wt = {n: [w.view(torch.bfloat16) for w in wdev[n]] for n in order}
-        xt = {n: xs[n].view(torch.bfloat16) for n in order}
-        yt = {n: torch.empty(infos[n].rows, dtype=torch.bfloat16, device=dev) for n in order}
-
-        def step_torch(c):
-            for n in order:
-                torch.mv(wt[n][c], xt[n], out=yt[n])
-
+    # every GEMV of a one-layer batch-1 step in a single launch (they read
+    # independent activations here): what the launch boundaries cost
+    single = None
+    if batch == 1 and wl.layers == 1 and len(groups) > 1:
+        iws = zeroed(nwc.gemv_batched_workspace_size([info[k] for k in keys]))
+        allb = [nwc.GemvBatch([info[k] for k in keys], [blobs[c][k] for k in keys], [xs[k][0] for k in keys],
+                              [ys[k] for k in keys], iws) for c in range(copies)]
         with torch.cuda.stream(stream):
-            step_torch(0)
+            for i in range(10):
+                nwc.nwc_gemv_batched(allb[i % copies], stream=stream)
+            e0.record(stream)
+            for i in range(reps):
+                nwc.nwc_gemv_batched(allb[i % copies], stream=stream)
+            e1.record(stream)
         torch.cuda.synchronize()
-        gt = []
-        for c in range(copies):
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        single = {"us": round(us, 3), "compressed_GBps": round(bytes_c / (us * 1e-6) / 1e9, 1)}
+
+    # -------------------------------------------- standalone decode (A5)
+    # every matrix of the step decoded to BF16 in HBM; bytes = blob read +
+    # 2 bytes per weight written
+    decode = None
+    if batch == 1:
+        wout = {k: torch.empty((info[k].rows, info[k].cols), dtype=torch.int16, device=dev) for k in keys}
+
+        def step_decode(c):
+            for k in keys:
+                nwc.nwc_decode(info[k], blobs[c][k], wout[k], stream=stream)
+        dgraphs = []
+        for c in range(copies if graphs is not None else 0):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                step_torch(c)
-            gt.append(g)
+                step_decode(c)
+            dgraphs.append(g)
         torch.cuda.synchronize()
         for i in range(args.warmup):
             with torch.cuda.stream(stream):
-                gt[i % copies].replay()
+                dgraphs[i % copies].replay() if dgraphs else step_decode(i % copies)
         torch.cuda.synchronize()
-        b0.record(stream)
+        e0.record(stream)
         for i in range(args.steps):
             with torch.cuda.stream(stream):
-                gt[i % copies].replay()
-        b1.record(stream)
+                dgraphs[i % copies].replay() if dgraphs else step_decode(i % copies)
+        e1.record(stream)
         torch.cuda.synchronize()
-        ms_t = b0.elapsed_time(b1) / args.steps
-        bf16["torch_mv"] = dict(ms_per_step=round(ms_t, 5), GBps=round(bytes_u / (ms_t * 1e-3) / 1e9, 1),
-                                    speedup_fused_vs_torch=round(ms_t / ms_per_step, 3))
-        del wdev, wt
+        ms_d = e0.elapsed_time(e1) / args.steps
+        moved = blob_total + sum(2 * info[k].rows * info[k].cols for k in keys)
+        decode = {"ms_per_step": round(ms_d, 5), "GBps_moved": round(moved / (ms_d * 1e-3) / 1e9, 1),
+                  "bytes_moved": int(moved), "pct_hbm_peak": round(100.0 * moved / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+        del wout, dgraphs
+
+    # ------------------------------------------------ plain BF16 comparators
+    bf16 = None
+    if want_bf16:
+        bf16 = bf16_comparators(torch, nwc, args, keys, info, wbf, xs, ys, batch, bytes_u, ms_per_step, stream,
+                                zeroed)
+        wbf.clear()
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(host, order, args.cpu_seconds)
+        cpu = cpu_baseline(wl, keys, info, batch, args.cpu_seconds)
 
     out = {
         "metric": "fused decode-GEMV GB/s (compressed + uncompressed-equiv), % HBM peak, batch 1",
@@ -280,20 +343,19 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "matrices": {n: [infos[n].rows, infos[n].cols] for n in order},
-                   "batch": 1, "launch_order": [list(g) for g in wl.groups], "device_copies": copies,
-                   "hip_graph": graphs is not None, "output": "bf16"},
+        "config": {"workload": wl.name, "layers": wl.layers,
+                   "matrices": {m.name: [m.rows, m.cols] for m in wl.matrices}, "batch": batch,
+                   "launch_order": groups_named, "launches_per_step": len(groups),
+                   "device_copies": copies, "hip_graph": graphs is not None, "output": "bf16",
+                   "encoder": params or "default"},
         "compressed_GBps": round(value, 1),
         "uncompressed_equiv_GBps": round(value_u, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "bytes_per_step": {"compressed": int(bytes_c), "uncompressed": int(bytes_u)},
         "bf16_gemv": bf16,
-        "single_launch_7_gemvs": {"us": round(indep_us, 3),
-                                  "compressed_GBps": round(bytes_c / (indep_us * 1e-6) / 1e9, 1)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "k_gemv via nwc_gemv_batched (%s)" % "+".join(groups[gi]),
-                     "bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_us, 3)},
+        "single_launch_all_gemvs": single,
+        "standalone_decode": decode,
+        "roofline": roofline(dom_us),
         "cpu_baseline": cpu,
         "wall_s": round(t_wall, 3),
         "encode_s": round(enc_s, 2),
@@ -301,39 +363,100 @@ def main():
     print(json.dumps(out))
 
 
-def cpu_baseline(host, order, seconds):
-    """The oracle (single-threaded C: bit-serial decode + FP64 GEMV) on a
-    bounded sample: row blocks of each matrix, round robin, until `seconds`
-    of CPU work; rate in compressed bytes per second of the sampled rows."""
+def bf16_comparators(torch, nwc, args, keys, info, wbf, xs, ys, batch, bytes_u, ms_per_step, stream, zeroed):
+    """The same GEMVs reading plain BF16 weights: our kernel with the same
+    skeleton (batch 1) and the vendor library's product (torch.mv /
+    F.linear), same matrices, same launch order, graph-captured, cycling
+    enough device copies to stream from HBM."""
+    ub = sum(2 * info[k].rows * info[k].cols for k in keys)
+    bcopies = max(1, int(np.ceil(STREAM_BYTES / ub)))
+    wdev = [{k: (wbf[k] if c == 0 else wbf[k].clone()) for k in keys} for c in range(bcopies)]
+    yb = {k: torch.empty_like(ys[k]) for k in keys}
+    wsb = {k: zeroed(nwc.nwc_bf16_workspace_size(info[k].rows, info[k].cols)) for k in keys}
+
+    def graphs_of(fn):
+        with torch.cuda.stream(stream):
+            fn(0)
+        torch.cuda.synchronize()
+        out = []
+        for c in range(bcopies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fn(c)
+            out.append(g)
+        torch.cuda.synchronize()
+        return out
+
+    def rep_timed(gr):
+        for i in range(args.warmup):
+            with torch.cuda.stream(stream):
+                gr[i % bcopies].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            with torch.cuda.stream(stream):
+                gr[i % bcopies].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    res = {}
+    if batch == 1:
+        def step_ours(c):
+            for k in keys:
+                nwc.nwc_gemv_bf16(wdev[c][k], xs[k][0], yb[k], wsb[k], stream=stream)
+        ms_b = rep_timed(graphs_of(step_ours))
+        res.update(ms_per_step=round(ms_b, 5), GBps=round(bytes_u / (ms_b * 1e-3) / 1e9, 1),
+                   speedup_fused_vs_bf16=round(ms_b / ms_per_step, 3))
+    wt = [{k: wdev[c][k].view(torch.bfloat16) for k in keys} for c in range(bcopies)]
+    xt = {k: xs[k].view(torch.bfloat16) for k in keys}
+    yt = {k: torch.empty(ys[k].shape, dtype=torch.bfloat16, device=ys[k].device) for k in keys}
+
+    def step_torch(c):
+        for k in keys:
+            if batch == 1:
+                torch.mv(wt[c][k], xt[k][0], out=yt[k])
+            else:
+                torch.nn.functional.linear(xt[k], wt[c][k], out=yt[k])
+    ms_t = rep_timed(graphs_of(step_torch))
+    res["torch"] = dict(op="torch.mv" if batch == 1 else "torch.nn.functional.linear",
+                        ms_per_step=round(ms_t, 5), GBps=round(bytes_u / (ms_t * 1e-3) / 1e9, 1),
+                        speedup_fused_vs_torch=round(ms_t / ms_per_step, 3))
+    return res
+
+
+def cpu_baseline(wl, keys, info, batch, seconds):
+    """The oracle (single-threaded C: bit-serial decode and FP64 GEMV/GEMM) on a
+    bounded sample: 256-row blocks of the workload's matrices, round robin,
+    until `seconds` of CPU work; rate in compressed bytes (blob + x + y) per
+    second of the sampled rows, the same definition as the GPU figure."""
     import oracle
-    import workloads  # noqa: F401
+    import workloads
 
     t_total = 0.0
     bytes_done = 0.0
-    rows_done = 0
     i = 0
-    blocks = {}
+    nb = 256
     while t_total < seconds and i < 1000:
-        n = order[i % len(order)]
-        w = host[n][0]
-        nb = 256
-        r0 = (i // len(order)) * nb % w.shape[0]
-        sub = np.ascontiguousarray(w[r0:r0 + nb])
-        key = (n, r0)
-        if key not in blocks:
-            blocks[key] = oracle.encode(sub, 8, 512, 64, 12)
-        blob = blocks[key]
-        x = np.zeros(sub.shape[1], np.uint16) + np.uint16(0x3F80)
+        layer, name = keys[i % len(keys)]
+        n_rows = info[(layer, name)].rows
+        r0 = (i // len(keys)) * nb % n_rows
+        sub = workloads.weights(wl.cid, name, layer=layer, rows=slice(r0, min(r0 + nb, n_rows)))
+        blob = oracle.encode(sub, 8, 512, 64, 12)
+        x = workloads.activations(wl.cid, name, batch=batch, layer=layer)
         t = time.perf_counter()
         wd = oracle.decode(blob)
-        oracle.gemv(wd, x)
+        if batch == 1:
+            oracle.gemv(wd, x[0])
+        else:
+            oracle.gemm(wd, x)
         t_total += time.perf_counter() - t
-        bytes_done += blob.size + 2 * sub.shape[1] + 2 * sub.shape[0]
-        rows_done += sub.shape[0]
+        bytes_done += blob.size + 2 * batch * (sub.shape[1] + sub.shape[0])
         i += 1
     return {"value": round(bytes_done / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d row blocks of 256 rows from the layer's matrices, oracle decode + FP64 GEMV, "
-                      "%.1f s of single-thread CPU time" % (i, t_total)}
+            "sample": "%d row blocks of 256 rows from the workload's matrices, oracle decode + FP64 %s, "
+                      "%.1f s of single-thread CPU time" % (i, "GEMV" if batch == 1 else "GEMM", t_total)}
 
 
 if __name__ == "__main__":
