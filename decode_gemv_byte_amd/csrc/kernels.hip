@@ -498,6 +498,11 @@ struct TileRegs {
   bool active;
   __device__ __forceinline__ void load(const BlobDev& b, const uint16_t* xp, uint64_t ti, uint32_t tj,
                                        uint32_t tw0, uint32_t tw1, uint32_t* buf) {
+    load_planes(b, xp, ti, tj);
+    load_stream(b, tw0, tw1, buf);
+  }
+  // raw bytes, x and chunk lengths: no dependence on the tile's word offsets
+  __device__ __forceinline__ void load_planes(const BlobDev& b, const uint16_t* xp, uint64_t ti, uint32_t tj) {
     const uint32_t lane = lane_id();
     const uint64_t t = ti * b.n_tc + tj;
     const uint64_t row0 = ti * TR;
@@ -515,8 +520,11 @@ struct TileRegs {
     x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(xp + col0, (b.cols - col0) * 2),
                                                                          lane * 16, 0, 0));
     cb = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(b.chunk_bits + t * 64, 128), lane * 2, 0, 0);
-    // the tile's stream words [w0 & ~3, w1 + 2) in 16-byte pieces, behind
-    // 4 zero guard words
+  }
+  // the tile's stream words [w0 & ~3, w1 + 2) in 16-byte pieces, behind 4 zero
+  // guard words
+  __device__ __forceinline__ void load_stream(const BlobDev& b, uint32_t tw0, uint32_t tw1, uint32_t* buf) {
+    const uint32_t lane = lane_id();
     w0 = tw0;
     const uint32_t w1 = tw1;
     a0 = w0 & ~3u;
@@ -657,10 +665,13 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   TileRegs<TR> in;
   uint32_t twn = 0;  // (lanes 0, 1) word offsets of tile t + 1
   if (t0 < t1) {
-    const uint32_t tw = fetch_tile_words(b, t0, t1);
+    // the first tile's word offsets come by scalar loads (no LDS reads are in
+    // flight yet), so only the stream waits for them while the planes and
+    // the next tile's offsets are already on their way
+    const uint32_t w0 = sload(b.tile_words, t0), w1 = sload(b.tile_words, t0 + 1);
     twn = fetch_tile_words(b, t0 + 1, t1);
-    wait_vmem();
-    in.load(b, job.x, ti, tj, __builtin_amdgcn_readlane(tw, 0), __builtin_amdgcn_readlane(tw, 1), buf);
+    in.load_planes(b, job.x, ti, tj);
+    in.load_stream(b, w0, w1, buf);
   }
   wait_vmem();
   __syncthreads();
