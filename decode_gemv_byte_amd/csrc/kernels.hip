@@ -472,8 +472,10 @@ struct GemvJob {
   uint32_t* count;  // [n_tr] ranges finished per row block
   uint32_t g0;      // first workgroup of this matrix
   uint32_t groups;  // workgroups of this matrix
+  uint32_t rb_per_group;  // 0: ranges over all tiles; else whole row blocks per workgroup
 };
 constexpr int kMaxJobs = 8;
+constexpr int kMaxGroupTiles = 64;  // tiles of a workgroup that owns whole row blocks
 struct GemvGroup {
   GemvJob job[kMaxJobs];
   uint32_t count;
@@ -629,8 +631,17 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 
 // Fused decode-GEMV, batch 1, for up to kMaxJobs matrices: y_j = W_j x_j.
 // LDS: static decode table | per wavefront: linear staging buffer
-// (buf_words) | lane-interleaved slot (64 J words).  While tile t decodes from
-// the slot, tile t + 1's stream lands in the linear buffer.
+// (buf_words) | lane-interleaved slot (64 J words) | tile sums of a
+// workgroup that owns whole row blocks [kMaxGroupTiles][TR].  While tile t
+// decodes from the slot, tile t + 1's stream lands in the linear buffer.
+// Two ways to share out a matrix's tiles:
+//  * ranges: equal contiguous ranges over all its tiles, one per wavefront;
+//    row blocks cut between ranges are added through the workspace;
+//  * whole row blocks: each workgroup owns rb_per_group row blocks and its
+//    wavefronts split their tiles; every tile sum goes to LDS and, after one
+//    barrier, the workgroup adds each row's sums in column order.  Used when
+//    it needs no more tiles per wavefront than ranges would, so small matrices
+//    skip the workspace round trips at the end.
 template <int TR, int MAXW>
 __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
@@ -650,12 +661,28 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   const uint32_t J = g.lane_words;
   uint32_t* buf = lds + wave * (g.buf_words + kWave * J);
   uint32_t* slot = buf + g.buf_words;
-  // W <= T ranges, none empty; wavefronts past the last range idle
-  const uint64_t T = b.n_tiles;
-  const uint64_t W = umin64(static_cast<uint64_t>(job.groups) * nw, T);
-  const uint64_t w = static_cast<uint64_t>(blockIdx.x - job.g0) * nw + wave;
-  const uint64_t t0 = w < W ? w * T / W : T, t1 = w < W ? (w + 1) * T / W : T;
+  float* gsum = reinterpret_cast<float*>(lds + nw * (g.buf_words + kWave * J));
   const uint32_t n_tc = b.n_tc;
+  const bool by_rows = job.rb_per_group != 0;
+  uint64_t T, W, t0, t1, g_t0 = 0, g_rb0 = 0, g_rb1 = 0;
+  if (by_rows) {
+    // this workgroup's row blocks [g_rb0, g_rb1), their tiles split evenly
+    g_rb0 = static_cast<uint64_t>(blockIdx.x - job.g0) * job.rb_per_group;
+    g_rb1 = umin64(g_rb0 + job.rb_per_group, b.n_tr);
+    g_t0 = g_rb0 * n_tc;
+    const uint64_t n = (g_rb1 - g_rb0) * n_tc;
+    T = b.n_tiles;
+    W = 0;
+    t0 = g_t0 + wave * n / nw;
+    t1 = g_t0 + (wave + 1) * n / nw;
+  } else {
+    // W <= T ranges, none empty; wavefronts past the last range idle
+    T = b.n_tiles;
+    W = umin64(static_cast<uint64_t>(job.groups) * nw, T);
+    const uint64_t w = static_cast<uint64_t>(blockIdx.x - job.g0) * nw + wave;
+    t0 = w < W ? w * T / W : T;
+    t1 = w < W ? (w + 1) * T / W : T;
+  }
 
   // the decode table and the first tile are loaded together
   for (uint32_t base = wave * kWave * 4; base < kTable; base += nw * kWave * 4)
@@ -717,7 +744,9 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     if (in.active) gemv_rows<TR, TR / 2, TR>(in, br, tab, acc);
     const float s = reduce_rows<TR>(acc);
     const uint64_t row = ti * TR + r;
-    if (whole) {
+    if (by_rows) {
+      if (row_lane) gsum[(t - g_t0) * TR + r] = s;
+    } else if (whole) {
       run += s;
       if (tj + 1 == n_tc) {
         if (row_lane && row < b.rows) store_y(job.y, row, run, g.y_f32);
@@ -734,6 +763,19 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     if (tj == 0) whole = ti * n_tc + n_tc <= t1;
     in = nx;
     twn = twnn;
+  }
+  if (by_rows) {
+    __syncthreads();
+    for (uint32_t k = threadIdx.x; k < (g_rb1 - g_rb0) * TR; k += blockDim.x) {
+      const uint32_t i = k / TR, rr = k % TR;
+      const uint64_t row2 = (g_rb0 + i) * TR + rr;
+      if (row2 < b.rows) {
+        float sum = 0.0f;
+        for (uint32_t c = 0; c < n_tc; c++) sum += gsum[(i * n_tc + c) * TR + rr];
+        store_y(job.y, row2, sum, g.y_f32);
+      }
+    }
+    return;
   }
   if (npend == 0) return;
   // count this range's shares of its cut row blocks (lanes 0 and 1 each do
@@ -1113,6 +1155,7 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   // wavefronts per workgroup: the size with the most resident wavefronts
   // per CU (registers and LDS both count), the larger size on a tie
   const size_t per_wave = (static_cast<size_t>(kWave) * lane_words + buf_words) * 4;
+  const size_t group_sums = static_cast<size_t>(kMaxGroupTiles) * TR * 4;
   uint32_t nw = 0;
   int per_cu = 0;
   const uint32_t sizes[] = {16, 12, 8, 4, 2, 1};
@@ -1130,9 +1173,31 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     }
   }
   if (nw == 0 || per_cu < 1) return NWC_ERR_UNSUPPORTED;
-  const size_t lds = nw * per_wave;
-  if (set_lds(k_gemv<TR, MAXW>, lds) != hipSuccess) return NWC_ERR_HIP;
   const uint64_t cap = static_cast<uint64_t>(cu_count()) * per_cu;
+  // whole row blocks per workgroup when that needs no more tiles per
+  // wavefront than ranges over all resident wavefronts, fits at once, and
+  // the tile sums' LDS costs no residency
+  bool by_rows = nw * per_wave + group_sums <= kMaxLds;
+  if (by_rows) {
+    int k = 0;
+    if (set_lds(k_gemv<TR, MAXW>, nw * per_wave + group_sums) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&k, k_gemv<TR, MAXW>, nw * kWave, nw * per_wave + group_sums) !=
+            hipSuccess)
+      return NWC_ERR_HIP;
+    by_rows = k == per_cu;
+  }
+  if (by_rows) {
+    const uint64_t waves = std::min<uint64_t>(cap * nw, total);
+    const uint64_t range_max = (total + waves - 1) / waves;
+    uint64_t need = 0;
+    for (int j = 0; j < count; j++) {
+      const uint64_t n_tc = L[j].b.n_tc;
+      const uint64_t r = std::max<uint64_t>(1, nw / n_tc);
+      if (r * n_tc > kMaxGroupTiles || (r * n_tc + nw - 1) / nw > range_max) by_rows = false;
+      need += (L[j].b.n_tr + r - 1) / r;
+    }
+    if (need > cap) by_rows = false;
+  }
   uint32_t groups = 0;
   for (int j = 0; j < count; j++) {
     GemvJob& job = g.job[j];
@@ -1142,11 +1207,19 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     job.count = reinterpret_cast<uint32_t*>(ws[j]);
     job.part = reinterpret_cast<float*>(ws[j] + (job.b.n_tr * 4 + 255) / 256 * 256);
     const uint64_t T = job.b.n_tiles;
-    const uint64_t share = 1 + (cap - count) * T / total;
-    job.groups = static_cast<uint32_t>(std::min<uint64_t>((T + nw - 1) / nw, share));
+    if (by_rows) {
+      job.rb_per_group = static_cast<uint32_t>(std::max<uint64_t>(1, nw / job.b.n_tc));
+      job.groups = static_cast<uint32_t>((job.b.n_tr + job.rb_per_group - 1) / job.rb_per_group);
+    } else {
+      const uint64_t share = 1 + (cap - count) * T / total;
+      job.rb_per_group = 0;
+      job.groups = static_cast<uint32_t>(std::min<uint64_t>((T + nw - 1) / nw, share));
+    }
     job.g0 = groups;
     groups += job.groups;
   }
+  const size_t lds = nw * per_wave + (by_rows ? group_sums : 0);
+  if (set_lds(k_gemv<TR, MAXW>, lds) != hipSuccess) return NWC_ERR_HIP;
   g.count = static_cast<uint32_t>(count);
   g.y_f32 = y_f32;
   g.lane_words = lane_words;
