@@ -127,6 +127,12 @@ __device__ __forceinline__ float partner(float v) {
 
 // Wait for every outstanding vector-memory load (including loads into LDS).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// all but the last N vector-memory operations of this wavefront are complete
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -496,32 +502,54 @@ template <int TR>
 struct TileRegs {
   uint2 raw[TR];
   uint4 x;
-  uint32_t cb, w0, a0, nrows;
+  // cbw: the dword holding this lane's chunk length (lanes 2k and 2k + 1
+  // share one); the half is picked where it is used, so no instruction
+  // touches the loaded value before the tile is waited for
+  uint32_t cbw, w0, a0, nrows;
+  uint32_t twn;  // (lanes 0, 1) word offsets of the tile after this one
   bool active;
+  __device__ __forceinline__ uint32_t cb() const { return __builtin_amdgcn_ubfe(cbw, (lane_id() & 1) * 16, 16); }
+  // A tile's loads come in two groups: what the first half of its rows needs
+  // (load_stream, load_planes) and the raw bytes of the second half
+  // (load_rest), issued last so that decoding can start before they land.
+  // The stream goes first: its number of pieces varies, and with a fixed
+  // number of loads behind it every wait on this tile has a known count.
   __device__ __forceinline__ void load(const BlobDev& b, const uint16_t* xp, uint64_t ti, uint32_t tj,
                                        uint32_t tw0, uint32_t tw1, uint32_t* buf) {
-    load_planes(b, xp, ti, tj);
     load_stream(b, tw0, tw1, buf);
+    load_planes(b, xp, ti, tj);
   }
-  // raw bytes, x and chunk lengths: no dependence on the tile's word offsets
+  // chunk lengths, x and the raw bytes of rows [0, TR / 2): no dependence on
+  // the tile's word offsets
   __device__ __forceinline__ void load_planes(const BlobDev& b, const uint16_t* xp, uint64_t ti, uint32_t tj) {
     const uint32_t lane = lane_id();
     const uint64_t t = ti * b.n_tc + tj;
     const uint64_t row0 = ti * TR;
     nrows = static_cast<uint32_t>(umin64(TR, b.rows - row0));
     active = static_cast<uint64_t>(tj) * 512 + lane * 8 < b.cols;
-    // raw plane: rows past the matrix edge re-read the last valid row
+    const uint64_t col0 = static_cast<uint64_t>(tj) * 512;
+    cbw = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(b.chunk_bits + t * 64, 128), (lane & ~1u) * 2, 0, 0);
+    x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(xp + col0, (b.cols - col0) * 2),
+                                                                         lane * 16, 0, 0));
+    load_raw<0, TR / 2>(b, ti, tj);
+  }
+  __device__ __forceinline__ void load_rest(const BlobDev& b, uint64_t ti, uint32_t tj) {
+    load_raw<TR / 2, TR>(b, ti, tj);
+  }
+  // raw plane rows [R0, R1) of the tile: rows past the matrix edge re-read
+  // the last valid row
+  template <int R0, int R1>
+  __device__ __forceinline__ void load_raw(const BlobDev& b, uint64_t ti, uint32_t tj) {
+    const uint32_t lane = lane_id();
+    const uint64_t row0 = ti * TR;
     const uint64_t col0 = static_cast<uint64_t>(tj) * 512;
     const __amdgpu_buffer_rsrc_t rr =
         buf_rsrc(b.raw + row0 * b.raw_ld + col0, (b.rows - row0) * b.raw_ld - col0);
 #pragma unroll
-    for (int r = 0; r < TR; r++) {
+    for (int r = R0; r < R1; r++) {
       const uint32_t rr_off = static_cast<uint32_t>((static_cast<uint32_t>(r) < nrows ? r : nrows - 1) * b.raw_ld);
       raw[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rr, lane * 8, rr_off, 0));
     }
-    x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(xp + col0, (b.cols - col0) * 2),
-                                                                         lane * 16, 0, 0));
-    cb = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(b.chunk_bits + t * 64, 128), lane * 2, 0, 0);
   }
   // the tile's stream words [w0 & ~3, w1 + 2) in 16-byte pieces, behind 4 zero
   // guard words
@@ -684,24 +712,34 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     t1 = w < W ? (w + 1) * T / W : T;
   }
 
-  // the decode table and the first tile are loaded together
-  for (uint32_t base = wave * kWave * 4; base < kTable; base += nw * kWave * 4)
-    __builtin_amdgcn_global_load_lds(b.table + base + lane * 4, tab + base, 16, 0, 0);
   uint64_t ti = t0 / n_tc;  // row block and column tile of tile t
   uint32_t tj = static_cast<uint32_t>(t0 - ti * n_tc);
   TileRegs<TR> in;
-  uint32_t twn = 0;  // (lanes 0, 1) word offsets of tile t + 1
-  if (t0 < t1) {
-    // the first tile's word offsets come by scalar loads (no LDS reads are in
-    // flight yet), so only the stream waits for them while the planes and
-    // the next tile's offsets are already on their way
-    const uint32_t w0 = sload(b.tile_words, t0), w1 = sload(b.tile_words, t0 + 1);
-    twn = fetch_tile_words(b, t0 + 1, t1);
-    in.load_planes(b, job.x, ti, tj);
-    in.load_stream(b, w0, w1, buf);
+  auto load_first = [&]() __attribute__((always_inline)) {
+    if (t0 < t1) {
+      // the first tile's word offsets come by scalar loads (no LDS reads are
+      // in flight yet)
+      const uint32_t w0 = sload(b.tile_words, t0), w1 = sload(b.tile_words, t0 + 1);
+      in.load(b, job.x, ti, tj, w0, w1, buf);
+      in.twn = fetch_tile_words(b, t0 + 1, t1);
+      asm volatile("" ::: "memory");
+      in.load_rest(b, ti, tj);
+    }
+  };
+  // Wavefront 0 loads the decode table and waits for it alone; the others
+  // only pass the barrier, so each wavefront starts when its own first tile
+  // lands rather than when the workgroup's last one does.  Wavefront 0 asks
+  // for its tile after the barrier.
+  if (wave == 0) {
+    for (uint32_t base = 0; base < kTable; base += kWave * 4)
+      __builtin_amdgcn_global_load_lds(b.table + base + lane * 4, tab + base, 16, 0, 0);
+    wait_vmem();
+  } else {
+    load_first();
   }
-  wait_vmem();
-  __syncthreads();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (wave == 0) load_first();
 
   constexpr uint32_t lanes_per_row = kWave / TR;
   const bool row_lane = (lane & (lanes_per_row - 1)) == 0;
@@ -712,11 +750,11 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   uint64_t pend[2] = {0, 0};  // cut row blocks whose share this range holds
   uint32_t npend = 0;
   for (uint64_t t = t0; t < t1; t++) {
-    wait_vmem();
+    wait_vmem_but<TR / 2>();
     wave_sync_lds();
     // this tile's stream into the slot; the linear buffer is then free for
     // the next tile
-    const uint32_t q0 = interleave(buf, in.w0, in.a0, in.cb, J, slot);
+    const uint32_t q0 = interleave(buf, in.w0, in.a0, in.cb(), J, slot);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the copy's reads are done
     wave_sync_lds();
     uint64_t ni = ti;
@@ -731,15 +769,18 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     LaneBits br;
     br.init(slot, q0);
     if (in.active) gemv_rows<TR, 0, TR / 2>(in, br, tab, acc);
-    // the next tile's loads go out halfway through this one: at the start of
-    // a launch every wavefront is loading at once and issuing more loads
-    // stalls until the memory queues drain
+    // the second half's raw bytes, then the next tile's loads: they go out
+    // halfway through this tile, since at the start of a launch every
+    // wavefront is loading at once and issuing more loads stalls until the
+    // memory queues drain.  Nothing touches them before the next iteration.
+    wait_vmem();
     asm volatile("" ::: "memory");
     TileRegs<TR> nx;
-    uint32_t twnn = 0;
     if (t + 1 < t1) {
-      nx.load(b, job.x, ni, nj, __builtin_amdgcn_readlane(twn, 0), __builtin_amdgcn_readlane(twn, 1), buf);
-      twnn = fetch_tile_words(b, t + 2, t1);
+      nx.load(b, job.x, ni, nj, __builtin_amdgcn_readlane(in.twn, 0), __builtin_amdgcn_readlane(in.twn, 1), buf);
+      nx.twn = fetch_tile_words(b, t + 2, t1);
+      asm volatile("" ::: "memory");
+      nx.load_rest(b, ni, nj);
     }
     if (in.active) gemv_rows<TR, TR / 2, TR>(in, br, tab, acc);
     const float s = reduce_rows<TR>(acc);
@@ -762,7 +803,6 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     tj = nj;
     if (tj == 0) whole = ti * n_tc + n_tc <= t1;
     in = nx;
-    twn = twnn;
   }
   if (by_rows) {
     __syncthreads();
