@@ -476,18 +476,19 @@ struct GemvJob {
   void* y;
   float* part;      // [n_tiles][TR] tile sums of cut row blocks
   uint32_t* count;  // [n_tr] ranges finished per row block
-  uint32_t g0;      // first workgroup of this matrix
-  uint32_t groups;  // workgroups of this matrix
-  uint32_t rb_per_group;  // 0: ranges over all tiles; else whole row blocks per workgroup
+  uint32_t g0;          // first workgroup of this matrix
+  uint32_t groups;      // workgroups of this matrix
+  uint32_t whole_rows;  // 1: each range is whole row blocks; 0: ranges cut anywhere
 };
 constexpr int kMaxJobs = 8;
-constexpr int kMaxGroupTiles = 64;  // tiles of a workgroup that owns whole row blocks
+constexpr uint32_t kGroupLds = 8192;       // per-workgroup LDS: control words, offsets, tile sums
 struct GemvGroup {
   GemvJob job[kMaxJobs];
   uint32_t count;
   int y_f32;
   uint32_t lane_words;  // stream words per lane in the interleaved slot (J, even)
   uint32_t buf_words;   // linear staging buffer per wavefront
+  uint32_t tw_words;    // LDS words for a range's tile offsets (>= tiles + 1)
 };
 
 // Registers of one tile for the batch-1 kernel: raw bytes of this lane's
@@ -506,7 +507,6 @@ struct TileRegs {
   // share one); the half is picked where it is used, so no instruction
   // touches the loaded value before the tile is waited for
   uint32_t cbw, w0, a0, nrows;
-  uint32_t twn;  // (lanes 0, 1) word offsets of the tile after this one
   bool active;
   __device__ __forceinline__ uint32_t cb() const { return __builtin_amdgcn_ubfe(cbw, (lane_id() & 1) * 16, 16); }
   // A tile's loads come in two groups: what the first half of its rows needs
@@ -568,12 +568,6 @@ struct TileRegs {
   }
 };
 
-// Lanes 0 and 1 fetch tile_words[t] and [t + 1] (0 elsewhere, or past t1).
-__device__ __forceinline__ uint32_t fetch_tile_words(const BlobDev& b, uint64_t t, uint64_t t1) {
-  const uint32_t lane = lane_id();
-  return t < t1 && lane < 2 ? b.tile_words[t + lane] : 0u;
-}
-
 // Copy this lane's words of the linearly staged stream into the lane-
 // interleaved slot (word j of lane l at slot word 64 j + l, so the decode
 // steps of the 64 lanes always hit 64 different banks).  A lane takes J
@@ -634,11 +628,11 @@ __device__ __forceinline__ void gemv_rows(const TileRegs<TR>& in, LaneBits& br, 
 
 // Data handed between workgroups.  On this chip each XCD has its own L2, and
 // an agent-scope fence writes back or invalidates the whole L2, which is far
-// too slow to do once per wavefront.  The partial sums instead go through
+// too slow to do once per workgroup.  The partial sums instead go through
 // agent-scope atomic stores and loads, which write and read through to the
-// level shared by all XCDs, and ordering needs only a wait for this
-// wavefront's own memory operations: the stores are complete before the
-// counter is incremented, and the loads are issued after its result returns.
+// level shared by all XCDs, and ordering needs only waits for the
+// workgroup's own memory operations: its stores are complete before the
+// counter is incremented, and its loads are issued after the result returns.
 __device__ __forceinline__ void put_shared(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -649,27 +643,24 @@ __device__ __forceinline__ void wait_stores_done() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   wait_vmem();
 }
-__device__ __forceinline__ void wait_loads_after_atomic() {
-  wait_vmem();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
-// wavefront whose range holds tile t, for ranges [w T / W, (w + 1) T / W)
+// the range that holds tile t, for ranges [w T / W, (w + 1) T / W)
 __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W) { return ((t + 1) * W - 1) / T; }
 
 // Fused decode-GEMV, batch 1, for up to kMaxJobs matrices: y_j = W_j x_j.
 // LDS: static decode table | per wavefront: linear staging buffer
-// (buf_words) | lane-interleaved slot (64 J words) | tile sums of a
-// workgroup that owns whole row blocks [kMaxGroupTiles][TR].  While tile t
-// decodes from the slot, tile t + 1's stream lands in the linear buffer.
-// Two ways to share out a matrix's tiles:
-//  * ranges: equal contiguous ranges over all its tiles, one per wavefront;
-//    row blocks cut between ranges are added through the workspace;
-//  * whole row blocks: each workgroup owns rb_per_group row blocks and its
-//    wavefronts split their tiles; every tile sum goes to LDS and, after one
-//    barrier, the workgroup adds each row's sums in column order.  Used when
-//    it needs no more tiles per wavefront than ranges would, so small matrices
-//    skip the workspace round trips at the end.
+// (buf_words) | lane-interleaved slot (64 J words) | per workgroup: control
+// words | word offsets of the range's tiles | the range's tile sums
+// [tiles][TR].
+// Each workgroup owns a contiguous range of a matrix's tiles (whole row
+// blocks when that keeps the ranges even).  Its wavefronts start on the
+// range's first tiles, then claim the rest one at a time from an LDS
+// counter, halfway through their current tile, so a tile goes to whichever
+// wavefront is furthest along.  While tile t decodes from the slot, the next
+// tile's stream lands in the linear buffer.  Every tile sum goes to LDS;
+// after one barrier the workgroup adds each row's sums in column order.  A
+// row block cut by a range edge has its tile sums added through the
+// workspace by whichever workgroup finishes it last.
 template <int TR, int MAXW>
 __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
@@ -689,67 +680,80 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   const uint32_t J = g.lane_words;
   uint32_t* buf = lds + wave * (g.buf_words + kWave * J);
   uint32_t* slot = buf + g.buf_words;
-  float* gsum = reinterpret_cast<float*>(lds + nw * (g.buf_words + kWave * J));
+  // [0] next tile of the range, [1] cut row blocks this workgroup completes
+  // (bit 0 the first, bit 1 the last)
+  uint32_t* ctl = lds + nw * (g.buf_words + kWave * J);
+  uint32_t* tw = ctl + 4;  // tile_words[r0 .. r1]
+  float* gsum = reinterpret_cast<float*>(tw + g.tw_words);
   const uint32_t n_tc = b.n_tc;
-  const bool by_rows = job.rb_per_group != 0;
-  uint64_t T, W, t0, t1, g_t0 = 0, g_rb0 = 0, g_rb1 = 0;
-  if (by_rows) {
-    // this workgroup's row blocks [g_rb0, g_rb1), their tiles split evenly
-    g_rb0 = static_cast<uint64_t>(blockIdx.x - job.g0) * job.rb_per_group;
-    g_rb1 = umin64(g_rb0 + job.rb_per_group, b.n_tr);
-    g_t0 = g_rb0 * n_tc;
-    const uint64_t n = (g_rb1 - g_rb0) * n_tc;
-    T = b.n_tiles;
-    W = 0;
-    t0 = g_t0 + wave * n / nw;
-    t1 = g_t0 + (wave + 1) * n / nw;
+  const uint64_t T = b.n_tiles;
+  // this workgroup's tiles [r0, r1)
+  const uint64_t G = job.groups, gi = blockIdx.x - job.g0;
+  uint64_t r0, r1;
+  if (job.whole_rows) {
+    r0 = gi * b.n_tr / G * n_tc;
+    r1 = (gi + 1) * b.n_tr / G * n_tc;
   } else {
-    // W <= T ranges, none empty; wavefronts past the last range idle
-    T = b.n_tiles;
-    W = umin64(static_cast<uint64_t>(job.groups) * nw, T);
-    const uint64_t w = static_cast<uint64_t>(blockIdx.x - job.g0) * nw + wave;
-    t0 = w < W ? w * T / W : T;
-    t1 = w < W ? (w + 1) * T / W : T;
+    r0 = gi * T / G;
+    r1 = (gi + 1) * T / G;
   }
+  const uint32_t n_r = static_cast<uint32_t>(r1 - r0);
 
-  uint64_t ti = t0 / n_tc;  // row block and column tile of tile t
-  uint32_t tj = static_cast<uint32_t>(t0 - ti * n_tc);
+  // the next tile of the range (claimed by lane 0, given to the wavefront)
+  auto claim = [&]() __attribute__((always_inline)) {
+    uint32_t v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return r0 + __builtin_amdgcn_readfirstlane(v);
+  };
+  // Wavefronts 1.. take the range's first tiles in order and ask for them at
+  // once.  Wavefront 0 sets the counter past those, loads the decode table
+  // and the range's word offsets, and waits for them alone; the barrier then
+  // publishes all three, and wavefront 0 claims its first tile after it.
+  // (when the first tiles cover the whole range, nothing is claimed)
+  const bool claims = n_r > nw - 1;
   TileRegs<TR> in;
-  auto load_first = [&]() __attribute__((always_inline)) {
-    if (t0 < t1) {
-      // the first tile's word offsets come by scalar loads (no LDS reads are
-      // in flight yet)
-      const uint32_t w0 = sload(b.tile_words, t0), w1 = sload(b.tile_words, t0 + 1);
+  uint64_t t = r1;
+  if (wave == 0) {
+    if (lane == 0) {
+      ctl[0] = nw - 1;
+      ctl[1] = 0u;
+    }
+    for (uint32_t base = 0; base < kTable; base += kWave * 4)
+      __builtin_amdgcn_global_load_lds(b.table + base + lane * 4, tab + base, 16, 0, 0);
+    if (claims)
+      for (uint32_t i = lane; i <= n_r; i += kWave) tw[i] = b.tile_words[r0 + i];
+    wait_vmem();
+  } else if (wave - 1 < n_r) {
+    // the first tile's word offsets come by scalar loads (no LDS reads are
+    // in flight yet)
+    t = r0 + wave - 1;
+    const uint64_t ti = t / n_tc;
+    const uint32_t tj = static_cast<uint32_t>(t - ti * n_tc);
+    const uint32_t w0 = sload(b.tile_words, t), w1 = sload(b.tile_words, t + 1);
+    in.load(b, job.x, ti, tj, w0, w1, buf);
+    asm volatile("" ::: "memory");
+    in.load_rest(b, ti, tj);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's LDS writes are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (wave == 0 && claims) {
+    t = claim();
+    if (t < r1) {
+      const uint64_t ti = t / n_tc;
+      const uint32_t tj = static_cast<uint32_t>(t - ti * n_tc);
+      const uint32_t w0 = __builtin_amdgcn_readfirstlane(tw[t - r0]);
+      const uint32_t w1 = __builtin_amdgcn_readfirstlane(tw[t - r0 + 1]);
       in.load(b, job.x, ti, tj, w0, w1, buf);
-      in.twn = fetch_tile_words(b, t0 + 1, t1);
       asm volatile("" ::: "memory");
       in.load_rest(b, ti, tj);
     }
-  };
-  // Wavefront 0 loads the decode table and waits for it alone; the others
-  // only pass the barrier, so each wavefront starts when its own first tile
-  // lands rather than when the workgroup's last one does.  Wavefront 0 asks
-  // for its tile after the barrier.
-  if (wave == 0) {
-    for (uint32_t base = 0; base < kTable; base += kWave * 4)
-      __builtin_amdgcn_global_load_lds(b.table + base + lane * 4, tab + base, 16, 0, 0);
-    wait_vmem();
-  } else {
-    load_first();
   }
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  if (wave == 0) load_first();
 
   constexpr uint32_t lanes_per_row = kWave / TR;
   const bool row_lane = (lane & (lanes_per_row - 1)) == 0;
   const uint32_t r = lane / lanes_per_row;  // row of the reduced sum this lane holds
-  // a row block is whole when this range holds all of its tiles
-  bool whole = tj == 0 && ti * n_tc + n_tc <= t1;
-  float run = 0.0f;
-  uint64_t pend[2] = {0, 0};  // cut row blocks whose share this range holds
-  uint32_t npend = 0;
-  for (uint64_t t = t0; t < t1; t++) {
+  while (t < r1) {
     wait_vmem_but<TR / 2>();
     wave_sync_lds();
     // this tile's stream into the slot; the linear buffer is then free for
@@ -757,12 +761,6 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     const uint32_t q0 = interleave(buf, in.w0, in.a0, in.cb(), J, slot);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the copy's reads are done
     wave_sync_lds();
-    uint64_t ni = ti;
-    uint32_t nj = tj + 1;
-    if (nj == n_tc) {
-      nj = 0;
-      ni++;
-    }
     float acc[TR];
 #pragma unroll
     for (int k = 0; k < TR; k++) acc[k] = 0.0f;
@@ -770,89 +768,95 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     br.init(slot, q0);
     if (in.active) gemv_rows<TR, 0, TR / 2>(in, br, tab, acc);
     // the second half's raw bytes, then the next tile's loads: they go out
-    // halfway through this tile, since at the start of a launch every
-    // wavefront is loading at once and issuing more loads stalls until the
-    // memory queues drain.  Nothing touches them before the next iteration.
+    // halfway through this tile and nothing touches them before the next
+    // iteration
     wait_vmem();
     asm volatile("" ::: "memory");
     TileRegs<TR> nx;
-    if (t + 1 < t1) {
-      nx.load(b, job.x, ni, nj, __builtin_amdgcn_readlane(in.twn, 0), __builtin_amdgcn_readlane(in.twn, 1), buf);
-      nx.twn = fetch_tile_words(b, t + 2, t1);
+    const uint64_t tn = claims ? claim() : r1;
+    if (tn < r1) {
+      const uint64_t ni = tn / n_tc;
+      const uint32_t nj = static_cast<uint32_t>(tn - ni * n_tc);
+      const uint32_t w0 = __builtin_amdgcn_readfirstlane(tw[tn - r0]);
+      const uint32_t w1 = __builtin_amdgcn_readfirstlane(tw[tn - r0 + 1]);
+      nx.load(b, job.x, ni, nj, w0, w1, buf);
       asm volatile("" ::: "memory");
       nx.load_rest(b, ni, nj);
     }
     if (in.active) gemv_rows<TR, TR / 2, TR>(in, br, tab, acc);
     const float s = reduce_rows<TR>(acc);
-    const uint64_t row = ti * TR + r;
-    if (by_rows) {
-      if (row_lane) gsum[(t - g_t0) * TR + r] = s;
-    } else if (whole) {
-      run += s;
-      if (tj + 1 == n_tc) {
-        if (row_lane && row < b.rows) store_y(job.y, row, run, g.y_f32);
-        run = 0.0f;
-      }
-    } else {
-      if (row_lane && row < b.rows) put_shared(job.part + t * TR + r, s);
-      // a cut row block's share ends here: counted at the end of the range
-      // (a range cuts at most its first and its last row block)
-      if (tj + 1 == n_tc || t + 1 == t1) pend[npend++] = ti;
-    }
-    ti = ni;
-    tj = nj;
-    if (tj == 0) whole = ti * n_tc + n_tc <= t1;
+    if (row_lane) gsum[(t - r0) * TR + r] = s;
     in = nx;
+    t = tn;
   }
-  if (by_rows) {
-    __syncthreads();
-    for (uint32_t k = threadIdx.x; k < (g_rb1 - g_rb0) * TR; k += blockDim.x) {
-      const uint32_t i = k / TR, rr = k % TR;
-      const uint64_t row2 = (g_rb0 + i) * TR + rr;
-      if (row2 < b.rows) {
-        float sum = 0.0f;
-        for (uint32_t c = 0; c < n_tc; c++) sum += gsum[(i * n_tc + c) * TR + rr];
-        store_y(job.y, row2, sum, g.y_f32);
+  __syncthreads();
+
+  // Row blocks [rb_a, rb_b] meet the range; a cut one (the first or the last)
+  // leaves its tile sums in the workspace.
+  if (n_r == 0) return;
+  const uint64_t rb_a = r0 / n_tc, rb_b = (r1 - 1) / n_tc;
+  const bool cut_a = r0 != rb_a * n_tc || r1 < rb_a * n_tc + n_tc;
+  const bool cut_b = r1 != rb_b * n_tc + n_tc || r0 > rb_b * n_tc;
+  for (uint32_t k = threadIdx.x; k < (rb_b - rb_a + 1) * TR; k += blockDim.x) {
+    const uint64_t rb = rb_a + k / TR;
+    const uint32_t rr = k % TR;
+    const uint64_t row = rb * TR + rr;
+    if (row >= b.rows) continue;
+    const uint64_t c0 = rb * n_tc > r0 ? rb * n_tc : r0;
+    const uint64_t c1 = rb * n_tc + n_tc < r1 ? rb * n_tc + n_tc : r1;
+    if ((rb == rb_a && cut_a) || (rb == rb_b && cut_b)) {
+      for (uint64_t c = c0; c < c1; c++) put_shared(job.part + c * TR + rr, gsum[(c - r0) * TR + rr]);
+    } else {
+      float sum = 0.0f;
+      for (uint64_t c = c0; c < c1; c++) sum += gsum[(c - r0) * TR + rr];
+      store_y(job.y, row, sum, g.y_f32);
+    }
+  }
+  if (!cut_a && !cut_b) return;
+  // count this workgroup's share of each cut row block; the workgroup that
+  // completes one adds all its tile sums in column order and zeroes them
+  wait_stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t mine = 0;
+    for (uint32_t k = 0; k < 2; k++) {
+      if (k == 0 ? !cut_a : (!cut_b || (rb_b == rb_a && cut_a))) continue;
+      const uint64_t rb = k == 0 ? rb_a : rb_b;
+      const uint64_t first = rb * n_tc;
+      const uint32_t groups = static_cast<uint32_t>(range_of(first + n_tc - 1, T, G) - range_of(first, T, G) + 1);
+      const uint32_t done = __hip_atomic_fetch_add(job.count + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+      if (done == groups) {
+        mine |= 1u << k;
+        __hip_atomic_store(job.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    return;
+    ctl[1] = mine;
   }
-  if (npend == 0) return;
-  // count this range's shares of its cut row blocks (lanes 0 and 1 each do
-  // one increment); the range that completes a row block adds all its tile
-  // sums in column order and zeroes them behind
-  wait_stores_done();
-  uint32_t done = 0;
-  if (lane < npend) {
-    const uint64_t rb = lane == 0 ? pend[0] : pend[1];
-    done = __hip_atomic_fetch_add(job.count + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-  }
-  const uint32_t done0 = __builtin_amdgcn_readlane(done, 0), done1 = __builtin_amdgcn_readlane(done, 1);
-  for (uint32_t k = 0; k < npend; k++) {
-    const uint64_t rb = k == 0 ? pend[0] : pend[1];
+  __syncthreads();
+  const uint32_t mine = ctl[1];
+  for (uint32_t k = 0; k < 2; k++) {
+    if (!(mine >> k & 1u)) continue;
+    const uint64_t rb = k == 0 ? rb_a : rb_b;
     const uint64_t first = rb * n_tc;
-    const uint32_t ranges = static_cast<uint32_t>(range_of(first + n_tc - 1, T, W) - range_of(first, T, W) + 1);
-    if ((k == 0 ? done0 : done1) != ranges) continue;
-    wait_loads_after_atomic();
-    const uint64_t row = rb * TR + r;
-    if (row_lane && row < b.rows) {
-      // the loads for up to 32 column tiles are all issued before the first
-      // add, so a row block costs one memory round trip; added in column order
+    for (uint32_t rr = threadIdx.x; rr < TR; rr += blockDim.x) {
+      const uint64_t row = rb * TR + rr;
+      if (row >= b.rows) continue;
+      // up to 32 tile sums are loaded before the first add, so a row block
+      // costs one memory round trip per 32 column tiles
       float sum = 0.0f;
       for (uint32_t c = 0; c < n_tc; c += 32) {
         float v[32];
 #pragma unroll
-        for (uint32_t u = 0; u < 32; u++) v[u] = c + u < n_tc ? get_shared(job.part + (first + c + u) * TR + r) : 0.0f;
+        for (uint32_t u = 0; u < 32; u++) v[u] = c + u < n_tc ? get_shared(job.part + (first + c + u) * TR + rr) : 0.0f;
 #pragma unroll
         for (uint32_t u = 0; u < 32; u++)
           if (c + u < n_tc) {
             sum += v[u];
-            put_shared(job.part + (first + c + u) * TR + r, 0.0f);
+            put_shared(job.part + (first + c + u) * TR + rr, 0.0f);
           }
       }
       store_y(job.y, row, sum, g.y_f32);
     }
-    if (lane == 0) __hip_atomic_store(job.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1173,7 +1177,10 @@ int cu_count() {
 
 // Batch-1 fused launch over `count` matrices with the same tile height.
 // Workgroups are shared out in proportion to each matrix's tiles, no more
-// than the chip holds at once, so every range runs in one pass.
+// than the chip holds at once, so every range runs in one pass.  A matrix's
+// ranges are whole row blocks when the largest such range is within 15% of
+// an even share of tiles or holds no more tiles than a workgroup has
+// wavefronts; otherwise they cut row blocks.
 template <int TR, int MAXW>
 nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y, uint8_t* const* ws, int count,
                        int y_f32, hipStream_t s) {
@@ -1195,13 +1202,12 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   // wavefronts per workgroup: the size with the most resident wavefronts
   // per CU (registers and LDS both count), the larger size on a tie
   const size_t per_wave = (static_cast<size_t>(kWave) * lane_words + buf_words) * 4;
-  const size_t group_sums = static_cast<size_t>(kMaxGroupTiles) * TR * 4;
   uint32_t nw = 0;
   int per_cu = 0;
   const uint32_t sizes[] = {16, 12, 8, 4, 2, 1};
   for (uint32_t n : sizes) {
     if (n > MAXW) continue;
-    const size_t l = n * per_wave;
+    const size_t l = n * per_wave + kGroupLds;
     if (l > kMaxLds) continue;
     if (set_lds(k_gemv<TR, MAXW>, l) != hipSuccess) return NWC_ERR_HIP;
     int k = 0;
@@ -1214,31 +1220,10 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   }
   if (nw == 0 || per_cu < 1) return NWC_ERR_UNSUPPORTED;
   const uint64_t cap = static_cast<uint64_t>(cu_count()) * per_cu;
-  // whole row blocks per workgroup when that needs no more tiles per
-  // wavefront than ranges over all resident wavefronts, fits at once, and
-  // the tile sums' LDS costs no residency
-  bool by_rows = nw * per_wave + group_sums <= kMaxLds;
-  if (by_rows) {
-    int k = 0;
-    if (set_lds(k_gemv<TR, MAXW>, nw * per_wave + group_sums) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&k, k_gemv<TR, MAXW>, nw * kWave, nw * per_wave + group_sums) !=
-            hipSuccess)
-      return NWC_ERR_HIP;
-    by_rows = k == per_cu;
-  }
-  if (by_rows) {
-    const uint64_t waves = std::min<uint64_t>(cap * nw, total);
-    const uint64_t range_max = (total + waves - 1) / waves;
-    uint64_t need = 0;
-    for (int j = 0; j < count; j++) {
-      const uint64_t n_tc = L[j].b.n_tc;
-      const uint64_t r = std::max<uint64_t>(1, nw / n_tc);
-      if (r * n_tc > kMaxGroupTiles || (r * n_tc + nw - 1) / nw > range_max) by_rows = false;
-      need += (L[j].b.n_tr + r - 1) / r;
-    }
-    if (need > cap) by_rows = false;
-  }
+  // the largest range whose offsets and tile sums fit the group's LDS
+  const uint64_t max_range = (kGroupLds / 4 - 4 - 4) / (TR + 1);
   uint32_t groups = 0;
+  uint64_t range = 1;
   for (int j = 0; j < count; j++) {
     GemvJob& job = g.job[j];
     job.b = L[j].b;
@@ -1246,24 +1231,28 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     job.y = y[j];
     job.count = reinterpret_cast<uint32_t*>(ws[j]);
     job.part = reinterpret_cast<float*>(ws[j] + (job.b.n_tr * 4 + 255) / 256 * 256);
-    const uint64_t T = job.b.n_tiles;
-    if (by_rows) {
-      job.rb_per_group = static_cast<uint32_t>(std::max<uint64_t>(1, nw / job.b.n_tc));
-      job.groups = static_cast<uint32_t>((job.b.n_tr + job.rb_per_group - 1) / job.rb_per_group);
-    } else {
-      const uint64_t share = 1 + (cap - count) * T / total;
-      job.rb_per_group = 0;
-      job.groups = static_cast<uint32_t>(std::min<uint64_t>((T + nw - 1) / nw, share));
-    }
+    const uint64_t T = job.b.n_tiles, n_tr = job.b.n_tr, n_tc = job.b.n_tc;
+    uint64_t G = std::min<uint64_t>(T, 1 + (cap - count) * T / total);
+    G = std::max<uint64_t>(G, (T + max_range - 1) / max_range);
+    // whole row blocks per range: k of them in every range but the last
+    const uint64_t k = (n_tr + G - 1) / G;
+    const bool whole = k * n_tc <= max_range &&
+                       (k * n_tc <= nw || static_cast<double>(k * n_tc) <= 1.15 * static_cast<double>(T) / G);
+    if (whole) G = (n_tr + k - 1) / k;
+    job.whole_rows = whole ? 1u : 0u;
+    job.groups = static_cast<uint32_t>(G);
+    range = std::max<uint64_t>(range, whole ? k * n_tc : (T + G - 1) / G);
     job.g0 = groups;
     groups += job.groups;
   }
-  const size_t lds = nw * per_wave + (by_rows ? group_sums : 0);
-  if (set_lds(k_gemv<TR, MAXW>, lds) != hipSuccess) return NWC_ERR_HIP;
   g.count = static_cast<uint32_t>(count);
   g.y_f32 = y_f32;
   g.lane_words = lane_words;
   g.buf_words = buf_words;
+  g.tw_words = static_cast<uint32_t>((range + 1 + 3) & ~3ull);
+  const size_t lds = nw * per_wave + (4 + g.tw_words + range * TR) * 4;
+  if (lds > nw * per_wave + kGroupLds) return NWC_ERR_UNSUPPORTED;
+  if (set_lds(k_gemv<TR, MAXW>, lds) != hipSuccess) return NWC_ERR_HIP;
   k_gemv<TR, MAXW><<<groups, nw * kWave, lds, s>>>(g);
   return launched();
 }
