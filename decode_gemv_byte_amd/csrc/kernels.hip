@@ -46,15 +46,12 @@
 namespace {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kWave = 64;
 constexpr int kMaxWaves = 16;      // wavefronts per workgroup, fused kernels
 constexpr int kGenericWaves = 4;   // wavefronts per workgroup, generic kernels
 constexpr int kTable = 4096;
 constexpr uint32_t kExpMask = 0x7F807F80u;  // exponent bits of two packed BF16
-constexpr int kMfmaRowPad = 512 + 8;        // bf16 per LDS row of a decoded tile
 
 struct BlobDev {
   const uint32_t* table;
@@ -482,6 +479,7 @@ struct GemvJob {
 };
 constexpr int kMaxJobs = 8;
 constexpr uint32_t kGroupLds = 8192;       // per-workgroup LDS: control words, offsets, tile sums
+constexpr uint32_t kSkinnyLds = 24576;     // per-workgroup LDS for the skinny mode's tile sums
 struct GemvGroup {
   GemvJob job[kMaxJobs];
   uint32_t count;
@@ -489,6 +487,9 @@ struct GemvGroup {
   uint32_t lane_words;  // stream words per lane in the interleaved slot (J, even)
   uint32_t buf_words;   // linear staging buffer per wavefront
   uint32_t tw_words;    // LDS words for a range's tile offsets (>= tiles + 1)
+  // skinny mode (one matrix): X rows of ldx elements, Y rows of ldy entries
+  uint64_t ldx, ldy;
+  uint32_t batch;
 };
 
 // Registers of one tile for the batch-1 kernel: raw bytes of this lane's
@@ -499,14 +500,15 @@ struct GemvGroup {
 // The tile's word offsets (tw0, tw1) come in from a vector load issued one
 // tile earlier: a scalar load would share its wait counter with the LDS
 // reads of the decode loop and stall it for a full memory round trip.
-template <int TR>
+template <int TR, int NX>
 struct TileRegs {
   uint2 raw[TR];
-  uint4 x;
+  uint4 x[NX > 0 ? NX : 1];  // X rows 0 .. NX - 1 at this lane's 8 columns
   // cbw: the dword holding this lane's chunk length (lanes 2k and 2k + 1
   // share one); the half is picked where it is used, so no instruction
   // touches the loaded value before the tile is waited for
   uint32_t cbw, w0, a0, nrows;
+  uint32_t col;  // column tile
   bool active;
   __device__ __forceinline__ uint32_t cb() const { return __builtin_amdgcn_ubfe(cbw, (lane_id() & 1) * 16, 16); }
   // A tile's loads come in two groups: what the first half of its rows needs
@@ -514,23 +516,30 @@ struct TileRegs {
   // (load_rest), issued last so that decoding can start before they land.
   // The stream goes first: its number of pieces varies, and with a fixed
   // number of loads behind it every wait on this tile has a known count.
-  __device__ __forceinline__ void load(const BlobDev& b, const uint16_t* xp, uint64_t ti, uint32_t tj,
-                                       uint32_t tw0, uint32_t tw1, uint32_t* buf) {
+  __device__ __forceinline__ void load(const BlobDev& b, const uint16_t* xp, uint64_t ldx, uint32_t nxr, uint64_t ti,
+                                       uint32_t tj, uint32_t tw0, uint32_t tw1, uint32_t* buf) {
     load_stream(b, tw0, tw1, buf);
-    load_planes(b, xp, ti, tj);
+    load_planes(b, xp, ldx, nxr, ti, tj);
   }
-  // chunk lengths, x and the raw bytes of rows [0, TR / 2): no dependence on
-  // the tile's word offsets
-  __device__ __forceinline__ void load_planes(const BlobDev& b, const uint16_t* xp, uint64_t ti, uint32_t tj) {
+  // chunk lengths, x (X rows below nxr; the others zero) and the raw bytes
+  // of rows [0, TR / 2): no dependence on the tile's word offsets
+  __device__ __forceinline__ void load_planes(const BlobDev& b, const uint16_t* xp, uint64_t ldx, uint32_t nxr,
+                                              uint64_t ti, uint32_t tj) {
     const uint32_t lane = lane_id();
     const uint64_t t = ti * b.n_tc + tj;
     const uint64_t row0 = ti * TR;
     nrows = static_cast<uint32_t>(umin64(TR, b.rows - row0));
     active = static_cast<uint64_t>(tj) * 512 + lane * 8 < b.cols;
+    col = tj;
     const uint64_t col0 = static_cast<uint64_t>(tj) * 512;
     cbw = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(b.chunk_bits + t * 64, 128), (lane & ~1u) * 2, 0, 0);
-    x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(xp + col0, (b.cols - col0) * 2),
-                                                                         lane * 16, 0, 0));
+#pragma unroll
+    for (int k = 0; k < NX; k++) {
+      x[k] = make_uint4(0, 0, 0, 0);
+      if (k == 0 || static_cast<uint32_t>(k) < nxr)
+        x[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             buf_rsrc(xp + k * ldx + col0, (b.cols - col0) * 2), lane * 16, 0, 0));
+    }
     load_raw<0, TR / 2>(b, ti, tj);
   }
   __device__ __forceinline__ void load_rest(const BlobDev& b, uint64_t ti, uint32_t tj) {
@@ -602,27 +611,78 @@ __device__ __forceinline__ uint32_t interleave(const uint32_t* buf, uint32_t w0,
 // slot, raw bytes and x in registers) into this lane's row sums over its 8
 // columns.  Rows past the matrix edge (last row block only; a wave-uniform
 // test) are not decoded and keep their zero sums.
-template <int TR, int R0, int R1>
-__device__ __forceinline__ void gemv_rows(const TileRegs<TR>& in, LaneBits& br, const uint32_t* tab,
-                                          float (&acc)[TR]) {
-  const uint4& xv = in.x;
+template <int TR, int NX, int R0, int R1>
+__device__ __forceinline__ void gemv_rows(const TileRegs<TR, NX>& in, LaneBits& br, const uint32_t* tab,
+                                          float (&acc)[TR * NX]) {
 #pragma unroll
   for (int r = R0; r < R1; r++) {
     if (static_cast<uint32_t>(r) < in.nrows) {
-      float a = 0.0f;
+      float a[NX];
+#pragma unroll
+      for (int k = 0; k < NX; k++) a[k] = 0.0f;
       // each product is pinned next to its decode step: left alone, the
       // compiler defers all of them to the end of the tile and keeps every
       // decoded pair live, which costs occupancy
-      a = dot2(assemble(decode_pair(br, tab), in.raw[r].x, false), xv.x, a);
-      asm volatile("" : "+v"(a));
-      a = dot2(assemble(decode_pair(br, tab), in.raw[r].x, true), xv.y, a);
-      asm volatile("" : "+v"(a));
-      a = dot2(assemble(decode_pair(br, tab), in.raw[r].y, false), xv.z, a);
-      asm volatile("" : "+v"(a));
-      a = dot2(assemble(decode_pair(br, tab), in.raw[r].y, true), xv.w, a);
-      asm volatile("" : "+v"(a));
-      acc[r] = a;
+      const uint32_t p0 = assemble(decode_pair(br, tab), in.raw[r].x, false);
+#pragma unroll
+      for (int k = 0; k < NX; k++) {
+        a[k] = dot2(p0, in.x[k].x, a[k]);
+        asm volatile("" : "+v"(a[k]));
+      }
+      const uint32_t p1 = assemble(decode_pair(br, tab), in.raw[r].x, true);
+#pragma unroll
+      for (int k = 0; k < NX; k++) {
+        a[k] = dot2(p1, in.x[k].y, a[k]);
+        asm volatile("" : "+v"(a[k]));
+      }
+      const uint32_t p2 = assemble(decode_pair(br, tab), in.raw[r].y, false);
+#pragma unroll
+      for (int k = 0; k < NX; k++) {
+        a[k] = dot2(p2, in.x[k].z, a[k]);
+        asm volatile("" : "+v"(a[k]));
+      }
+      const uint32_t p3 = assemble(decode_pair(br, tab), in.raw[r].y, true);
+#pragma unroll
+      for (int k = 0; k < NX; k++) {
+        a[k] = dot2(p3, in.x[k].w, a[k]);
+        asm volatile("" : "+v"(a[k]));
+      }
+#pragma unroll
+      for (int k = 0; k < NX; k++) acc[r * NX + k] = a[k];
     }
+  }
+}
+
+// Skinny mode: rows [R0, R1) of the tile decoded into registers, four BF16
+// pairs per row (rows past the matrix edge stay zero).
+template <int TR, int NX, int R0, int R1>
+__device__ __forceinline__ void decode_rows(const TileRegs<TR, NX>& in, LaneBits& br, const uint32_t* tab,
+                                            uint32_t (&wv)[TR][4]) {
+#pragma unroll
+  for (int r = R0; r < R1; r++) {
+    if (static_cast<uint32_t>(r) < in.nrows) {
+      wv[r][0] = assemble(decode_pair(br, tab), in.raw[r].x, false);
+      wv[r][1] = assemble(decode_pair(br, tab), in.raw[r].x, true);
+      wv[r][2] = assemble(decode_pair(br, tab), in.raw[r].y, false);
+      wv[r][3] = assemble(decode_pair(br, tab), in.raw[r].y, true);
+    }
+  }
+}
+
+// Skinny mode: this lane's 8 columns of X rows [g GB, g GB + GB) for column
+// tile tj (zero past the matrix edge and past the batch).
+template <int GB>
+__device__ __forceinline__ void load_xg(const BlobDev& b, const uint16_t* X, uint64_t ldx, uint32_t batch, uint32_t g,
+                                        uint32_t tj, uint4 (&xg)[GB]) {
+  const uint64_t col0 = static_cast<uint64_t>(tj) * 512;
+#pragma unroll
+  for (int k = 0; k < GB; k++) {
+    const uint32_t beta = g * GB + k;
+    xg[k] = make_uint4(0, 0, 0, 0);
+    if (beta < batch)
+      xg[k] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(X + beta * ldx + col0, (b.cols - col0) * 2),
+                                                       lane_id() * 16, 0, 0));
   }
 }
 
@@ -661,8 +721,15 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 // after one barrier the workgroup adds each row's sums in column order.  A
 // row block cut by a range edge has its tile sums added through the
 // workspace by whichever workgroup finishes it last.
-template <int TR, int MAXW>
+// NB: 1 for y = W x; 2 or 4 for Y = X W^T with up to NB X rows (TR NB <= 32),
+// their products formed as each pair is decoded; 0 for any batch 2..16, the tile
+// decoded into registers first and then multiplied by the X rows 32 / TR at
+// a time.  NB != 1 is the skinny mode: one matrix, ranges of whole row blocks.
+template <int TR, int MAXW, int NB>
 __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
+  constexpr bool SKINNY = NB != 1;
+  constexpr int NX = NB;  // X rows that come with each tile
+  constexpr int NA = NB > 0 ? NB : 1;  // sums per row of a tile formed while decoding
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const uint32_t nw = blockDim.x / kWave;
@@ -711,7 +778,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   // publishes all three, and wavefront 0 claims its first tile after it.
   // (when the first tiles cover the whole range, nothing is claimed)
   const bool claims = n_r > nw - 1;
-  TileRegs<TR> in;
+  TileRegs<TR, NX> in;
   uint64_t t = r1;
   if (wave == 0) {
     if (lane == 0) {
@@ -730,7 +797,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     const uint64_t ti = t / n_tc;
     const uint32_t tj = static_cast<uint32_t>(t - ti * n_tc);
     const uint32_t w0 = sload(b.tile_words, t), w1 = sload(b.tile_words, t + 1);
-    in.load(b, job.x, ti, tj, w0, w1, buf);
+    in.load(b, job.x, g.ldx, g.batch, ti, tj, w0, w1, buf);
     asm volatile("" ::: "memory");
     in.load_rest(b, ti, tj);
   }
@@ -744,52 +811,105 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       const uint32_t tj = static_cast<uint32_t>(t - ti * n_tc);
       const uint32_t w0 = __builtin_amdgcn_readfirstlane(tw[t - r0]);
       const uint32_t w1 = __builtin_amdgcn_readfirstlane(tw[t - r0 + 1]);
-      in.load(b, job.x, ti, tj, w0, w1, buf);
+      in.load(b, job.x, g.ldx, g.batch, ti, tj, w0, w1, buf);
       asm volatile("" ::: "memory");
       in.load_rest(b, ti, tj);
     }
   }
 
-  constexpr uint32_t lanes_per_row = kWave / TR;
-  const bool row_lane = (lane & (lanes_per_row - 1)) == 0;
-  const uint32_t r = lane / lanes_per_row;  // row of the reduced sum this lane holds
   while (t < r1) {
     wait_vmem_but<TR / 2>();
     wave_sync_lds();
     // this tile's stream into the slot; the linear buffer is then free for
     // the next tile
     const uint32_t q0 = interleave(buf, in.w0, in.a0, in.cb(), J, slot);
+    // skinny mode: the first batch rows' X, on its way while this tile decodes
+    constexpr int GB = 32 / TR;  // batch rows per group: TR GB sums reduce at once
+    uint4 xg[GB];
+    if constexpr (NB == 0) load_xg<GB>(b, job.x, g.ldx, g.batch, 0, in.col, xg);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the copy's reads are done
     wave_sync_lds();
-    float acc[TR];
+    float acc[TR * NA];
+    uint32_t wv[TR][4];
 #pragma unroll
-    for (int k = 0; k < TR; k++) acc[k] = 0.0f;
+    for (int k = 0; k < TR * NA; k++) acc[k] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < TR; k++) wv[k][0] = wv[k][1] = wv[k][2] = wv[k][3] = 0u;
     LaneBits br;
     br.init(slot, q0);
-    if (in.active) gemv_rows<TR, 0, TR / 2>(in, br, tab, acc);
+    if constexpr (NB == 0) {
+      if (in.active) decode_rows<TR, NX, 0, TR / 2>(in, br, tab, wv);
+    } else {
+      if (in.active) gemv_rows<TR, NX, 0, TR / 2>(in, br, tab, acc);
+    }
     // the second half's raw bytes, then the next tile's loads: they go out
     // halfway through this tile and nothing touches them before the next
     // iteration
     wait_vmem();
     asm volatile("" ::: "memory");
-    TileRegs<TR> nx;
+    TileRegs<TR, NX> nx;
     const uint64_t tn = claims ? claim() : r1;
     if (tn < r1) {
       const uint64_t ni = tn / n_tc;
       const uint32_t nj = static_cast<uint32_t>(tn - ni * n_tc);
       const uint32_t w0 = __builtin_amdgcn_readfirstlane(tw[tn - r0]);
       const uint32_t w1 = __builtin_amdgcn_readfirstlane(tw[tn - r0 + 1]);
-      nx.load(b, job.x, ni, nj, w0, w1, buf);
+      nx.load(b, job.x, g.ldx, g.batch, ni, nj, w0, w1, buf);
       asm volatile("" ::: "memory");
       nx.load_rest(b, ni, nj);
     }
-    if (in.active) gemv_rows<TR, TR / 2, TR>(in, br, tab, acc);
-    const float s = reduce_rows<TR>(acc);
-    if (row_lane) gsum[(t - r0) * TR + r] = s;
+    if constexpr (NB == 0) {
+      if (in.active) decode_rows<TR, NX, TR / 2, TR>(in, br, tab, wv);
+      // X rows in groups of GB: TR GB sums per lane, reduced over the
+      // wavefront at once; lanes 2v and 2v + 1 end with sum v (row v / GB,
+      // batch row g GB + v % GB)
+      const uint32_t v = lane / 2, vr = v / GB;
+      for (uint32_t gi2 = 0; gi2 * GB < g.batch; gi2++) {
+        if (gi2 > 0) load_xg<GB>(b, job.x, g.ldx, g.batch, gi2, in.col, xg);
+        float sums[TR * GB];
+#pragma unroll
+        for (int rr = 0; rr < TR; rr++)
+#pragma unroll
+          for (int k = 0; k < GB; k++) {
+            float a = dot2(wv[rr][0], xg[k].x, 0.0f);
+            a = dot2(wv[rr][1], xg[k].y, a);
+            a = dot2(wv[rr][2], xg[k].z, a);
+            sums[rr * GB + k] = dot2(wv[rr][3], xg[k].w, a);
+          }
+        const float sv = reduce_rows<TR * GB>(sums);
+        const uint32_t beta = gi2 * GB + v % GB;
+        if ((lane & 1u) == 0 && beta < g.batch) gsum[((t - r0) * TR + vr) * g.batch + beta] = sv;
+      }
+    } else {
+      if (in.active) gemv_rows<TR, NX, TR / 2, TR>(in, br, tab, acc);
+      // lanes (64 / (TR NB)) v .. hold sum v: row v / NB, X row v % NB
+      const float s = reduce_rows<TR * NA>(acc);
+      constexpr uint32_t lanes_per_sum = kWave / (TR * NA);
+      const uint32_t v = lane / lanes_per_sum;
+      if ((lane & (lanes_per_sum - 1)) == 0) gsum[(t - r0) * TR * NA + v] = s;
+    }
     in = nx;
     t = tn;
   }
   __syncthreads();
+
+  if constexpr (SKINNY) {
+    // whole row blocks only: every output adds its tile sums in column order
+    if (n_r == 0) return;
+    const uint64_t rb_a = r0 / n_tc;
+    const uint32_t nbs = NB > 0 ? NB : g.batch;  // sums per row of a tile in LDS
+    const uint32_t per_rb = TR * g.batch;
+    for (uint32_t k = threadIdx.x; k < n_r / n_tc * per_rb; k += blockDim.x) {
+      const uint64_t rb = rb_a + k / per_rb;
+      const uint32_t rr = (k % per_rb) / g.batch, beta = k % g.batch;
+      const uint64_t row = rb * TR + rr;
+      if (row >= b.rows) continue;
+      float sum = 0.0f;
+      for (uint64_t c = rb * n_tc; c < rb * n_tc + n_tc; c++) sum += gsum[((c - r0) * TR + rr) * nbs + beta];
+      store_y(job.y, beta * g.ldy + row, sum, g.y_f32);
+    }
+    return;
+  }
 
   // Row blocks [rb_a, rb_b] meet the range; a cut one (the first or the last)
   // leaves its tile sums in the workspace.
@@ -857,88 +977,6 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       }
       store_y(job.y, row, sum, g.y_f32);
     }
-  }
-}
-
-// Skinny decode-GEMM with MFMA, batch 2..16, TR = 8 or 16 (the 16-row MFMA
-// operand is padded with zero rows for TR = 8); one row block per work item,
-// its column tiles split across the workgroup's wavefronts.
-// LDS: table | per-wavefront D [waves][16][16] | stream buffers | decoded
-// tiles [waves][16][kMfmaRowPad].
-template <int TR>
-__global__ __launch_bounds__(kMaxWaves * kWave) void k_gemm_mfma(BlobDev b, const uint16_t* __restrict__ X,
-                                                                 uint64_t ldx, int batch, void* __restrict__ Y,
-                                                                 uint64_t ldy, int y_f32) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
-  float* red = reinterpret_cast<float*>(lds);
-  const uint32_t nwaves = blockDim.x / kWave;
-  const uint32_t wave = uniform(threadIdx.x / kWave);
-  const uint32_t lane = lane_id();
-  uint32_t* buf = lds + nwaves * 256 + wave * b.buf_words;
-  uint16_t* wt_lds = reinterpret_cast<uint16_t*>(lds + nwaves * 256 + nwaves * b.buf_words) +
-                     wave * static_cast<size_t>(16) * kMfmaRowPad;
-  load_table(tab, b.table);
-  __syncthreads();
-  const uint32_t mrow = lane % 16, kq = lane / 16;  // MFMA A: weight row, 8-column group
-  const uint32_t nb = lane % 16;                    // MFMA B: batch row
-  for (uint64_t ti = blockIdx.x; ti < b.n_tr; ti += gridDim.x) {
-    f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (uint32_t tj = wave; tj < b.n_tc; tj += nwaves) {
-      TileIn<TR> in;
-      in.load(b, ti, tj, buf);
-      uint4 xb[16];
-#pragma unroll
-      for (int kb = 0; kb < 16; kb++) {
-        const uint64_t gk = static_cast<uint64_t>(tj) * 512 + kb * 32 + kq * 8;
-        const bool ok = static_cast<int>(nb) < batch && gk < b.cols;
-        const uint4 v = *reinterpret_cast<const uint4*>(X + (ok ? nb * ldx + gk : 0));
-        xb[kb] = ok ? v : make_uint4(0, 0, 0, 0);
-      }
-      const uint32_t bit = in.start_bit();
-      wait_vmem();
-      wave_sync_lds();
-      Bits br;
-      if (in.active) br.init(buf, bit);
-#pragma unroll
-      for (int r = 0; r < TR; r++) {
-        uint4 o = make_uint4(0, 0, 0, 0);
-        if (in.active) {
-          o.x = assemble(br.pair(tab), in.raw[r].x, false);
-          o.y = assemble(br.pair(tab), in.raw[r].x, true);
-          o.z = assemble(br.pair(tab), in.raw[r].y, false);
-          o.w = assemble(br.pair(tab), in.raw[r].y, true);
-        }
-        // columns past the edge must be exact zeros (they meet zero X in the
-        // contraction); rows past the edge only reach rows that are not stored
-        *reinterpret_cast<uint4*>(wt_lds + r * kMfmaRowPad + lane * 8) = o;
-      }
-#pragma unroll
-      for (int r = TR; r < 16; r++)  // padding rows of the 16-row operand
-        *reinterpret_cast<uint4*>(wt_lds + r * kMfmaRowPad + lane * 8) = make_uint4(0, 0, 0, 0);
-      wave_sync_lds();
-#pragma unroll
-      for (int kb = 0; kb < 16; kb++) {
-        const uint4 av = *reinterpret_cast<const uint4*>(wt_lds + mrow * kMfmaRowPad + kb * 32 + kq * 8);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                    __builtin_bit_cast(bf16x8_t, xb[kb]), d, 0, 0, 0);
-      }
-      wave_sync_lds();
-    }
-    // lane holds D[4 * (lane / 16) + i][lane % 16]: rows x batch
-#pragma unroll
-    for (int i = 0; i < 4; i++) red[wave * 256 + (4 * (lane / 16) + i) * 16 + nb] = d[i];
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) {
-      const uint32_t r = i / 16, beta = i % 16;
-      const uint64_t row = ti * TR + r;
-      if (static_cast<int>(beta) < batch && r < TR && row < b.rows) {
-        float sum = 0.0f;
-        for (uint32_t w = 0; w < nwaves; w++) sum += red[w * 256 + i];
-        store_y(Y, beta * ldy + row, sum, y_f32);
-      }
-    }
-    __syncthreads();
   }
 }
 
@@ -1176,72 +1214,152 @@ int cu_count() {
 }
 
 // Batch-1 fused launch over `count` matrices with the same tile height.
+// Split of a launch's tiles into workgroup ranges: the ranges' sizes and the
+// LDS they need besides the wavefronts' buffers.
+struct GemvPlan {
+  uint32_t groups[kMaxJobs];
+  uint32_t whole_rows[kMaxJobs];
+  uint32_t total_groups;
+  uint64_t range;  // tiles in the largest range
+  uint32_t tw_words() const { return static_cast<uint32_t>((range + 1 + 3) & ~3ull); }
+  // sums per tile: TR (batch 1) or TR x batch (skinny mode)
+  size_t group_lds(uint32_t sums_per_tile) const { return (4 + tw_words() + range * sums_per_tile) * 4; }
+};
+
 // Workgroups are shared out in proportion to each matrix's tiles, no more
-// than the chip holds at once, so every range runs in one pass.  A matrix's
-// ranges are whole row blocks when the largest such range is within 15% of
-// an even share of tiles or holds no more tiles than a workgroup has
-// wavefronts; otherwise they cut row blocks.
-template <int TR, int MAXW>
-nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y, uint8_t* const* ws, int count,
-                       int y_f32, hipStream_t s) {
-  GemvGroup g;
-  std::memset(&g, 0, sizeof(g));
-  uint32_t lane_words = 0, buf_words = 0;
+// than `cap` (what the chip holds at once), so every range runs in one pass.
+// A matrix's ranges are whole row blocks when the largest such range is
+// within 15% of an even share of tiles or holds no more tiles than a
+// workgroup has wavefronts; otherwise they cut row blocks.
+template <int TR>
+GemvPlan plan_gemv(const Launch* L, int count, uint64_t cap, uint32_t nw) {
+  GemvPlan p;
+  std::memset(&p, 0, sizeof(p));
   uint64_t total = 0;
-  for (int j = 0; j < count; j++) {
-    // a lane's words start with the one holding bit (chunk start - 2), so
-    // the reader starts at bit <= 31 and its last window (at most chunk
-    // bits - 1 further) reads one word of look-ahead; rounded up to even
-    lane_words = std::max(lane_words, (((30 + L[j].max_chunk_bits) >> 5) + 2 + 1) & ~1u);
-    buf_words = std::max(buf_words, L[j].b.buf_words);
-    total += L[j].b.n_tiles;
-  }
-  // the interleaving copy reads up to lane_words past the last chunk start;
-  // whole 256-byte units keep every slot 256-byte aligned
-  buf_words = (buf_words + lane_words + 63) & ~63u;
-  // wavefronts per workgroup: the size with the most resident wavefronts
-  // per CU (registers and LDS both count), the larger size on a tie
-  const size_t per_wave = (static_cast<size_t>(kWave) * lane_words + buf_words) * 4;
-  uint32_t nw = 0;
-  int per_cu = 0;
-  const uint32_t sizes[] = {16, 12, 8, 4, 2, 1};
-  for (uint32_t n : sizes) {
-    if (n > MAXW) continue;
-    const size_t l = n * per_wave + kGroupLds;
-    if (l > kMaxLds) continue;
-    if (set_lds(k_gemv<TR, MAXW>, l) != hipSuccess) return NWC_ERR_HIP;
-    int k = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&k, k_gemv<TR, MAXW>, n * kWave, l) != hipSuccess)
-      return NWC_ERR_HIP;
-    if (static_cast<uint64_t>(k) * n > static_cast<uint64_t>(per_cu) * nw) {
-      nw = n;
-      per_cu = k;
-    }
-  }
-  if (nw == 0 || per_cu < 1) return NWC_ERR_UNSUPPORTED;
-  const uint64_t cap = static_cast<uint64_t>(cu_count()) * per_cu;
+  for (int j = 0; j < count; j++) total += L[j].b.n_tiles;
   // the largest range whose offsets and tile sums fit the group's LDS
   const uint64_t max_range = (kGroupLds / 4 - 4 - 4) / (TR + 1);
-  uint32_t groups = 0;
-  uint64_t range = 1;
+  p.range = 1;
   for (int j = 0; j < count; j++) {
-    GemvJob& job = g.job[j];
-    job.b = L[j].b;
-    job.x = x[j];
-    job.y = y[j];
-    job.count = reinterpret_cast<uint32_t*>(ws[j]);
-    job.part = reinterpret_cast<float*>(ws[j] + (job.b.n_tr * 4 + 255) / 256 * 256);
-    const uint64_t T = job.b.n_tiles, n_tr = job.b.n_tr, n_tc = job.b.n_tc;
-    uint64_t G = std::min<uint64_t>(T, 1 + (cap - count) * T / total);
+    const uint64_t T = L[j].b.n_tiles, n_tr = L[j].b.n_tr, n_tc = L[j].b.n_tc;
+    uint64_t G = std::min<uint64_t>(T, 1 + (cap > static_cast<uint64_t>(count) ? cap - count : 0) * T / total);
     G = std::max<uint64_t>(G, (T + max_range - 1) / max_range);
     // whole row blocks per range: k of them in every range but the last
     const uint64_t k = (n_tr + G - 1) / G;
     const bool whole = k * n_tc <= max_range &&
                        (k * n_tc <= nw || static_cast<double>(k * n_tc) <= 1.15 * static_cast<double>(T) / G);
     if (whole) G = (n_tr + k - 1) / k;
-    job.whole_rows = whole ? 1u : 0u;
-    job.groups = static_cast<uint32_t>(G);
-    range = std::max<uint64_t>(range, whole ? k * n_tc : (T + G - 1) / G);
+    p.whole_rows[j] = whole ? 1u : 0u;
+    p.groups[j] = static_cast<uint32_t>(G);
+    p.range = std::max<uint64_t>(p.range, whole ? k * n_tc : (T + G - 1) / G);
+    p.total_groups += p.groups[j];
+  }
+  return p;
+}
+
+// Sums the skinny mode keeps per row of a tile: the batch, except that with
+// 8-row tiles a batch of 3 runs as 4 (the cross-lane sum needs a power of two).
+uint32_t skinny_sums_per_row(int tr, int batch) { return tr == 8 && batch == 3 ? 4u : static_cast<uint32_t>(batch); }
+
+// Row blocks of one matrix per skinny-mode range: as many as keep one range
+// per resident workgroup, no more than fit kSkinnyLds (0: not even one).
+uint64_t skinny_rows_per_range(uint64_t n_tr, uint64_t n_tc, int tr, int batch, uint64_t cap) {
+  const uint64_t fit = kSkinnyLds / (n_tc * tr * skinny_sums_per_row(tr, batch) * 4);
+  if (fit == 0) return 0;
+  return std::max<uint64_t>(1, std::min<uint64_t>(fit, (n_tr + cap - 1) / cap));
+}
+
+template <int TR>
+GemvPlan plan_skinny(const Launch& L, int batch, uint64_t cap) {
+  GemvPlan p;
+  std::memset(&p, 0, sizeof(p));
+  const uint64_t k = skinny_rows_per_range(L.b.n_tr, L.b.n_tc, TR, batch, cap);
+  p.whole_rows[0] = 1;
+  p.groups[0] = static_cast<uint32_t>((L.b.n_tr + k - 1) / k);
+  p.total_groups = p.groups[0];
+  p.range = k * L.b.n_tc;
+  return p;
+}
+
+// The batch-1 launch (count matrices) or the skinny one (one matrix, batch
+// 2..16): wavefronts per workgroup are the size with the most resident
+// wavefronts per CU (registers and LDS both count, the ranges' LDS
+// included), the larger size on a tie.
+template <int TR, int MAXW, int NB>
+nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y, uint8_t* const* ws, int count,
+                       int y_f32, hipStream_t s, int batch = 1, uint64_t ldx = 0, uint64_t ldy = 0) {
+  GemvGroup g;
+  std::memset(&g, 0, sizeof(g));
+  uint32_t lane_words = 0, buf_words = 0;
+  for (int j = 0; j < count; j++) {
+    // a lane's words start with the one holding bit (chunk start - 2), so
+    // the reader starts at bit <= 31 and its last window (at most chunk
+    // bits - 1 further) reads one word of look-ahead; rounded up to even
+    lane_words = std::max(lane_words, (((30 + L[j].max_chunk_bits) >> 5) + 2 + 1) & ~1u);
+    buf_words = std::max(buf_words, L[j].b.buf_words);
+  }
+  // the interleaving copy reads up to lane_words past the last chunk start;
+  // whole 256-byte units keep every slot 256-byte aligned
+  buf_words = (buf_words + lane_words + 63) & ~63u;
+  const size_t per_wave = (static_cast<size_t>(kWave) * lane_words + buf_words) * 4;
+  constexpr bool SKINNY = NB != 1;
+  const uint32_t sums = NB == 0 ? TR * batch : TR * NB;
+  const uint32_t cus = static_cast<uint32_t>(cu_count());
+  auto occupancy = [&](uint32_t n, size_t lds, int* k) {
+    if (lds > kMaxLds) {
+      *k = 0;
+      return hipSuccess;
+    }
+    hipError_t e = set_lds(k_gemv<TR, MAXW, NB>, lds);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(k, k_gemv<TR, MAXW, NB>, n * kWave, lds);
+    return e;
+  };
+  auto plan = [&](uint64_t cap, uint32_t n) {
+    if constexpr (SKINNY)
+      return plan_skinny<TR>(L[0], batch, cap);
+    else
+      return plan_gemv<TR>(L, count, cap, n);
+  };
+  uint32_t nw = 0;
+  int per_cu = 0;
+  GemvPlan best;
+  std::memset(&best, 0, sizeof(best));
+  const uint32_t sizes[] = {16, 12, 8, 4, 2, 1};
+  for (uint32_t n : sizes) {
+    if (n > MAXW) continue;
+    int k = 0;
+    if (occupancy(n, n * per_wave, &k) != hipSuccess) return NWC_ERR_HIP;
+    if (k < 1) continue;
+    // the ranges' LDS may cost residency: plan again with what is left
+    GemvPlan p = plan(static_cast<uint64_t>(cus) * k, n);
+    int k2 = 0;
+    if (occupancy(n, n * per_wave + p.group_lds(sums), &k2) != hipSuccess) return NWC_ERR_HIP;
+    if (k2 < k) {
+      if (k2 < 1) continue;
+      k = k2;
+      p = plan(static_cast<uint64_t>(cus) * k, n);
+      if (occupancy(n, n * per_wave + p.group_lds(sums), &k2) != hipSuccess) return NWC_ERR_HIP;
+      if (k2 < k) continue;
+    }
+    if (static_cast<uint64_t>(k) * n > static_cast<uint64_t>(per_cu) * nw) {
+      nw = n;
+      per_cu = k;
+      best = p;
+    }
+  }
+  if (nw == 0 || per_cu < 1) return NWC_ERR_UNSUPPORTED;
+  uint32_t groups = 0;
+  for (int j = 0; j < count; j++) {
+    GemvJob& job = g.job[j];
+    job.b = L[j].b;
+    job.x = x[j];
+    job.y = y[j];
+    if (!SKINNY) {
+      job.count = reinterpret_cast<uint32_t*>(ws[j]);
+      job.part = reinterpret_cast<float*>(ws[j] + (job.b.n_tr * 4 + 255) / 256 * 256);
+    }
+    job.whole_rows = best.whole_rows[j];
+    job.groups = best.groups[j];
     job.g0 = groups;
     groups += job.groups;
   }
@@ -1249,12 +1367,23 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   g.y_f32 = y_f32;
   g.lane_words = lane_words;
   g.buf_words = buf_words;
-  g.tw_words = static_cast<uint32_t>((range + 1 + 3) & ~3ull);
-  const size_t lds = nw * per_wave + (4 + g.tw_words + range * TR) * 4;
-  if (lds > nw * per_wave + kGroupLds) return NWC_ERR_UNSUPPORTED;
-  if (set_lds(k_gemv<TR, MAXW>, lds) != hipSuccess) return NWC_ERR_HIP;
-  k_gemv<TR, MAXW><<<groups, nw * kWave, lds, s>>>(g);
+  g.tw_words = best.tw_words();
+  g.ldx = ldx;
+  g.ldy = ldy;
+  g.batch = static_cast<uint32_t>(batch);
+  const size_t lds = nw * per_wave + best.group_lds(sums);
+  if (set_lds(k_gemv<TR, MAXW, NB>, lds) != hipSuccess) return NWC_ERR_HIP;
+  k_gemv<TR, MAXW, NB><<<groups, nw * kWave, lds, s>>>(g);
   return launched();
+}
+
+// Whether a blob and batch take the skinny mode of the fused kernel (no
+// workspace): default chunk geometry, 8- or 16-row tiles, and one row
+// block's tile sums within kSkinnyLds.
+bool skinny_fits(const nwc::Geometry& g, int batch) {
+  const bool fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16) && g.cols % 8 == 0;
+  return fast && batch >= 2 && batch <= 16 &&
+         static_cast<uint64_t>(g.n_tc) * g.tr * skinny_sums_per_row(static_cast<int>(g.tr), batch) * 4 <= kSkinnyLds;
 }
 
 size_t generic_ws_bytes(const nwc::Geometry& g, int batch) {
@@ -1297,7 +1426,7 @@ nwc_status nwc_workspace_size(const nwc_info* info, int batch, size_t* bytes) {
   const bool fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
   if (fast && batch == 1)
     *bytes = fused_ws_bytes(g);
-  else if (fast && (g.tr == 8 || g.tr == 16))
+  else if (skinny_fits(g, batch))
     *bytes = 0;
   else
     *bytes = generic_ws_bytes(g, batch);
@@ -1363,25 +1492,27 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
     void* yy = Y;
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     switch (L.b.tr) {
-      case 8: return launch_gemv<8, 16>(&L, &X, &yy, &w8, 1, y_f32, s);
-      case 16: return launch_gemv<16, 8>(&L, &X, &yy, &w8, 1, y_f32, s);
-      default: return launch_gemv<32, 4>(&L, &X, &yy, &w8, 1, y_f32, s);
+      case 8: return launch_gemv<8, 16, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
+      case 16: return launch_gemv<16, 8, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
+      default: return launch_gemv<32, 4, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
     }
   }
   if (need == 0) {
-    const uint32_t nw = std::min<uint32_t>(L.b.n_tc, 4);
-    const size_t lds = (nw * 256 + static_cast<size_t>(nw) * L.b.buf_words) * 4 +
-                       static_cast<size_t>(nw) * 16 * kMfmaRowPad * 2;
-    if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
-    const unsigned grid = static_cast<unsigned>(std::min<uint64_t>(L.b.n_tr, kCUs * 2));
+    // skinny mode of the fused kernel (nwc_workspace_size said so)
+    const uint16_t* XX = X;
+    void* yy = Y;
+    // up to 32 / TR X rows are multiplied as each pair is decoded; more go
+    // through the tile decoded into registers
     if (L.b.tr == 8) {
-      if (set_lds(k_gemm_mfma<8>, lds) != hipSuccess) return NWC_ERR_HIP;
-      k_gemm_mfma<8><<<grid, nw * kWave, lds, s>>>(L.b, X, ldx, batch, Y, ldy, y_f32);
-    } else {
-      if (set_lds(k_gemm_mfma<16>, lds) != hipSuccess) return NWC_ERR_HIP;
-      k_gemm_mfma<16><<<grid, nw * kWave, lds, s>>>(L.b, X, ldx, batch, Y, ldy, y_f32);
+      switch (batch) {
+        case 2: return launch_gemv<8, 16, 2>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+        case 3:  // a power-of-two count of sums per lane: X row 3 is zero
+        case 4: return launch_gemv<8, 16, 4>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+        default: return launch_gemv<8, 16, 0>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+      }
     }
-    return launched();
+    if (batch == 2) return launch_gemv<16, 8, 2>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+    return launch_gemv<16, 8, 0>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
   }
   // generic path: partial sums per column tile, then a reduction
   const size_t lds = (static_cast<size_t>(kGenericWaves) * L.b.buf_words) * 4 +
@@ -1429,9 +1560,9 @@ nwc_status nwc_gemv_batched(int count, const nwc_info* infos, const void* const*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int y_f32 = y_type == NWC_OUT_F32 ? 1 : 0;
   switch (L[0].b.tr) {
-    case 8: return launch_gemv<8, 16>(L, x_dev, y_dev, w8, count, y_f32, s);
-    case 16: return launch_gemv<16, 8>(L, x_dev, y_dev, w8, count, y_f32, s);
-    default: return launch_gemv<32, 4>(L, x_dev, y_dev, w8, count, y_f32, s);
+    case 8: return launch_gemv<8, 16, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
+    case 16: return launch_gemv<16, 8, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
+    default: return launch_gemv<32, 4, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
   }
 }
 
