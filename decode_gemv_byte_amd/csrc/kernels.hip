@@ -478,7 +478,7 @@ struct GemvJob {
   uint32_t whole_rows;  // 1: each range is whole row blocks; 0: ranges cut anywhere
 };
 constexpr int kMaxJobs = 8;
-constexpr uint32_t kGroupLds = 8192;       // per-workgroup LDS: control words, offsets, tile sums
+constexpr uint32_t kGroupLds = 8192;       // least per-workgroup LDS for control words, offsets, tile sums
 constexpr uint32_t kSkinnyLds = 24576;     // per-workgroup LDS for the skinny mode's tile sums
 struct GemvGroup {
   GemvJob job[kMaxJobs];
@@ -1232,13 +1232,13 @@ struct GemvPlan {
 // within 15% of an even share of tiles or holds no more tiles than a
 // workgroup has wavefronts; otherwise they cut row blocks.
 template <int TR>
-GemvPlan plan_gemv(const Launch* L, int count, uint64_t cap, uint32_t nw) {
+GemvPlan plan_gemv(const Launch* L, int count, uint64_t cap, uint32_t nw, size_t group_lds) {
   GemvPlan p;
   std::memset(&p, 0, sizeof(p));
   uint64_t total = 0;
   for (int j = 0; j < count; j++) total += L[j].b.n_tiles;
   // the largest range whose offsets and tile sums fit the group's LDS
-  const uint64_t max_range = (kGroupLds / 4 - 4 - 4) / (TR + 1);
+  const uint64_t max_range = std::max<uint64_t>(1, (group_lds / 4 - 4 - 4) / (TR + 1));
   p.range = 1;
   for (int j = 0; j < count; j++) {
     const uint64_t T = L[j].b.n_tiles, n_tr = L[j].b.n_tr, n_tc = L[j].b.n_tc;
@@ -1314,11 +1314,18 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(k, k_gemv<TR, MAXW, NB>, n * kWave, lds);
     return e;
   };
-  auto plan = [&](uint64_t cap, uint32_t n) {
+  // the LDS a workgroup has for its ranges' sums when k workgroups of n
+  // wavefronts share a CU (the decode table is static LDS)
+  auto group_budget = [&](uint32_t n, int k) -> size_t {
+    const size_t per_group = (kMaxLds + kTable * 4) / static_cast<size_t>(k);  // all of a CU's LDS, shared
+    const size_t used = kTable * 4 + n * per_wave + 1024;  // table, wavefront buffers, allocation slack
+    return per_group > used + 1024 ? per_group - used : 1024;
+  };
+  auto plan = [&](uint64_t cap, uint32_t n, int k) {
     if constexpr (SKINNY)
       return plan_skinny<TR>(L[0], batch, cap);
     else
-      return plan_gemv<TR>(L, count, cap, n);
+      return plan_gemv<TR>(L, count, cap, n, std::max<size_t>(kGroupLds, group_budget(n, k)));
   };
   uint32_t nw = 0;
   int per_cu = 0;
@@ -1331,13 +1338,13 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     if (occupancy(n, n * per_wave, &k) != hipSuccess) return NWC_ERR_HIP;
     if (k < 1) continue;
     // the ranges' LDS may cost residency: plan again with what is left
-    GemvPlan p = plan(static_cast<uint64_t>(cus) * k, n);
+    GemvPlan p = plan(static_cast<uint64_t>(cus) * k, n, k);
     int k2 = 0;
     if (occupancy(n, n * per_wave + p.group_lds(sums), &k2) != hipSuccess) return NWC_ERR_HIP;
     if (k2 < k) {
       if (k2 < 1) continue;
       k = k2;
-      p = plan(static_cast<uint64_t>(cus) * k, n);
+      p = plan(static_cast<uint64_t>(cus) * k, n, k);
       if (occupancy(n, n * per_wave + p.group_lds(sums), &k2) != hipSuccess) return NWC_ERR_HIP;
       if (k2 < k) continue;
     }
