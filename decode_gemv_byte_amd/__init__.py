@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional
+from typing import Optional, Sequence
 
 import numpy as np
 
@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnwc.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libnwc.so is not built; run `python -m decode_gemv_byte_amd.build` "
+    raise ImportError("libnwc.so is not built; run `python decode_gemv_byte_amd/build.py` "
                       "(or __graft_entry__.build())")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -79,14 +79,16 @@ _lib.nwc_bf16_workspace_size.argtypes = [_u64, _u64, ctypes.POINTER(_sz)]
 _lib.nwc_gemv_bf16.argtypes = [_vp, _u64, _u64, _u64, _vp, _vp, _i, _vp, _sz, _vp]
 _lib.nwc_gemv_batched.argtypes = [_i, ctypes.POINTER(nwc_info), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                   ctypes.POINTER(_vp), _i, _vp, _sz, _vp]
+_lib.nwc_decode_batched.argtypes = [_i, ctypes.POINTER(nwc_info), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                    ctypes.POINTER(_u64), _vp]
 for _f in ("nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode", "nwc_workspace_size", "nwc_gemv",
-           "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched"):
+           "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched", "nwc_decode_batched"):
     getattr(_lib, _f).restype = _st
 
 # the exported C symbols, for checks against include/nwc.h
 EXPORTS = ("nwc_status_str", "nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode",
            "nwc_workspace_size", "nwc_gemv", "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16",
-           "nwc_gemv_batched")
+           "nwc_gemv_batched", "nwc_decode_batched")
 
 
 def _check(st: int, where: str):
@@ -191,6 +193,28 @@ def nwc_decode(info: nwc_info, blob_dev, w_dev, ld: Optional[int] = None, stream
     if ld is None:
         ld = int(w_dev.shape[-1])
     _check(_lib.nwc_decode(ctypes.byref(info), _dptr(blob_dev), _dptr(w_dev), ld, _stream(stream)), "nwc_decode")
+
+
+class DecodeBatch:
+    """Marshalled arguments of one nwc_decode_batched call (blobs i written to
+    w_devs[i], row stride = its last dimension), built once and reusable."""
+
+    def __init__(self, infos: Sequence[nwc_info], blobs_dev, w_devs):
+        n = len(infos)
+        if not (n == len(blobs_dev) == len(w_devs)) or n < 1:
+            raise ValueError("need equal, non-empty lists")
+        self.count = n
+        self.infos = (nwc_info * n)(*infos)
+        self.blobs = (_vp * n)(*[_dptr(t).value for t in blobs_dev])
+        self.outs = (_vp * n)(*[_dptr(t).value for t in w_devs])
+        self.ld = (_u64 * n)(*[int(t.shape[-1]) for t in w_devs])
+        self._keep = (list(blobs_dev), list(w_devs))
+
+
+def nwc_decode_batched(batch: DecodeBatch, stream=None):
+    """Several independent decodes in one launch."""
+    _check(_lib.nwc_decode_batched(batch.count, batch.infos, batch.blobs, batch.outs, batch.ld, _stream(stream)),
+           "nwc_decode_batched")
 
 
 def _ws(ws):

@@ -1,6 +1,8 @@
 """Build libnwc.so (host codec + gfx950 HIP kernels) in-tree with hipcc.
 
-    python -m decode_gemv_byte_amd.build
+    python decode_gemv_byte_amd/build.py
+
+(run as a script: importing the package would load the library first).
 
 Every HIP source is compiled for gfx950 only, with packed-FP32 instruction
 selection disabled.

@@ -370,44 +370,6 @@ struct TileIn {
 
 // ------------------------------------------------------------------ decode
 
-// Fast path (S = 64 chunks of 8 columns, K % 8 == 0): wavefronts take tiles
-// in a grid-stride loop and write 16 bytes per lane per row.
-template <int TR>
-__global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_fast(BlobDev b, uint16_t* __restrict__ out,
-                                                                       uint64_t ld) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
-  const uint32_t wave = uniform(threadIdx.x / kWave);
-  uint32_t* buf = lds + wave * b.buf_words;
-  load_table(tab, b.table);
-  __syncthreads();
-  const uint64_t nwaves = static_cast<uint64_t>(gridDim.x) * (blockDim.x / kWave);
-  for (uint64_t t = static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + wave; t < b.n_tiles; t += nwaves) {
-    const uint64_t ti = t / b.n_tc;
-    const uint32_t tj = static_cast<uint32_t>(t % b.n_tc);
-    TileIn<TR> in;
-    in.load(b, ti, tj, buf);
-    const uint32_t bit = in.start_bit();
-    wait_vmem();
-    wave_sync_lds();
-    if (in.active) {
-      Bits br;
-      br.init(buf, bit);
-      const uint64_t row0 = ti * TR;
-#pragma unroll
-      for (int r = 0; r < TR; r++) {
-        uint4 o;
-        o.x = assemble(br.pair(tab), in.raw[r].x, false);
-        o.y = assemble(br.pair(tab), in.raw[r].x, true);
-        o.z = assemble(br.pair(tab), in.raw[r].y, false);
-        o.w = assemble(br.pair(tab), in.raw[r].y, true);
-        if (static_cast<uint32_t>(r) < in.nrows) *reinterpret_cast<uint4*>(out + (row0 + r) * ld + in.c0) = o;
-      }
-    }
-    wave_sync_lds();
-  }
-}
-
 // Generic path: any geometry, one symbol at a time, scalar stores.
 __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDev b, uint16_t* __restrict__ out,
                                                                           uint64_t ld) {
@@ -476,6 +438,7 @@ struct GemvJob {
   uint32_t g0;          // first workgroup of this matrix
   uint32_t groups;      // workgroups of this matrix
   uint32_t whole_rows;  // 1: each range is whole row blocks; 0: ranges cut anywhere
+  uint64_t ld;          // decode mode: row stride of W' in elements
 };
 constexpr int kMaxJobs = 8;
 constexpr uint32_t kGroupLds = 8192;       // least per-workgroup LDS for control words, offsets, tile sums
@@ -508,7 +471,8 @@ struct TileRegs {
   // share one); the half is picked where it is used, so no instruction
   // touches the loaded value before the tile is waited for
   uint32_t cbw, w0, a0, nrows;
-  uint32_t col;  // column tile
+  uint32_t col;     // column tile
+  uint32_t rowblk;  // row block
   bool active;
   __device__ __forceinline__ uint32_t cb() const { return __builtin_amdgcn_ubfe(cbw, (lane_id() & 1) * 16, 16); }
   // A tile's loads come in two groups: what the first half of its rows needs
@@ -531,6 +495,7 @@ struct TileRegs {
     nrows = static_cast<uint32_t>(umin64(TR, b.rows - row0));
     active = static_cast<uint64_t>(tj) * 512 + lane * 8 < b.cols;
     col = tj;
+    rowblk = static_cast<uint32_t>(ti);
     const uint64_t col0 = static_cast<uint64_t>(tj) * 512;
     cbw = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(b.chunk_bits + t * 64, 128), (lane & ~1u) * 2, 0, 0);
 #pragma unroll
@@ -724,11 +689,14 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 // NB: 1 for y = W x; 2 or 4 for Y = X W^T with up to NB X rows (TR NB <= 32),
 // their products formed as each pair is decoded; 0 for any batch 2..16, the tile
 // decoded into registers first and then multiplied by the X rows 32 / TR at
-// a time.  NB != 1 is the skinny mode: one matrix, ranges of whole row blocks.
+// a time (NB 0, 2, 4: the skinny mode, one matrix, ranges of whole row
+// blocks); -1 for the standalone decode, which writes each decoded tile to
+// W' (job.y, rows of g.ldy elements) once the next tile's data is in.
 template <int TR, int MAXW, int NB>
 __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
-  constexpr bool SKINNY = NB != 1;
-  constexpr int NX = NB;  // X rows that come with each tile
+  constexpr bool DECODE = NB < 0;
+  constexpr bool SKINNY = NB == 0 || NB > 1;
+  constexpr int NX = NB > 0 ? NB : 0;  // X rows that come with each tile
   constexpr int NA = NB > 0 ? NB : 1;  // sums per row of a tile formed while decoding
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
@@ -817,8 +785,31 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     }
   }
 
+  // decode mode: the tile decoded last, stored right after the next tile's
+  // data is in, as exactly TR stores (rows past the matrix edge write row 0
+  // again, the same bytes), so that the wait halfway through the tile can
+  // leave just those stores outstanding: memory operations of a wavefront
+  // complete in the order they were issued
+  uint32_t pv[TR][4];
+  uint32_t p_row = 0, p_col = 0, p_nrows = 0;
+  bool p_active = false;
+  auto store_prev = [&]() __attribute__((always_inline)) {
+    if (p_nrows == 0) return;
+    uint16_t* out = static_cast<uint16_t*>(job.y);
+#pragma unroll
+    for (int rr = 0; rr < TR; rr++) {
+      const bool in_matrix = static_cast<uint32_t>(rr) < p_nrows;
+      const uint32_t row = in_matrix ? rr : 0;
+      const uint4 v = in_matrix ? make_uint4(pv[rr][0], pv[rr][1], pv[rr][2], pv[rr][3])
+                                : make_uint4(pv[0][0], pv[0][1], pv[0][2], pv[0][3]);
+      if (p_active)
+        *reinterpret_cast<uint4*>(out + (static_cast<uint64_t>(p_row) * TR + row) * job.ld +
+                                  static_cast<uint64_t>(p_col) * 512 + lane * 8) = v;
+    }
+  };
   while (t < r1) {
     wait_vmem_but<TR / 2>();
+    if constexpr (DECODE) store_prev();
     wave_sync_lds();
     // this tile's stream into the slot; the linear buffer is then free for
     // the next tile
@@ -837,15 +828,18 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     for (int k = 0; k < TR; k++) wv[k][0] = wv[k][1] = wv[k][2] = wv[k][3] = 0u;
     LaneBits br;
     br.init(slot, q0);
-    if constexpr (NB == 0) {
+    if constexpr (NB <= 0) {
       if (in.active) decode_rows<TR, NX, 0, TR / 2>(in, br, tab, wv);
     } else {
       if (in.active) gemv_rows<TR, NX, 0, TR / 2>(in, br, tab, acc);
     }
     // the second half's raw bytes, then the next tile's loads: they go out
     // halfway through this tile and nothing touches them before the next
-    // iteration
-    wait_vmem();
+    // iteration (decode mode: the previous tile's TR stores may stay in flight)
+    if (DECODE && p_nrows > 0)
+      wait_vmem_but<TR>();
+    else
+      wait_vmem();
     asm volatile("" ::: "memory");
     TileRegs<TR, NX> nx;
     const uint64_t tn = claims ? claim() : r1;
@@ -858,7 +852,17 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       asm volatile("" ::: "memory");
       nx.load_rest(b, ni, nj);
     }
-    if constexpr (NB == 0) {
+    if constexpr (DECODE) {
+      if (in.active) decode_rows<TR, NX, TR / 2, TR>(in, br, tab, wv);
+#pragma unroll
+      for (int rr = 0; rr < TR; rr++)
+#pragma unroll
+        for (int k = 0; k < 4; k++) pv[rr][k] = wv[rr][k];
+      p_row = in.rowblk;
+      p_col = in.col;
+      p_nrows = in.nrows;
+      p_active = in.active;
+    } else if constexpr (NB == 0) {
       if (in.active) decode_rows<TR, NX, TR / 2, TR>(in, br, tab, wv);
       // X rows in groups of GB: TR GB sums per lane, reduced over the
       // wavefront at once; lanes 2v and 2v + 1 end with sum v (row v / GB,
@@ -890,6 +894,10 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     }
     in = nx;
     t = tn;
+  }
+  if constexpr (DECODE) {
+    store_prev();  // nothing if this wavefront decoded no tile
+    return;
   }
   __syncthreads();
 
@@ -1281,13 +1289,15 @@ GemvPlan plan_skinny(const Launch& L, int batch, uint64_t cap) {
   return p;
 }
 
-// The batch-1 launch (count matrices) or the skinny one (one matrix, batch
-// 2..16): wavefronts per workgroup are the size with the most resident
-// wavefronts per CU (registers and LDS both count, the ranges' LDS
-// included), the larger size on a tie.
+// The batch-1 launch (count matrices), the skinny one (one matrix, batch
+// 2..16) or the standalone decode (one matrix, W' rows of ldy elements):
+// wavefronts per workgroup are the size with the most resident wavefronts
+// per CU (registers and LDS both count, the ranges' LDS included), the
+// larger size on a tie.
 template <int TR, int MAXW, int NB>
 nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y, uint8_t* const* ws, int count,
-                       int y_f32, hipStream_t s, int batch = 1, uint64_t ldx = 0, uint64_t ldy = 0) {
+                       int y_f32, hipStream_t s, int batch = 1, uint64_t ldx = 0, uint64_t ldy = 0,
+                       const uint64_t* ld_out = nullptr) {
   GemvGroup g;
   std::memset(&g, 0, sizeof(g));
   uint32_t lane_words = 0, buf_words = 0;
@@ -1302,8 +1312,8 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   // whole 256-byte units keep every slot 256-byte aligned
   buf_words = (buf_words + lane_words + 63) & ~63u;
   const size_t per_wave = (static_cast<size_t>(kWave) * lane_words + buf_words) * 4;
-  constexpr bool SKINNY = NB != 1;
-  const uint32_t sums = NB == 0 ? TR * batch : TR * NB;
+  constexpr bool SKINNY = NB == 0 || NB > 1;
+  const uint32_t sums = NB < 0 ? 0 : NB == 0 ? TR * batch : TR * NB;
   const uint32_t cus = static_cast<uint32_t>(cu_count());
   auto occupancy = [&](uint32_t n, size_t lds, int* k) {
     if (lds > kMaxLds) {
@@ -1361,12 +1371,13 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     job.b = L[j].b;
     job.x = x[j];
     job.y = y[j];
-    if (!SKINNY) {
+    if (NB == 1) {
       job.count = reinterpret_cast<uint32_t*>(ws[j]);
       job.part = reinterpret_cast<float*>(ws[j] + (job.b.n_tr * 4 + 255) / 256 * 256);
     }
     job.whole_rows = best.whole_rows[j];
     job.groups = best.groups[j];
+    job.ld = ld_out ? ld_out[j] : 0;
     job.g0 = groups;
     groups += job.groups;
   }
@@ -1455,19 +1466,12 @@ nwc_status nwc_decode(const nwc_info* info, const void* blob_dev, uint16_t* w_de
   const unsigned grid = static_cast<unsigned>(std::min<uint64_t>(blocks, kCUs * 8));
   const unsigned threads = kGenericWaves * kWave;
   if (L.fast && vec) {
+    const uint16_t* none = nullptr;
+    void* out = w_dev;
     switch (L.b.tr) {
-      case 8:
-        if (set_lds(k_decode_fast<8>, lds) != hipSuccess) return NWC_ERR_HIP;
-        k_decode_fast<8><<<grid, threads, lds, s>>>(L.b, w_dev, ld);
-        break;
-      case 16:
-        if (set_lds(k_decode_fast<16>, lds) != hipSuccess) return NWC_ERR_HIP;
-        k_decode_fast<16><<<grid, threads, lds, s>>>(L.b, w_dev, ld);
-        break;
-      default:
-        if (set_lds(k_decode_fast<32>, lds) != hipSuccess) return NWC_ERR_HIP;
-        k_decode_fast<32><<<grid, threads, lds, s>>>(L.b, w_dev, ld);
-        break;
+      case 8: return launch_gemv<8, 16, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
+      case 16: return launch_gemv<16, 8, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
+      default: return launch_gemv<32, 4, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
     }
   } else {
     if (set_lds(k_decode_generic, lds) != hipSuccess) return NWC_ERR_HIP;
@@ -1570,6 +1574,29 @@ nwc_status nwc_gemv_batched(int count, const nwc_info* infos, const void* const*
     case 8: return launch_gemv<8, 16, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
     case 16: return launch_gemv<16, 8, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
     default: return launch_gemv<32, 4, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
+  }
+}
+
+nwc_status nwc_decode_batched(int count, const nwc_info* infos, const void* const* blobs_dev, uint16_t* const* w_dev,
+                              const uint64_t* ld, void* stream) {
+  if (count < 1 || count > kMaxJobs || !infos || !blobs_dev || !w_dev || !ld) return NWC_ERR_INVALID_ARG;
+  Launch L[kMaxJobs];
+  const uint16_t* none[kMaxJobs] = {};
+  void* out[kMaxJobs];
+  for (int j = 0; j < count; j++) {
+    if (!w_dev[j]) return NWC_ERR_INVALID_ARG;
+    nwc_status st = prepare(&infos[j], blobs_dev[j], &L[j]);
+    if (st) return st;
+    if (ld[j] < L[j].b.cols) return NWC_ERR_INVALID_ARG;
+    if (!L[j].fast || L[j].b.tr != L[0].b.tr) return NWC_ERR_UNSUPPORTED;
+    if (!aligned(w_dev[j], 16) || ld[j] % 8) return NWC_ERR_ALIGNMENT;
+    out[j] = w_dev[j];
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (L[0].b.tr) {
+    case 8: return launch_gemv<8, 16, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
+    case 16: return launch_gemv<16, 8, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
+    default: return launch_gemv<32, 4, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
   }
 }
 

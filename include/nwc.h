@@ -177,6 +177,17 @@ nwc_status nwc_gemv_batched(int count, const nwc_info *infos, const void *const 
                             const uint16_t *const *x_dev, void *const *y_dev,
                             nwc_out_type y_type, void *ws, size_t ws_bytes, void *stream);
 
+/* Several independent standalone decodes in one launch (count <= 8): blob i
+ * (infos[i], blobs_dev[i]) written to w_dev[i] with row stride ld[i] >= its
+ * cols, exactly as nwc_decode would.  Every blob must have the default chunk
+ * geometry (64 chunks of 8 columns, cols % 8 == 0) and all must share
+ * tile_rows; each w_dev[i] 16-byte aligned and ld[i] % 8 == 0.  As with the
+ * batched GEMV, one grid keeps the whole GPU busy where small separate
+ * launches each pay a start-up and a tail.  Async.
+ * Errors: INVALID_ARG, UNSUPPORTED (geometry), ALIGNMENT, HIP. */
+nwc_status nwc_decode_batched(int count, const nwc_info *infos, const void *const *blobs_dev,
+                              uint16_t *const *w_dev, const uint64_t *ld, void *stream);
+
 /* Skinny decode-GEMM for batch 2..16: Y[b, n] = sum_k X[b, k] W[n, k] with X
  * (device, batch x cols, row stride ldx) and Y (device, batch x rows, row
  * stride ldy, y_type).  Same decode as nwc_gemv; FP32 accumulation.  Async.

@@ -132,6 +132,26 @@ def test_decode_padded_leading_dimension():
         assert np.all(got[:, 1001:] == 0x1234)     # nothing written past the row
 
 
+def test_decode_batched_equals_originals():
+    # the seven matrices of one layer in one launch, one of them into a wider
+    # output (ld > cols): every weight back bit-exactly, nothing written past
+    # a row
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    ws = [_w(2, n) for n in names]
+    blobs = [Blob(w) for w in ws]
+    outs = []
+    for i, w in enumerate(ws):
+        ld = w.shape[1] + (8 if i == 2 else 0)
+        outs.append(torch.full((w.shape[0], ld), 0x1234, dtype=torch.int16, device="cuda"))
+    _say("decode_batched 7 matrices")
+    nwc.nwc_decode_batched(nwc.DecodeBatch([b.info for b in blobs], [b.dev for b in blobs], outs))
+    torch.cuda.synchronize()
+    for w, out, n in zip(ws, outs, names):
+        got = out.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got[:, :w.shape[1]], w), n
+        assert np.all(got[:, w.shape[1]:] == 0x1234), n
+
+
 def test_decode_oracle_written_blob():
     # the GPU decoder follows the format, not just the library's encoder
     w = _w(1, "w")

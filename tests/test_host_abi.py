@@ -247,3 +247,16 @@ def test_device_calls_validate_before_launch():
     assert L.nwc_gemv_batched(2, mixed, ok, ok, ok, 0, A, 1 << 20, None) == nwc.NWC_ERR_UNSUPPORTED
     gen = (nwc.nwc_info * 2)(info, ginfo)
     assert L.nwc_gemv_batched(2, gen, ok, ok, ok, 0, A, 1 << 20, None) == nwc.NWC_ERR_UNSUPPORTED
+    # grouped decode: count, NULL arrays, row strides, alignment, geometry mix
+    U2 = ctypes.c_uint64 * 2
+    lds = U2(info.cols, info.cols)
+    for count in (0, 9):
+        assert L.nwc_decode_batched(count, infos, ok, ok, lds, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_decode_batched(2, None, ok, ok, lds, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_decode_batched(2, infos, ok, ok, None, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_decode_batched(2, infos, ok, V2(A, None), lds, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_decode_batched(2, infos, ok, ok, U2(info.cols, info.cols - 1), None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_decode_batched(2, infos, ok, V2(A, A + 8), lds, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_decode_batched(2, infos, ok, ok, U2(info.cols, info.cols + 4), None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_decode_batched(2, mixed, ok, ok, U2(info.cols, 512), None) == nwc.NWC_ERR_UNSUPPORTED
+    assert L.nwc_decode_batched(2, gen, ok, ok, U2(info.cols, 500), None) == nwc.NWC_ERR_UNSUPPORTED
