@@ -421,25 +421,24 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDe
 // -------------------------------------------------------------------- GEMV
 
 // One matrix of a fused batch-1 launch.  Its tiles, numbered row block by row
-// block (t = i * n_tc + j), are cut into equal contiguous ranges (sizes differ
-// by at most one), one per wavefront of the matrix's `groups` workgroups.  A
-// row block whose tiles all fall in one range is summed in registers.  A row
-// block cut between ranges leaves one sum per tile and row in `part`; the
-// wavefront that completes the row block's last range (counted on `count`)
-// adds them and sets the counter and the sums back to zero, so the workspace
-// is all zero between launches.  Both add a row's tile sums in column order
-// starting from zero, so y does not depend on the cut.
+// block (t = i * n_tc + j), are cut into `groups` contiguous ranges, one per
+// workgroup: whole row blocks (whole_rows), or equal ranges (sizes differ by
+// at most one) that may cut a row block.  A row block inside a range is
+// summed in LDS; a cut one is finished through `slots` (one 64-bit slot per
+// tile and row, all zero between launches) by the chain described at the end
+// of the kernel.
 struct GemvJob {
   BlobDev b;
   const uint16_t* x;
   void* y;
-  float* part;      // [n_tiles][TR] tile sums of cut row blocks
-  uint32_t* count;  // [n_tr] ranges finished per row block
+  uint64_t* slots;      // [n_tiles][TR]: link i of row block rb's chain at tile rb * n_tc + i
   uint32_t g0;          // first workgroup of this matrix
   uint32_t groups;      // workgroups of this matrix
-  uint32_t whole_rows;  // 1: each range is whole row blocks; 0: ranges cut anywhere
+  uint32_t whole_rows;  // 1: each range is whole row blocks; 0: equal ranges
   uint64_t ld;          // decode mode: row stride of W' in elements
 };
+// a chain slot holds a partial sum's FP32 bits with this flag set
+constexpr uint64_t kSlotFull = 1ull << 32;
 constexpr int kMaxJobs = 8;
 constexpr uint32_t kGroupLds = 8192;       // least per-workgroup LDS for control words, offsets, tile sums
 constexpr uint32_t kSkinnyLds = 24576;     // per-workgroup LDS for the skinny mode's tile sums
@@ -651,23 +650,11 @@ __device__ __forceinline__ void load_xg(const BlobDev& b, const uint16_t* X, uin
   }
 }
 
-// Data handed between workgroups.  On this chip each XCD has its own L2, and
-// an agent-scope fence writes back or invalidates the whole L2, which is far
-// too slow to do once per workgroup.  The partial sums instead go through
-// agent-scope atomic stores and loads, which write and read through to the
-// level shared by all XCDs, and ordering needs only waits for the
-// workgroup's own memory operations: its stores are complete before the
-// counter is incremented, and its loads are issued after the result returns.
-__device__ __forceinline__ void put_shared(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get_shared(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores_done() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  wait_vmem();
-}
+// Partial sums handed between workgroups travel inside agent-scope atomic
+// exchanges.  On this chip each XCD has its own L2, and an agent-scope fence
+// writes back or invalidates a whole L2, far too slow to do per workgroup;
+// an agent-scope atomic is performed at the level all XCDs share, and a
+// value carried by the atomic itself needs no fence at all.
 
 // the range that holds tile t, for ranges [w T / W, (w + 1) T / W)
 __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W) { return ((t + 1) * W - 1) / T; }
@@ -919,71 +906,50 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     return;
   }
 
-  // Row blocks [rb_a, rb_b] meet the range; a cut one (the first or the last)
-  // leaves its tile sums in the workspace.
+  // Row blocks [rb_a, rb_b] meet the range.  A row block inside it: each
+  // row adds its tile sums in column order and is stored.  A row block that
+  // range edges cut has contributors c = 0 .. k - 1, the workgroups whose
+  // ranges meet it in column order, each with p_c, its own tile sums of the
+  // row added in column order; y = ((p_0 + p_1) + p_2) + ... is formed along
+  // a chain of k - 1 links, one workspace slot each (per row).  Link i meets
+  // the running sum of p_0 .. p_(i-1) and p_i (p_0 goes to link 1): each
+  // side swaps its value into the slot with the flag set, and the one that
+  // finds the other's value there adds the two (one rounding of the same two
+  // operands in either order), clears the slot, and carries the sum on to
+  // link i + 1, or stores y at the last link.  One atomic per link and no
+  // waiting on another workgroup; the order of the additions is fixed by the
+  // ranges, so repeated calls give the same bits.
   if (n_r == 0) return;
   const uint64_t rb_a = r0 / n_tc, rb_b = (r1 - 1) / n_tc;
-  const bool cut_a = r0 != rb_a * n_tc || r1 < rb_a * n_tc + n_tc;
-  const bool cut_b = r1 != rb_b * n_tc + n_tc || r0 > rb_b * n_tc;
   for (uint32_t k = threadIdx.x; k < (rb_b - rb_a + 1) * TR; k += blockDim.x) {
     const uint64_t rb = rb_a + k / TR;
     const uint32_t rr = k % TR;
     const uint64_t row = rb * TR + rr;
     if (row >= b.rows) continue;
-    const uint64_t c0 = rb * n_tc > r0 ? rb * n_tc : r0;
-    const uint64_t c1 = rb * n_tc + n_tc < r1 ? rb * n_tc + n_tc : r1;
-    if ((rb == rb_a && cut_a) || (rb == rb_b && cut_b)) {
-      for (uint64_t c = c0; c < c1; c++) put_shared(job.part + c * TR + rr, gsum[(c - r0) * TR + rr]);
-    } else {
-      float sum = 0.0f;
-      for (uint64_t c = c0; c < c1; c++) sum += gsum[(c - r0) * TR + rr];
+    const uint64_t first = rb * n_tc, last = first + n_tc;
+    const uint64_t c0 = first > r0 ? first : r0;
+    const uint64_t c1 = last < r1 ? last : r1;
+    float sum = 0.0f;
+    for (uint64_t c = c0; c < c1; c++) sum += gsum[(c - r0) * TR + rr];
+    if (c0 == first && c1 == last) {
       store_y(job.y, row, sum, g.y_f32);
+      continue;
     }
-  }
-  if (!cut_a && !cut_b) return;
-  // count this workgroup's share of each cut row block; the workgroup that
-  // completes one adds all its tile sums in column order and zeroes them
-  wait_stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t mine = 0;
-    for (uint32_t k = 0; k < 2; k++) {
-      if (k == 0 ? !cut_a : (!cut_b || (rb_b == rb_a && cut_a))) continue;
-      const uint64_t rb = k == 0 ? rb_a : rb_b;
-      const uint64_t first = rb * n_tc;
-      const uint32_t groups = static_cast<uint32_t>(range_of(first + n_tc - 1, T, G) - range_of(first, T, G) + 1);
-      const uint32_t done = __hip_atomic_fetch_add(job.count + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-      if (done == groups) {
-        mine |= 1u << k;
-        __hip_atomic_store(job.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // a cut row block (equal ranges only): links 1 .. g_last - g_first
+    const uint64_t g_first = range_of(first, T, G), links = range_of(last - 1, T, G) - g_first;
+    uint64_t link = gi == g_first ? 1 : gi - g_first;
+    for (;;) {
+      uint64_t* slot = job.slots + (first + link) * TR + rr;
+      const uint64_t old = __hip_atomic_exchange(slot, kSlotFull | __builtin_bit_cast(uint32_t, sum), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+      if (!(old & kSlotFull)) break;  // first at this link: the other side carries on
+      sum += __builtin_bit_cast(float, static_cast<uint32_t>(old));
+      __hip_atomic_store(slot, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (link == links) {
+        store_y(job.y, row, sum, g.y_f32);
+        break;
       }
-    }
-    ctl[1] = mine;
-  }
-  __syncthreads();
-  const uint32_t mine = ctl[1];
-  for (uint32_t k = 0; k < 2; k++) {
-    if (!(mine >> k & 1u)) continue;
-    const uint64_t rb = k == 0 ? rb_a : rb_b;
-    const uint64_t first = rb * n_tc;
-    for (uint32_t rr = threadIdx.x; rr < TR; rr += blockDim.x) {
-      const uint64_t row = rb * TR + rr;
-      if (row >= b.rows) continue;
-      // up to 32 tile sums are loaded before the first add, so a row block
-      // costs one memory round trip per 32 column tiles
-      float sum = 0.0f;
-      for (uint32_t c = 0; c < n_tc; c += 32) {
-        float v[32];
-#pragma unroll
-        for (uint32_t u = 0; u < 32; u++) v[u] = c + u < n_tc ? get_shared(job.part + (first + c + u) * TR + rr) : 0.0f;
-#pragma unroll
-        for (uint32_t u = 0; u < 32; u++)
-          if (c + u < n_tc) {
-            sum += v[u];
-            put_shared(job.part + (first + c + u) * TR + rr, 0.0f);
-          }
-      }
-      store_y(job.y, row, sum, g.y_f32);
+      link++;
     }
   }
 }
@@ -1207,10 +1173,9 @@ unsigned grid_for(uint64_t items, uint32_t waves, size_t lds) {
   return static_cast<unsigned>(std::min<uint64_t>(items, kCUs * per_cu));
 }
 
-// Workspace of the fused batch-1 path: row-block counters, then tile sums.
+// Workspace of the fused batch-1 path: one 64-bit chain slot per tile and row.
 size_t fused_ws_bytes(const nwc::Geometry& g) {
-  auto up = [](uint64_t v) { return (v + 255) / 256 * 256; };
-  return up(g.n_tr * 4) + up(g.n_tiles * static_cast<uint64_t>(g.tr) * 4);
+  return (g.n_tiles * static_cast<uint64_t>(g.tr) * 8 + 255) / 256 * 256;
 }
 
 int cu_count() {
@@ -1234,11 +1199,14 @@ struct GemvPlan {
   size_t group_lds(uint32_t sums_per_tile) const { return (4 + tw_words() + range * sums_per_tile) * 4; }
 };
 
-// Workgroups are shared out in proportion to each matrix's tiles, no more
-// than `cap` (what the chip holds at once), so every range runs in one pass.
-// A matrix's ranges are whole row blocks when the largest such range is
-// within 15% of an even share of tiles or holds no more tiles than a
-// workgroup has wavefronts; otherwise they cut row blocks.
+// Workgroups: as many as the chip holds at once (`cap`), or one per tile
+// when there are fewer tiles, shared out in proportion to each matrix's tiles
+// (largest remainders); each matrix's tiles are cut into equal ranges.
+// Workgroups land one per CU, then a second per CU, so equal ranges give
+// every CU the same number of tiles and every wavefront the same number give
+// or take one, which whole row blocks per range rarely can.  A matrix's
+// ranges are whole row blocks instead when that changes neither its
+// workgroups nor its tiles per wavefront.
 template <int TR>
 GemvPlan plan_gemv(const Launch* L, int count, uint64_t cap, uint32_t nw, size_t group_lds) {
   GemvPlan p;
@@ -1247,19 +1215,39 @@ GemvPlan plan_gemv(const Launch* L, int count, uint64_t cap, uint32_t nw, size_t
   for (int j = 0; j < count; j++) total += L[j].b.n_tiles;
   // the largest range whose offsets and tile sums fit the group's LDS
   const uint64_t max_range = std::max<uint64_t>(1, (group_lds / 4 - 4 - 4) / (TR + 1));
+  const uint64_t want = std::max<uint64_t>(count, std::min<uint64_t>(cap, total));
+  uint64_t G[kMaxJobs], given = 0;
+  for (int j = 0; j < count; j++) {
+    G[j] = want * L[j].b.n_tiles / total;
+    given += G[j];
+  }
+  bool bumped[kMaxJobs] = {};
+  while (given < want) {  // fewer than count times
+    int best = -1;
+    uint64_t rem = 0;
+    for (int j = 0; j < count; j++) {
+      const uint64_t r = want * L[j].b.n_tiles % total;
+      if (!bumped[j] && (best < 0 || r > rem)) {
+        rem = r;
+        best = j;
+      }
+    }
+    bumped[best] = true;
+    G[best]++;
+    given++;
+  }
   p.range = 1;
   for (int j = 0; j < count; j++) {
     const uint64_t T = L[j].b.n_tiles, n_tr = L[j].b.n_tr, n_tc = L[j].b.n_tc;
-    uint64_t G = std::min<uint64_t>(T, 1 + (cap > static_cast<uint64_t>(count) ? cap - count : 0) * T / total);
-    G = std::max<uint64_t>(G, (T + max_range - 1) / max_range);
-    // whole row blocks per range: k of them in every range but the last
-    const uint64_t k = (n_tr + G - 1) / G;
-    const bool whole = k * n_tc <= max_range &&
-                       (k * n_tc <= nw || static_cast<double>(k * n_tc) <= 1.15 * static_cast<double>(T) / G);
-    if (whole) G = (n_tr + k - 1) / k;
+    uint64_t Gj = std::min<uint64_t>(T, std::max<uint64_t>(1, G[j]));
+    Gj = std::max<uint64_t>(Gj, (T + max_range - 1) / max_range);
+    const uint64_t range = (T + Gj - 1) / Gj;
+    const uint64_t k = (n_tr + Gj - 1) / Gj;  // row blocks per whole-row range
+    const bool whole = (n_tr + k - 1) / k == Gj && k * n_tc <= max_range &&
+                       (k * n_tc + nw - 1) / nw <= (range + nw - 1) / nw;
     p.whole_rows[j] = whole ? 1u : 0u;
-    p.groups[j] = static_cast<uint32_t>(G);
-    p.range = std::max<uint64_t>(p.range, whole ? k * n_tc : (T + G - 1) / G);
+    p.groups[j] = static_cast<uint32_t>(Gj);
+    p.range = std::max<uint64_t>(p.range, whole ? k * n_tc : range);
     p.total_groups += p.groups[j];
   }
   return p;
@@ -1372,8 +1360,7 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     job.x = x[j];
     job.y = y[j];
     if (NB == 1) {
-      job.count = reinterpret_cast<uint32_t*>(ws[j]);
-      job.part = reinterpret_cast<float*>(ws[j] + (job.b.n_tr * 4 + 255) / 256 * 256);
+      job.slots = reinterpret_cast<uint64_t*>(ws[j]);
     }
     job.whole_rows = best.whole_rows[j];
     job.groups = best.groups[j];

@@ -134,12 +134,12 @@ nwc_status nwc_decode(const nwc_info *info, const void *blob_dev, uint16_t *w_de
 
 /* Workspace bytes needed by nwc_gemv (batch = 1) or nwc_gemm_skinny
  * (batch 2..16) for this blob.
- *  - Fused batch-1 path (default geometry, cols % 8 == 0): one counter per
- *    row block and one FP32 partial sum per (tile, row), 256-byte aligned
- *    sections.  The kernel splits the tiles evenly over the GPU, so a row
- *    block can be shared by several wavefronts; the counters tell the last
- *    one to finish that it adds the partial sums.  The workspace must be
- *    zero-filled before its first use; every call leaves it zero-filled.
+ *  - Fused batch-1 path (default geometry, cols % 8 == 0): one 64-bit slot
+ *    per (tile, row), rounded up to 256 bytes.  The kernel splits the tiles
+ *    evenly over the GPU, so a row block can be shared by several
+ *    workgroups; their partial sums meet in these slots.  The workspace
+ *    must be zero-filled before its first use; every call leaves it
+ *    zero-filled.
  *  - Fused skinny path (tile_rows 8 or 16, batch 2..16): 0 (ws may be NULL).
  *  - Otherwise FP32 partial sums, one per (column tile, batch row, output
  *    row), for the one-symbol-at-a-time path, which runs a second reduction
@@ -149,9 +149,10 @@ nwc_status nwc_workspace_size(const nwc_info *info, int batch, size_t *bytes);
 /* Fused decode-GEMV (pages: "Fused kernel"; Unweight "Direct GPU
  * Decompression"): y = W x with x (device, cols BF16, 16-byte aligned) and y
  * (device, rows entries of y_type).  Weights are decoded in registers and
- * LDS and never written to memory; each output row adds its per-tile FP32
- * sums in column order, so y does not depend on how the tiles were shared
- * out, and each y entry is written once.  ws is a device workspace of at
+ * LDS and never written to memory; FP32 accumulation, each output row's
+ * partial sums added in an order fixed by the blob's shape, the launch's
+ * other matrices and the GPU, so repeated calls give bitwise-identical y.
+ * Each y entry is written once.  ws is a device workspace of at
  * least nwc_workspace_size(info, 1) bytes, 256-byte aligned, used as that
  * function describes (zero-filled before first use on the fused path).
  * Calls that share a workspace must not run concurrently (same stream, or
@@ -170,8 +171,10 @@ nwc_status nwc_gemv(const nwc_info *info, const void *blob_dev, const uint16_t *
  * fused batch-1 path and all must share tile_rows.  ws (256-byte aligned,
  * zero-filled before first use, left zero-filled) holds the workspaces of
  * all blobs back to back: at least the sum over i of
- * nwc_workspace_size(&infos[i], 1).  Each y_i is bitwise identical to what
- * nwc_gemv computes for it.  Same concurrency rule as nwc_gemv.  Async.
+ * nwc_workspace_size(&infos[i], 1).  Each y_i meets nwc_gemv's accuracy;
+ * its bits may differ from a single call's (the tiles are shared out over
+ * the whole launch), and repeating the same batched call repeats them.
+ * Same concurrency rule as nwc_gemv.  Async.
  * Errors: INVALID_ARG, BUFFER_TOO_SMALL (ws), UNSUPPORTED, ALIGNMENT, HIP. */
 nwc_status nwc_gemv_batched(int count, const nwc_info *infos, const void *const *blobs_dev,
                             const uint16_t *const *x_dev, void *const *y_dev,

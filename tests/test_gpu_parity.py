@@ -275,25 +275,26 @@ def _counters_zero(blobs, ws):
     return int(ws[:n].count_nonzero()) == 0
 
 
-def test_gemv_batched_equals_single_calls():
+def test_gemv_batched_seven_matrices_and_repeats():
+    # the whole layer in one launch: every y within the bound, the workspace
+    # left zero, and the same call twice gives the same bits
     names = ["q", "k", "v", "o", "gate", "up", "down"]
     blobs = [Blob(_w(2, n)) for n in names]
     xs = [dev(workloads.activations(2, n)[0]) for n in names]
     for out_f32 in (False, True):
         dt = torch.float32 if out_f32 else torch.bfloat16
         ys = [torch.empty(b.info.rows, dtype=dt, device="cuda") for b in blobs]
+        ys2 = [torch.empty_like(y) for y in ys]
         ws = _batched_ws(blobs)
-        batch = nwc.GemvBatch([b.info for b in blobs], [b.dev for b in blobs], xs, ys, ws)
-        _say("gemv_batched 7 matrices f32=%s" % out_f32)
-        nwc.nwc_gemv_batched(batch)
-        torch.cuda.synchronize()
-        assert _counters_zero(blobs, ws)
-        for b, x, y, n in zip(blobs, xs, ys, names):
-            y1 = torch.empty_like(y)
-            nwc.nwc_gemv(b.info, b.dev, x, y1, b.ws())
+        for out in (ys, ys2):
+            batch = nwc.GemvBatch([b.info for b in blobs], [b.dev for b in blobs], xs, out, ws)
+            _say("gemv_batched 7 matrices f32=%s" % out_f32)
+            nwc.nwc_gemv_batched(batch)
             torch.cuda.synchronize()
-            assert torch.equal(y.view(torch.int16) if not out_f32 else y.view(torch.int32),
-                               y1.view(torch.int16) if not out_f32 else y1.view(torch.int32)), n
+            assert _counters_zero(blobs, ws)
+        for b, x, y, y2, n in zip(blobs, xs, ys, ys2, names):
+            iv = torch.int32 if out_f32 else torch.int16
+            assert torch.equal(y.view(iv), y2.view(iv)), n
             y_ref, a_ref = oracle.gemv(b.w, x.cpu().numpy())
             _check_y(_to_f64(y), y_ref, a_ref, out_f32, n)
 

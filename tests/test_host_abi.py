@@ -162,20 +162,20 @@ def test_workspace_sizes():
     for bad in (0, 17):
         with pytest.raises(nwc.NwcError):
             nwc.nwc_workspace_size(info, bad)
-    # fused batch 1: row-block counters, then one sum per (tile, row), each
-    # section rounded up to 256 bytes; the fused skinny path needs none
+    # fused batch 1: one 64-bit chain slot per (tile, row), rounded up to 256
+    # bytes; the fused skinny path needs none
     up = lambda v: -(-v // 256) * 256
     fast = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2)))
-    assert nwc.nwc_workspace_size(fast, 1) == up(13 * 4) + up(13 * 3 * 8 * 4)
+    assert nwc.nwc_workspace_size(fast, 1) == up(13 * 3 * 8 * 8)
     tr16 = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2), dict(tile_rows=16)))
-    assert nwc.nwc_workspace_size(tr16, 1) == up(7 * 4) + up(7 * 3 * 16 * 4)
+    assert nwc.nwc_workspace_size(tr16, 1) == up(7 * 3 * 16 * 8)
     assert nwc.nwc_workspace_size(tr16, 8) == 0
     assert nwc.nwc_workspace_size(fast, 8) == 0
     assert nwc.gemv_batched_workspace_size([fast, tr16]) == (nwc.nwc_workspace_size(fast, 1) +
                                                              nwc.nwc_workspace_size(tr16, 1))
     # batch > 1 with tile_rows 32 takes the generic path
     tr32 = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2), dict(tile_rows=32)))
-    assert nwc.nwc_workspace_size(tr32, 1) == up(4 * 4) + up(4 * 3 * 32 * 4)
+    assert nwc.nwc_workspace_size(tr32, 1) == up(4 * 3 * 32 * 8)
     assert nwc.nwc_workspace_size(tr32, 8) == 3 * 8 * 100 * 4
     assert nwc.nwc_bf16_workspace_size(100, 1500) == 0
 
