@@ -452,7 +452,8 @@ def cpu_baseline(wl, keys, info, batch, seconds):
         n_rows = info[(layer, name)].rows
         r0 = (i // len(keys)) * nb % n_rows
         sub = workloads.weights(wl.cid, name, layer=layer, rows=slice(r0, min(r0 + nb, n_rows)))
-        blob = oracle.encode(sub, 8, 512, 64, 12)
+        li = info[(layer, name)]  # the library blob's geometry and code length limit
+        blob = oracle.encode(sub, li.tile_rows, li.tile_cols, li.chunks_per_tile, li.max_code_len)
         x = workloads.activations(wl.cid, name, batch=batch, layer=layer)
         t = time.perf_counter()
         wd = oracle.decode(blob)

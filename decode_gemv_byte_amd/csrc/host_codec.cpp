@@ -192,7 +192,7 @@ bool params_resolve(const nwc_params* p, Geometry* g) {
   g->tr = (p && p->tile_rows) ? p->tile_rows : 8;
   g->tc = (p && p->tile_cols) ? p->tile_cols : 512;
   g->s = (p && p->chunks_per_tile) ? p->chunks_per_tile : 64;
-  g->lmax = (p && p->max_code_len) ? p->max_code_len : 12;
+  g->lmax = (p && p->max_code_len) ? p->max_code_len : 8;
   if (g->tc % g->s) return false;
   if (g->lmax < 8 || g->lmax > 12) return false;
   g->v = g->tc / g->s;

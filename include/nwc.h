@@ -77,7 +77,7 @@ typedef struct {
   uint32_t tile_rows;       /* TR rows per tile [8] */
   uint32_t tile_cols;       /* TC columns per tile [512] */
   uint32_t chunks_per_tile; /* S column-strip chunks per tile [64] */
-  uint32_t max_code_len;    /* L, longest code in bits [12] */
+  uint32_t max_code_len;    /* L, longest code in bits [8] */
 } nwc_params;
 
 /* Everything a device call needs, read from a validated blob. */

@@ -16,7 +16,7 @@ import workloads
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nwc.h")
 
-DEFAULT = dict(tile_rows=8, tile_cols=512, chunks_per_tile=64, max_code_len=12)
+DEFAULT = dict(tile_rows=8, tile_cols=512, chunks_per_tile=64, max_code_len=8)
 
 
 def _declared_functions():
@@ -51,7 +51,7 @@ def _oracle_blob(w, p):
 
 GEOMS = [None, dict(tile_rows=16), dict(tile_rows=32), dict(tile_rows=5, tile_cols=24, chunks_per_tile=3,
                                                               max_code_len=11),
-         dict(tile_rows=3, tile_cols=7, chunks_per_tile=7, max_code_len=10), dict(max_code_len=8)]
+         dict(tile_rows=3, tile_cols=7, chunks_per_tile=7, max_code_len=10), dict(max_code_len=12)]
 
 
 @pytest.mark.parametrize("geom", GEOMS)
