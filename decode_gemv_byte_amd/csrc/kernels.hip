@@ -46,6 +46,8 @@
 namespace {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kWave = 64;
 constexpr int kMaxWaves = 16;      // wavefronts per workgroup, fused kernels
@@ -184,6 +186,14 @@ __device__ __forceinline__ uint32_t lds_word(uint32_t byte_addr) {
 typedef __attribute__((address_space(3))) uint32_t lds_u32w;
 __device__ __forceinline__ void lds_put(uint32_t byte_addr, uint32_t v) {
   *(lds_u32w*)(static_cast<uintptr_t>(byte_addr)) = v;
+}
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u128;
+__device__ __forceinline__ void lds_put4(uint32_t byte_addr, uint4 v) {
+  *(lds_u128*)(static_cast<uintptr_t>(byte_addr)) = __builtin_bit_cast(u32x4_t, v);
+}
+__device__ __forceinline__ uint4 lds_get4(uint32_t byte_addr) {
+  return __builtin_bit_cast(uint4, *(const lds_u128*)(static_cast<uintptr_t>(byte_addr)));
 }
 
 // Raw buffer resource over [base, base + bytes) (bytes capped at 4 GiB - 1):
@@ -678,13 +688,17 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 // decoded into registers first and then multiplied by the X rows 32 / TR at
 // a time (NB 0, 2, 4: the skinny mode, one matrix, ranges of whole row
 // blocks); -1 for the standalone decode, which writes each decoded tile to
-// W' (job.y, rows of g.ldy elements) once the next tile's data is in.
+// W' (job.y, rows of g.ldy elements) once the next tile's data is in; 16
+// for Y = X W^T with up to 16 X rows on the matrix cores (8-row tiles: the
+// decoded tile goes through LDS into MFMA operand layout).
 template <int TR, int MAXW, int NB>
 __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   constexpr bool DECODE = NB < 0;
+  constexpr bool MF = NB == 16;
   constexpr bool SKINNY = NB == 0 || NB > 1;
-  constexpr int NX = NB > 0 ? NB : 0;  // X rows that come with each tile
-  constexpr int NA = NB > 0 ? NB : 1;  // sums per row of a tile formed while decoding
+  constexpr int NX = NB > 0 && !MF ? NB : 0;  // X rows that come with each tile
+  constexpr int NA = NB > 0 && !MF ? NB : 1;  // sums per row of a tile formed while decoding
+  static_assert(!MF || TR == 8, "the matrix-core mode takes 8-row tiles");
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const uint32_t nw = blockDim.x / kWave;
@@ -795,6 +809,86 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     }
   };
   while (t < r1) {
+    if constexpr (MF) {
+      // Matrix-core mode.  The whole tile is in (the next tile's loads go out
+      // at the end of this one, so that the X loads below never wait behind
+      // them: vector memory operations retire in order).
+      wait_vmem();
+      wave_sync_lds();
+      const uint32_t q0 = interleave(buf, in.w0, in.a0, in.cb(), J, slot);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      wave_sync_lds();
+      uint32_t wv[TR][4];
+#pragma unroll
+      for (int k = 0; k < TR; k++) wv[k][0] = wv[k][1] = wv[k][2] = wv[k][3] = 0u;
+      LaneBits br;
+      br.init(slot, q0);
+      if (in.active) decode_rows<TR, NX, 0, TR>(in, br, tab, wv);
+      // Y block (16 weight rows x 16 X rows) += W block (16 x 32) x X^T block
+      // (32 x 16), 16 times over the tile's 512 columns.  MFMA operands: lane
+      // l holds row l % 16 of W (rows 8..15 zero) and row l % 16 of X (zero
+      // past the batch), columns 8 (l / 16) .. + 7 of the 32; the result holds
+      // W rows 4 (l / 16) .. + 3 for X row l % 16.  The tile goes through the
+      // slot, whose stream is no longer needed, 128 columns (16 lanes) at a
+      // time: T[r][c] at byte r * 272 + 2 c (rows padded against bank
+      // conflicts).
+      const uint32_t m = lane & 15u, gq = lane >> 4;
+      const uint32_t T = lds_addr(slot);
+      const uint32_t zero = lds_addr(buf);  // the staging buffer's 4 zero guard words
+      const uint32_t a_at = m < TR ? T + m * 272u + gq * 16u : zero;
+      const uint32_t a_step = m < TR ? 64u : 0u;
+      const uint64_t col0 = static_cast<uint64_t>(in.col) * 512;
+      const bool x_row = m < g.batch;
+      const uint16_t* xr = job.x + (x_row ? static_cast<uint64_t>(m) * g.ldx : 0) + col0;
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int h = 0; h < 4; h++) {
+        // this phase's X (issued here, not hoisted: four phases at once would
+        // not fit the registers)
+        asm volatile("" ::: "memory");
+        uint4 xb[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) {
+          const uint32_t kc = static_cast<uint32_t>(128 * h + 32 * qq) + gq * 8u;
+          const bool ok = x_row && col0 + kc < b.cols;
+          xb[qq] = *reinterpret_cast<const uint4*>(xr + (ok ? kc : 0u));
+          if (!ok) xb[qq] = make_uint4(0, 0, 0, 0);
+        }
+        if (gq == static_cast<uint32_t>(h)) {
+#pragma unroll
+          for (int r = 0; r < TR; r++)
+            lds_put4(T + static_cast<uint32_t>(r) * 272u + m * 16u,
+                     make_uint4(wv[r][0], wv[r][1], wv[r][2], wv[r][3]));
+        }
+        wave_sync_lds();
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) {
+          const uint4 av = lds_get4(a_at + static_cast<uint32_t>(qq) * a_step);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                        __builtin_bit_cast(bf16x8_t, xb[qq]), acc, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // this phase's reads are done before T is written again
+        wave_sync_lds();
+      }
+      if (gq < TR / 4 && x_row) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) gsum[((t - r0) * TR + gq * 4 + e) * g.batch + m] = acc[e];
+      }
+      TileRegs<TR, NX> nx;
+      const uint64_t tn = claims ? claim() : r1;
+      if (tn < r1) {
+        const uint64_t ni = tn / n_tc;
+        const uint32_t nj = static_cast<uint32_t>(tn - ni * n_tc);
+        const uint32_t w0 = __builtin_amdgcn_readfirstlane(tw[tn - r0]);
+        const uint32_t w1 = __builtin_amdgcn_readfirstlane(tw[tn - r0 + 1]);
+        nx.load(b, job.x, g.ldx, g.batch, ni, nj, w0, w1, buf);
+        asm volatile("" ::: "memory");
+        nx.load_rest(b, ni, nj);
+      }
+      in = nx;
+      t = tn;
+      continue;
+    }
     wait_vmem_but<TR / 2>();
     if constexpr (DECODE) store_prev();
     wave_sync_lds();
@@ -817,7 +911,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     br.init(slot, q0);
     if constexpr (NB <= 0) {
       if (in.active) decode_rows<TR, NX, 0, TR / 2>(in, br, tab, wv);
-    } else {
+    } else if constexpr (!MF) {
       if (in.active) gemv_rows<TR, NX, 0, TR / 2>(in, br, tab, acc);
     }
     // the second half's raw bytes, then the next tile's loads: they go out
@@ -871,7 +965,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
         const uint32_t beta = gi2 * GB + v % GB;
         if ((lane & 1u) == 0 && beta < g.batch) gsum[((t - r0) * TR + vr) * g.batch + beta] = sv;
       }
-    } else {
+    } else if constexpr (!MF) {
       if (in.active) gemv_rows<TR, NX, TR / 2, TR>(in, br, tab, acc);
       // lanes (64 / (TR NB)) v .. hold sum v: row v / NB, X row v % NB
       const float s = reduce_rows<TR * NA>(acc);
@@ -892,7 +986,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     // whole row blocks only: every output adds its tile sums in column order
     if (n_r == 0) return;
     const uint64_t rb_a = r0 / n_tc;
-    const uint32_t nbs = NB > 0 ? NB : g.batch;  // sums per row of a tile in LDS
+    const uint32_t nbs = NB > 0 && !MF ? NB : g.batch;  // sums per row of a tile in LDS
     const uint32_t per_rb = TR * g.batch;
     for (uint32_t k = threadIdx.x; k < n_r / n_tc * per_rb; k += blockDim.x) {
       const uint64_t rb = rb_a + k / per_rb;
@@ -1258,18 +1352,19 @@ GemvPlan plan_gemv(const Launch* L, int count, uint64_t cap, uint32_t nw, size_t
 uint32_t skinny_sums_per_row(int tr, int batch) { return tr == 8 && batch == 3 ? 4u : static_cast<uint32_t>(batch); }
 
 // Row blocks of one matrix per skinny-mode range: as many as keep one range
-// per resident workgroup, no more than fit kSkinnyLds (0: not even one).
-uint64_t skinny_rows_per_range(uint64_t n_tr, uint64_t n_tc, int tr, int batch, uint64_t cap) {
-  const uint64_t fit = kSkinnyLds / (n_tc * tr * skinny_sums_per_row(tr, batch) * 4);
-  if (fit == 0) return 0;
+// per resident workgroup (so that every range runs in one pass), no more
+// than the workgroup's LDS for tile sums holds (at least kSkinnyLds, which
+// always holds one row block's).
+uint64_t skinny_rows_per_range(uint64_t n_tr, uint64_t n_tc, int tr, int batch, uint64_t cap, size_t group_lds) {
+  const uint64_t fit = std::max<size_t>(kSkinnyLds, group_lds) / (n_tc * tr * skinny_sums_per_row(tr, batch) * 4 + 4 * n_tc);
   return std::max<uint64_t>(1, std::min<uint64_t>(fit, (n_tr + cap - 1) / cap));
 }
 
 template <int TR>
-GemvPlan plan_skinny(const Launch& L, int batch, uint64_t cap) {
+GemvPlan plan_skinny(const Launch& L, int batch, uint64_t cap, size_t group_lds) {
   GemvPlan p;
   std::memset(&p, 0, sizeof(p));
-  const uint64_t k = skinny_rows_per_range(L.b.n_tr, L.b.n_tc, TR, batch, cap);
+  const uint64_t k = skinny_rows_per_range(L.b.n_tr, L.b.n_tc, TR, batch, cap, group_lds);
   p.whole_rows[0] = 1;
   p.groups[0] = static_cast<uint32_t>((L.b.n_tr + k - 1) / k);
   p.total_groups = p.groups[0];
@@ -1296,12 +1391,15 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     lane_words = std::max(lane_words, (((30 + L[j].max_chunk_bits) >> 5) + 2 + 1) & ~1u);
     buf_words = std::max(buf_words, L[j].b.buf_words);
   }
+  // the matrix-core mode passes each decoded tile through the slot (8 rows
+  // of 272 bytes)
+  if (NB == 16) lane_words = std::max(lane_words, 10u);
   // the interleaving copy reads up to lane_words past the last chunk start;
   // whole 256-byte units keep every slot 256-byte aligned
   buf_words = (buf_words + lane_words + 63) & ~63u;
   const size_t per_wave = (static_cast<size_t>(kWave) * lane_words + buf_words) * 4;
   constexpr bool SKINNY = NB == 0 || NB > 1;
-  const uint32_t sums = NB < 0 ? 0 : NB == 0 ? TR * batch : TR * NB;
+  const uint32_t sums = NB < 0 ? 0 : NB == 0 || NB == 16 ? TR * batch : TR * NB;
   const uint32_t cus = static_cast<uint32_t>(cu_count());
   auto occupancy = [&](uint32_t n, size_t lds, int* k) {
     if (lds > kMaxLds) {
@@ -1321,7 +1419,7 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   };
   auto plan = [&](uint64_t cap, uint32_t n, int k) {
     if constexpr (SKINNY)
-      return plan_skinny<TR>(L[0], batch, cap);
+      return plan_skinny<TR>(L[0], batch, cap, group_budget(n, k));
     else
       return plan_gemv<TR>(L, count, cap, n, std::max<size_t>(kGroupLds, group_budget(n, k)));
   };
@@ -1500,13 +1598,17 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
     const uint16_t* XX = X;
     void* yy = Y;
     // up to 32 / TR X rows are multiplied as each pair is decoded; more go
-    // through the tile decoded into registers
+    // through the tile decoded into registers, and from 10 X rows on (8-row
+    // tiles) through the matrix cores, which then cost less than the
+    // vector products they replace
     if (L.b.tr == 8) {
       switch (batch) {
         case 2: return launch_gemv<8, 16, 2>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
         case 3:  // a power-of-two count of sums per lane: X row 3 is zero
         case 4: return launch_gemv<8, 16, 4>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
-        default: return launch_gemv<8, 16, 0>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+        default:
+          if (batch < 10) return launch_gemv<8, 16, 0>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+          return launch_gemv<8, 16, 16>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
       }
     }
     if (batch == 2) return launch_gemv<16, 8, 2>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);

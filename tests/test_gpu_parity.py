@@ -327,7 +327,7 @@ def _gemm(blob: Blob, X: np.ndarray, out_f32: bool):
     return Y
 
 
-@pytest.mark.parametrize("batch", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("batch", [2, 3, 4, 5, 8, 13, 16])
 @pytest.mark.parametrize("name,params", [("cfg1", None), ("127x1001", None), ("1000x256", None),
                                          ("cfg1", dict(tile_rows=16)), ("1000x256", dict(tile_rows=16)),
                                          ("cfg1", dict(tile_rows=32)), ("wide_odd", None)])
