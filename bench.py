@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0   # dense BF16 matrix-core peak
 STREAM_BYTES = 1.0e9          # device copies cycled per pass, well above the Infinity Cache
 CHECK_ROWS = 256              # rows per matrix checked against an FP64 product
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemv_qwen3_4b_gate_up_traffic.txt")
@@ -116,8 +117,8 @@ def main():
     dev = torch.device("cuda", 0)
     wl = workloads.WORKLOADS[args.workload]
     batch = args.batch or wl.batches[0]
-    if not 1 <= batch <= 16:
-        sys.exit("batch must be 1..16")
+    if not 1 <= batch <= 8192:
+        sys.exit("batch must be 1..8192 (above 16: decode + hipBLASLt GEMM)")
     params = {k: v for k, v in (("tile_rows", args.tile_rows), ("max_code_len", args.max_code_len)) if v}
     groups_named = [list(g) for g in wl.groups] if wl.groups else [[m.name] for m in wl.matrices]
     # the step: every layer's groups in order; a key is (layer, matrix name)
@@ -174,12 +175,21 @@ def main():
 
         def launch(c, i):
             nwc.nwc_gemv_batched(launches[c][i], stream=stream)
-    else:
+    elif batch <= 16:
         kws = {k: zeroed(nwc.nwc_workspace_size(info[k], batch)) for k in keys}
 
         def launch(c, i):
             for k in groups[i]:
                 nwc.nwc_gemm_skinny(info[k], blobs[c][k], xs[k], ys[k], kws[k], stream=stream)
+    else:
+        # prefill: each matrix decoded into one shared BF16 workspace, then a
+        # hipBLASLt GEMM (the calls run one after another on one stream)
+        blas = nwc.Blas()
+        pws = torch.empty(max(nwc.nwc_prefill_workspace_size(info[k]) for k in keys), dtype=torch.uint8, device=dev)
+
+        def launch(c, i):
+            for k in groups[i]:
+                nwc.nwc_gemm_prefill(blas, info[k], blobs[c][k], xs[k], ys[k], pws, stream=stream)
 
     def step(c):
         for i in range(len(groups)):
@@ -202,14 +212,33 @@ def main():
         return e0.elapsed_time(e1) * 1e3 / reps
 
     dom_name = "+".join("%s%s" % (n, "@%d" % l if wl.layers > 1 else "") for (l, n) in groups[gi])
-    kernel = "k_gemv via nwc_gemv_batched" if batch == 1 else "k_gemm_mfma via nwc_gemm_skinny"
+    kernel = ("k_gemv via nwc_gemv_batched" if batch == 1 else "k_gemv skinny mode via nwc_gemm_skinny"
+              if batch <= 16 else "k_gemv decode mode + hipBLASLt GEMM via nwc_gemm_prefill")
 
     def roofline(us):
-        a = gbytes[gi] / (us * 1e-6) / 1e9
+        if batch <= 16:
+            a = gbytes[gi] / (us * 1e-6) / 1e9
+            return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(a / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic_from_profile() if (args.workload == 2 and batch == 1) else None,
+                    "kernel": "%s (%s)" % (kernel, dom_name), "bytes_per_launch": int(gbytes[gi]),
+                    "avg_launch_us": round(us, 3)}
+        # prefill: the decode writes W' once and the GEMM reads it back, so
+        # its bytes are blob + 4 N K + X + Y; past the ridge point the GEMM's
+        # flops bound it instead
+        g_bytes = sum(info[k].blob_bytes + 4 * info[k].rows * info[k].cols + 2 * batch * (info[k].rows + info[k].cols)
+                      for k in groups[gi])
+        g_flops = sum(2.0 * batch * info[k].rows * info[k].cols for k in groups[gi])
+        if g_flops / g_bytes > MFMA_BF16_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+            a = g_flops / (us * 1e-6) / 1e12
+            return {"bound": "mfma", "achieved": round(a, 1), "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(a / MFMA_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": "%s (%s)" % (kernel, dom_name), "flops_per_launch": g_flops,
+                    "avg_launch_us": round(us, 3)}
+        a = g_bytes / (us * 1e-6) / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_from_profile() if (args.workload == 2 and batch == 1) else None,
-                "kernel": "%s (%s)" % (kernel, dom_name), "bytes_per_launch": int(gbytes[gi]),
+                "frac": round(a / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "%s (%s)" % (kernel, dom_name), "bytes_per_launch": int(g_bytes),
                 "avg_launch_us": round(us, 3)}
 
     if args.roofline_only:
@@ -217,21 +246,25 @@ def main():
         print(json.dumps({"roofline": roofline(us), "config": {"workload": wl.name, "batch": batch}}))
         return
 
-    # correctness guard (not timed): one eager step, sampled rows against an
-    # FP64 product of the same BF16 values
+    # correctness guard (not timed): sampled rows of every output against an
+    # FP64 product of the same BF16 values, after one eager step and again
+    # after the timed graph replays
+    def verify(when):
+        for k in keys:
+            rows, wr = check[k]
+            wf = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).double()
+            xf = xs[k].cpu().view(torch.bfloat16).double()                      # [batch, K]
+            ref = (xf @ wf.T).numpy()
+            a = (xf.abs() @ wf.abs().T).numpy()
+            got = ys[k].reshape(batch, -1).cpu().double().numpy()[:, rows]
+            if not np.all(np.abs(got - ref) <= 2.0 ** -10 * a + 2.0 ** -8 * np.abs(ref)):
+                print("bench: %s outside tolerance %s" % (k, when), file=sys.stderr)
+                sys.exit(1)
+
     with torch.cuda.stream(stream):
         step(0)
     torch.cuda.synchronize()
-    for k in keys:
-        rows, wr = check[k]
-        wf = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).double()
-        xf = xs[k].cpu().view(torch.bfloat16).double()                      # [batch, K]
-        ref = (xf @ wf.T).numpy()
-        a = (xf.abs() @ wf.abs().T).numpy()
-        got = ys[k].reshape(batch, -1).cpu().double().numpy()[:, rows]
-        if not np.all(np.abs(got - ref) <= 2.0 ** -10 * a + 2.0 ** -8 * np.abs(ref)):
-            print("bench: %s outside tolerance" % (k,), file=sys.stderr)
-            sys.exit(1)
+    verify("after an eager step")
 
     graphs = None
     if not args.no_graph:
@@ -263,6 +296,7 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_start
     ms_per_step = e0.elapsed_time(e1) / args.steps
+    verify("after the timed steps")
     value = bytes_c / (ms_per_step * 1e-3) / 1e9
     value_u = bytes_u / (ms_per_step * 1e-3) / 1e9
     dom_us = time_dominant()
@@ -356,7 +390,9 @@ def main():
                    "matrices": {m.name: [m.rows, m.cols] for m in wl.matrices}, "batch": batch,
                    "launch_order": groups_named, "launches_per_step": len(groups),
                    "device_copies": copies, "hip_graph": graphs is not None, "output": "bf16",
-                   "encoder": params or "default"},
+                   "encoder": params or "default",
+                   "path": ("fused decode-GEMV" if batch == 1 else "fused skinny decode-GEMM" if batch <= 16
+                            else "decode to BF16 + hipBLASLt GEMM")},
         "compressed_GBps": round(value, 1),
         "uncompressed_equiv_GBps": round(value_u, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),

@@ -81,14 +81,20 @@ _lib.nwc_gemv_batched.argtypes = [_i, ctypes.POINTER(nwc_info), ctypes.POINTER(_
                                   ctypes.POINTER(_vp), _i, _vp, _sz, _vp]
 _lib.nwc_decode_batched.argtypes = [_i, ctypes.POINTER(nwc_info), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                     ctypes.POINTER(_u64), _vp]
+_lib.nwc_blas_create.argtypes = [ctypes.POINTER(_vp)]
+_lib.nwc_blas_destroy.argtypes = [_vp]
+_lib.nwc_prefill_workspace_size.argtypes = [ctypes.POINTER(nwc_info), ctypes.POINTER(_sz)]
+_lib.nwc_gemm_prefill.argtypes = [_vp, ctypes.POINTER(nwc_info), _vp, _vp, _u64, _i, _vp, _u64, _i, _vp, _sz, _vp]
 for _f in ("nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode", "nwc_workspace_size", "nwc_gemv",
-           "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched", "nwc_decode_batched"):
+           "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched", "nwc_decode_batched",
+           "nwc_blas_create", "nwc_blas_destroy", "nwc_prefill_workspace_size", "nwc_gemm_prefill"):
     getattr(_lib, _f).restype = _st
 
 # the exported C symbols, for checks against include/nwc.h
 EXPORTS = ("nwc_status_str", "nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode",
            "nwc_workspace_size", "nwc_gemv", "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16",
-           "nwc_gemv_batched", "nwc_decode_batched")
+           "nwc_gemv_batched", "nwc_decode_batched", "nwc_blas_create", "nwc_blas_destroy",
+           "nwc_prefill_workspace_size", "nwc_gemm_prefill")
 
 
 def _check(st: int, where: str):
@@ -118,10 +124,14 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _dptr(t) -> ctypes.c_void_p:
+def _dptr(t, rows: bool = False) -> ctypes.c_void_p:
+    """Device address of a tensor: contiguous, or with rows=True a 2-D tensor
+    whose rows are contiguous and may sit any stride(0) apart."""
     if hasattr(t, "data_ptr"):
         if not t.is_cuda:
             raise ValueError("expected a device (cuda) tensor")
+        if rows and t.dim() == 2 and t.stride(1) == 1:
+            return ctypes.c_void_p(t.data_ptr())
         if not t.is_contiguous():
             raise ValueError("expected a contiguous tensor")
         return ctypes.c_void_p(t.data_ptr())
@@ -271,9 +281,45 @@ def nwc_gemm_skinny(info: nwc_info, blob_dev, X_dev, Y_dev, ws=None, stream=None
     """Y[b] = W X[b] for X_dev [batch, cols] and Y_dev [batch, rows]."""
     batch = int(X_dev.shape[0])
     wp, wn = _ws(ws)
-    _check(_lib.nwc_gemm_skinny(ctypes.byref(info), _dptr(blob_dev), _dptr(X_dev), int(X_dev.stride(0)), batch,
-                                _dptr(Y_dev), int(Y_dev.stride(0)), _ytype(Y_dev), wp, wn, _stream(stream)),
+    _check(_lib.nwc_gemm_skinny(ctypes.byref(info), _dptr(blob_dev), _dptr(X_dev, rows=True), int(X_dev.stride(0)),
+                                batch, _dptr(Y_dev, rows=True), int(Y_dev.stride(0)), _ytype(Y_dev), wp, wn,
+                                _stream(stream)),
            "nwc_gemm_skinny")
+
+
+class Blas:
+    """Owns an nwc_blas context (a hipBLASLt handle and its algorithm cache)."""
+
+    def __init__(self):
+        h = _vp()
+        _check(_lib.nwc_blas_create(ctypes.byref(h)), "nwc_blas_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            _check(_lib.nwc_blas_destroy(self.handle), "nwc_blas_destroy")
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def nwc_prefill_workspace_size(info: nwc_info) -> int:
+    out = _sz()
+    _check(_lib.nwc_prefill_workspace_size(ctypes.byref(info), ctypes.byref(out)), "nwc_prefill_workspace_size")
+    return out.value
+
+
+def nwc_gemm_prefill(blas: Blas, info: nwc_info, blob_dev, X_dev, Y_dev, ws, stream=None):
+    """Y[b] = W X[b] for any batch: W decoded into ws, then one hipBLASLt GEMM."""
+    batch = int(X_dev.shape[0])
+    _check(_lib.nwc_gemm_prefill(blas.handle, ctypes.byref(info), _dptr(blob_dev), _dptr(X_dev, rows=True),
+                                 int(X_dev.stride(0)), batch, _dptr(Y_dev, rows=True), int(Y_dev.stride(0)),
+                                 _ytype(Y_dev), _dptr(ws),
+                                 int(ws.numel() * ws.element_size()), _stream(stream)), "nwc_gemm_prefill")
 
 
 def nwc_gemv_bf16(w_dev, x_dev, y_dev, ws=None, stream=None):

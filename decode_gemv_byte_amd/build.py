@@ -39,16 +39,18 @@ def _run(cmd):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    for src in ("host_codec.cpp", "kernels.hip"):
+    for src in ("host_codec.cpp", "kernels.hip", "prefill.cpp"):
         obj = os.path.join(BUILD, src + ".o")
-        cmd = [HIPCC] + COMMON + (DEVICE if src.endswith(".hip") else ["-x", "c++"]) + \
+        host = ["-x", "c++", "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__"]  # host code (HIP runtime API only)
+        cmd = [HIPCC] + COMMON + (DEVICE if src.endswith(".hip") else host) + \
               ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd))
         _run(cmd)
         objs.append(obj)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs + ["-lpthread"]
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs + \
+          ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lhipblaslt", "-lpthread"]
     if verbose:
         print(" ".join(cmd))
     _run(cmd)

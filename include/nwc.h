@@ -199,6 +199,35 @@ nwc_status nwc_gemm_skinny(const nwc_info *info, const void *blob_dev, const uin
                            uint64_t ldx, int batch, void *Y_dev, uint64_t ldy,
                            nwc_out_type y_type, void *ws, size_t ws_bytes, void *stream);
 
+/* Prefill-sized batches ("NWC -- Neural Weight Compression", How it works,
+ * bullet "Dequantization and embedding lookup": the batched path
+ * dequantizes and then calls the vendor GEMM): W is decoded into the
+ * workspace (nwc_decode's kernel), then one hipBLASLt GEMM forms
+ * Y[b, n] = sum_k X[b, k] W[n, k] for any batch >= 1, FP32 accumulation,
+ * X (device, batch x cols, row stride ldx % 8 == 0, 16-byte aligned) and Y
+ * (device, batch x rows, row stride ldy, y_type, 16-byte aligned, ldy a
+ * multiple of 16 bytes).  Meant for more X rows than nwc_gemm_skinny takes:
+ * it reads the compressed weights once, writes and reads them back as BF16,
+ * so it saves memory, not time.
+ *  - nwc_blas: an opaque context the caller creates and destroys, holding a
+ *    hipBLASLt handle (whose creation may allocate) and the algorithm picked
+ *    for each problem shape; it may be shared by calls on any stream.
+ *  - ws (256-byte aligned): at least nwc_prefill_workspace_size bytes: the
+ *    decoded W (rows x cols rounded up to 8, BF16), then 32 MiB for
+ *    hipBLASLt.  Calls sharing a workspace must not run concurrently.
+ *  - The result is deterministic for a given context state, library and
+ *    GPU (the vendor GEMM's own summation order).  Async.
+ * Errors: INVALID_ARG, BUFFER_TOO_SMALL, ALIGNMENT, UNSUPPORTED (no GEMM
+ * algorithm for the shape), HIP. */
+typedef struct nwc_blas nwc_blas;
+nwc_status nwc_blas_create(nwc_blas **out);
+nwc_status nwc_blas_destroy(nwc_blas *h);
+nwc_status nwc_prefill_workspace_size(const nwc_info *info, size_t *bytes);
+nwc_status nwc_gemm_prefill(nwc_blas *h, const nwc_info *info, const void *blob_dev,
+                            const uint16_t *X_dev, uint64_t ldx, int batch, void *Y_dev,
+                            uint64_t ldy, nwc_out_type y_type, void *ws, size_t ws_bytes,
+                            void *stream);
+
 /* Uncompressed comparator: the same GEMV on a plain BF16 matrix (device,
  * rows x cols, row stride ld, cols and ld multiples of 8), with the same
  * tiling, work split, loads and summation order as the fused kernel, reading

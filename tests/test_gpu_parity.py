@@ -377,6 +377,64 @@ def test_gemm_deterministic():
     assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
 
 
+# ------------------------------------------- prefill: decode + hipBLASLt ----
+
+_BLAS = []
+
+
+def _blas():
+    if not _BLAS:
+        _BLAS.append(nwc.Blas())
+    return _BLAS[0]
+
+
+def _padded(a: np.ndarray, cols_to: int):
+    """A device copy of a [rows, cols] array whose rows are cols_to elements apart."""
+    out = torch.zeros((a.shape[0], cols_to), dtype=torch.int16, device="cuda")
+    out[:, :a.shape[1]] = dev(a.view(np.int16))
+    return out[:, :a.shape[1]]
+
+
+def _prefill(blob: Blob, X: np.ndarray, out_f32: bool):
+    up8 = lambda v: -(-v // 8) * 8
+    Xd = _padded(X, up8(X.shape[1]))
+    Yfull = torch.full((X.shape[0], up8(blob.info.rows)), float("nan"),
+                       dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+    Y = Yfull[:, :blob.info.rows]
+    ws = torch.empty(nwc.nwc_prefill_workspace_size(blob.info), dtype=torch.uint8, device="cuda")
+    nwc.nwc_gemm_prefill(_blas(), blob.info, blob.dev, Xd, Y, ws)
+    torch.cuda.synchronize()
+    return Y
+
+
+@pytest.mark.parametrize("name,params,batch", [("cfg1", None, 17), ("cfg1", None, 64), ("127x1001", None, 20),
+                                               ("1000x256", dict(tile_rows=16), 33), ("wide_odd", None, 40),
+                                               ("1x1", None, 17), ("cfg1", dict(max_code_len=12), 100)])
+def test_gemm_prefill_small(name, params, batch):
+    w = _special(name)
+    X = workloads.gaussian_bits((batch, w.shape[1]), 1.0, 14)
+    _say("prefill %s %s batch %d %s" % (name, w.shape, batch, params))
+    b = Blob(w, params)
+    Y_ref, A_ref = oracle.gemm(w, X)
+    for out_f32 in (False, True):
+        Y = _to_f64(_prefill(b, X, out_f32))
+        for beta in range(batch):
+            _check_y(Y[beta], Y_ref[beta], A_ref[beta], out_f32, "%s b%d" % (name, beta))
+
+
+@pytest.mark.parametrize("name", ["w_4096x14336", "w_14336x4096"])
+def test_gemm_prefill_workload_sampled(name):
+    w = _w(4, name)
+    X = workloads.activations(4, name, batch=64)
+    _say("prefill workload 4 %s batch 64" % name)
+    b = Blob(w)
+    Y = _to_f64(_prefill(b, X, False))
+    idx = _sample_rows(w.shape[0], 256, seed=64)
+    Y_ref, A_ref = oracle.gemm(np.ascontiguousarray(w[idx]), X)
+    for beta in range(0, 64, 7):
+        _check_y(Y[beta][idx], Y_ref[beta], A_ref[beta], False, "%s b%d" % (name, beta))
+
+
 # ------------------------------------------------------ BF16 comparator ----
 
 @pytest.mark.parametrize("cid,name", [(1, "w"), (2, "q"), (2, "down")])

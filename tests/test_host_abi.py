@@ -260,3 +260,34 @@ def test_device_calls_validate_before_launch():
     assert L.nwc_decode_batched(2, infos, ok, ok, U2(info.cols, info.cols + 4), None) == nwc.NWC_ERR_ALIGNMENT
     assert L.nwc_decode_batched(2, mixed, ok, ok, U2(info.cols, 512), None) == nwc.NWC_ERR_UNSUPPORTED
     assert L.nwc_decode_batched(2, gen, ok, ok, U2(info.cols, 500), None) == nwc.NWC_ERR_UNSUPPORTED
+
+
+def test_prefill_validation():
+    # everything here fails before any device work, so it runs without a GPU
+    L = nwc._lib
+    blob = nwc.nwc_encode(workloads.gaussian_bits((100, 1000), 0.02, 2))
+    info = nwc.nwc_inspect(blob)
+    need = nwc.nwc_prefill_workspace_size(info)
+    assert need == -(-100 * 1000 * 2 // 256) * 256 + (32 << 20)
+    A = 1 << 20  # a 256-byte aligned stand-in address (never dereferenced)
+    h = ctypes.c_void_p(A)
+    ok = ctypes.c_void_p(A)
+    call = lambda h_, batch=20, ldx=1000, ldy=104, X=ok, Y=ok, ws=ok, n=need, yt=0: L.nwc_gemm_prefill(
+        h_, ctypes.byref(info), ok, X, ldx, batch, Y, ldy, yt, ws, n, None)
+    assert call(None) == nwc.NWC_ERR_INVALID_ARG
+    assert call(h, batch=0) == nwc.NWC_ERR_INVALID_ARG
+    assert call(h, ldx=999) == nwc.NWC_ERR_INVALID_ARG
+    assert call(h, ldy=99) == nwc.NWC_ERR_INVALID_ARG
+    assert call(h, yt=7) == nwc.NWC_ERR_INVALID_ARG
+    assert call(h, X=None) == nwc.NWC_ERR_INVALID_ARG
+    assert call(h, n=need - 1) == nwc.NWC_ERR_BUFFER_TOO_SMALL
+    assert call(h, X=ctypes.c_void_p(A + 2)) == nwc.NWC_ERR_ALIGNMENT
+    assert call(h, ws=ctypes.c_void_p(A + 16)) == nwc.NWC_ERR_ALIGNMENT
+    assert call(h, ldx=1004) == nwc.NWC_ERR_ALIGNMENT
+    assert call(h, ldy=100) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_blas_create(None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_blas_destroy(None) == nwc.NWC_ERR_INVALID_ARG
+    with pytest.raises(nwc.NwcError):
+        bad = nwc.nwc_info()
+        nwc.nwc_prefill_workspace_size(bad)
+
