@@ -361,6 +361,40 @@ def main():
                   "bytes_moved": int(moved), "pct_hbm_peak": round(100.0 * moved / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
         del wout, dgraphs, dbatch
 
+    # ------------------------------- embedding lookup from a tied LM head
+    # rows by token id straight from the compressed matrix, against torch's
+    # index_select on the BF16 weights (one launch each, HIP events)
+    gather = None
+    if args.workload == 5:
+        k = keys[0]
+        g_rng = np.random.default_rng(7)
+        gather = {}
+        for n_ids in (1, 16, 256):
+            ids = torch.from_numpy(g_rng.integers(0, info[k].rows, n_ids).astype(np.int32)).to(dev)
+            gout = torch.empty((n_ids, info[k].cols), dtype=torch.int16, device=dev)
+            ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                for i in range(5):
+                    nwc.nwc_gather_rows(info[k], blobs[i % copies][k], ids, gout, stream=stream)
+                ge0.record(stream)
+                for i in range(50):
+                    nwc.nwc_gather_rows(info[k], blobs[i % copies][k], ids, gout, stream=stream)
+                ge1.record(stream)
+            torch.cuda.synchronize()
+            entry = {"us": round(ge0.elapsed_time(ge1) * 1e3 / 50, 3)}
+            if want_bf16:
+                ids64 = ids.long()
+                with torch.cuda.stream(stream):
+                    for i in range(5):
+                        torch.index_select(wbf[k], 0, ids64)
+                    ge0.record(stream)
+                    for i in range(50):
+                        torch.index_select(wbf[k], 0, ids64)
+                    ge1.record(stream)
+                torch.cuda.synchronize()
+                entry["torch_index_select_us"] = round(ge0.elapsed_time(ge1) * 1e3 / 50, 3)
+            gather["rows_%d" % n_ids] = entry
+
     # ------------------------------------------------ plain BF16 comparators
     bf16 = None
     if want_bf16:
@@ -400,6 +434,7 @@ def main():
         "bf16_gemv": bf16,
         "single_launch_all_gemvs": single,
         "standalone_decode": decode,
+        "embedding_gather": gather,
         "roofline": roofline(dom_us),
         "cpu_baseline": cpu,
         "wall_s": round(t_wall, 3),

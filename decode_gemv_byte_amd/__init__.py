@@ -63,6 +63,7 @@ class NwcError(RuntimeError):
 _vp = ctypes.c_void_p
 _sz = ctypes.c_size_t
 _u64 = ctypes.c_uint64
+_u32 = ctypes.c_uint32
 _i = ctypes.c_int
 _st = ctypes.c_int
 
@@ -81,20 +82,22 @@ _lib.nwc_gemv_batched.argtypes = [_i, ctypes.POINTER(nwc_info), ctypes.POINTER(_
                                   ctypes.POINTER(_vp), _i, _vp, _sz, _vp]
 _lib.nwc_decode_batched.argtypes = [_i, ctypes.POINTER(nwc_info), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                     ctypes.POINTER(_u64), _vp]
+_lib.nwc_gather_rows.argtypes = [ctypes.POINTER(nwc_info), _vp, _vp, _u32, _vp, _u64, _vp]
 _lib.nwc_blas_create.argtypes = [ctypes.POINTER(_vp)]
 _lib.nwc_blas_destroy.argtypes = [_vp]
 _lib.nwc_prefill_workspace_size.argtypes = [ctypes.POINTER(nwc_info), ctypes.POINTER(_sz)]
 _lib.nwc_gemm_prefill.argtypes = [_vp, ctypes.POINTER(nwc_info), _vp, _vp, _u64, _i, _vp, _u64, _i, _vp, _sz, _vp]
 for _f in ("nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode", "nwc_workspace_size", "nwc_gemv",
            "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched", "nwc_decode_batched",
-           "nwc_blas_create", "nwc_blas_destroy", "nwc_prefill_workspace_size", "nwc_gemm_prefill"):
+           "nwc_blas_create", "nwc_blas_destroy", "nwc_prefill_workspace_size", "nwc_gemm_prefill",
+           "nwc_gather_rows"):
     getattr(_lib, _f).restype = _st
 
 # the exported C symbols, for checks against include/nwc.h
 EXPORTS = ("nwc_status_str", "nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode",
            "nwc_workspace_size", "nwc_gemv", "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16",
            "nwc_gemv_batched", "nwc_decode_batched", "nwc_blas_create", "nwc_blas_destroy",
-           "nwc_prefill_workspace_size", "nwc_gemm_prefill")
+           "nwc_prefill_workspace_size", "nwc_gemm_prefill", "nwc_gather_rows")
 
 
 def _check(st: int, where: str):
@@ -285,6 +288,14 @@ def nwc_gemm_skinny(info: nwc_info, blob_dev, X_dev, Y_dev, ws=None, stream=None
                                 batch, _dptr(Y_dev, rows=True), int(Y_dev.stride(0)), _ytype(Y_dev), wp, wn,
                                 _stream(stream)),
            "nwc_gemm_skinny")
+
+
+def nwc_gather_rows(info: nwc_info, blob_dev, ids_dev, out_dev, stream=None):
+    """out_dev[i] = W[ids_dev[i]] (exact BF16 bits; ids past the matrix give zeros): ids_dev a device
+    uint32 / int32 vector, out_dev a device [n, cols] int16 or bfloat16 tensor (rows may be strided)."""
+    n = int(ids_dev.numel())
+    _check(_lib.nwc_gather_rows(ctypes.byref(info), _dptr(blob_dev), _dptr(ids_dev), n, _dptr(out_dev, rows=True),
+                                int(out_dev.stride(0)), _stream(stream)), "nwc_gather_rows")
 
 
 class Blas:

@@ -428,6 +428,68 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDe
   }
 }
 
+// Rows of W by index (an embedding lookup from the compressed table of a tied
+// LM head): work item (i, tj) decodes column tile tj of the row block that
+// holds row ids[i], each chunk up to that row (the rows of a chunk follow
+// one another in its code stream), one symbol at a time, and writes that
+// row's columns of the tile to out row i.  Any geometry.  An id past the
+// matrix gives a row of zeros.
+__global__ __launch_bounds__(kGenericWaves * kWave) void k_gather(BlobDev b, const uint32_t* __restrict__ ids,
+                                                                  uint32_t n_ids, uint16_t* __restrict__ out,
+                                                                  uint64_t ld) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* buf = lds + wave * b.buf_words;
+  load_table(tab, b.table);
+  __syncthreads();
+  const uint32_t lane = lane_id();
+  const uint64_t nwaves = static_cast<uint64_t>(gridDim.x) * (blockDim.x / kWave);
+  const uint64_t items = static_cast<uint64_t>(n_ids) * b.n_tc;
+  for (uint64_t it = static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + wave; it < items; it += nwaves) {
+    const uint64_t i = it / b.n_tc, tj = it % b.n_tc;
+    const uint64_t id = uniform(ids[i]);
+    const uint64_t tile_c0 = tj * b.tc, tile_c1 = umin64(b.cols, tile_c0 + b.tc);
+    uint16_t* orow = out + i * ld;
+    if (id >= b.rows) {
+      for (uint64_t k = tile_c0 + lane; k < tile_c1; k += kWave) orow[k] = 0;
+      continue;
+    }
+    const uint64_t ti = id / b.tr;
+    const uint64_t t = ti * b.n_tc + tj;
+    const uint64_t row0 = ti * b.tr;
+    const uint32_t w0 = sload(b.tile_words, t);
+    const uint32_t w1 = sload(b.tile_words, t + 1);
+    const uint32_t a0 = w0 & ~3u;
+    stage_stream(b, a0, stage_blocks(b, a0, w1 < w0 ? w0 : w1), buf);
+    wait_vmem();
+    wave_sync_lds();
+    uint32_t base = 128 + (w0 - a0) * 32;  // start bit of the first chunk of this round
+    for (uint32_t c0i = 0; c0i < b.s; c0i += kWave) {
+      const uint32_t c = c0i + lane;
+      const uint32_t cb = c < b.s ? b.chunk_bits[t * b.s + c] : 0u;
+      const uint32_t excl = wave_excl_scan(cb);
+      const uint32_t bit = base + excl;
+      base += __builtin_amdgcn_readlane(excl + cb, kWave - 1);
+      if (c < b.s) {
+        const uint64_t cc0 = tile_c0 + static_cast<uint64_t>(c) * b.v;
+        if (cc0 < tile_c1) {
+          const uint64_t cc1 = umin64(tile_c1, cc0 + b.v);
+          Bits br;
+          br.init(buf, bit);
+          for (uint64_t n = (id - row0) * (cc1 - cc0); n > 0; n--) br.one(tab);  // the rows before it
+          for (uint64_t k = cc0; k < cc1; k++) {
+            const uint32_t e = br.one(tab);
+            const uint32_t rb = b.raw[id * b.raw_ld + k];
+            orow[k] = static_cast<uint16_t>(((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu));
+          }
+        }
+      }
+    }
+    wave_sync_lds();
+  }
+}
+
 // -------------------------------------------------------------------- GEMV
 
 // One matrix of a fused batch-1 launch.  Its tiles, numbered row block by row
@@ -1562,6 +1624,23 @@ nwc_status nwc_decode(const nwc_info* info, const void* blob_dev, uint16_t* w_de
     if (set_lds(k_decode_generic, lds) != hipSuccess) return NWC_ERR_HIP;
     k_decode_generic<<<grid, threads, lds, s>>>(L.b, w_dev, ld);
   }
+  return launched();
+}
+
+nwc_status nwc_gather_rows(const nwc_info* info, const void* blob_dev, const uint32_t* ids_dev, uint32_t n_ids,
+                           uint16_t* out_dev, uint64_t ld, void* stream) {
+  if (!ids_dev || !out_dev || n_ids == 0) return NWC_ERR_INVALID_ARG;
+  Launch L;
+  nwc_status st = prepare(info, blob_dev, &L);
+  if (st) return st;
+  if (ld < L.b.cols) return NWC_ERR_INVALID_ARG;
+  if (!aligned(out_dev, 2) || !aligned(ids_dev, 4)) return NWC_ERR_ALIGNMENT;
+  const size_t lds = (static_cast<size_t>(kGenericWaves) * L.b.buf_words) * 4;
+  if (lds > kMaxLds) return NWC_ERR_UNSUPPORTED;
+  const uint64_t items = static_cast<uint64_t>(n_ids) * L.b.n_tc;
+  const unsigned grid = static_cast<unsigned>(std::min<uint64_t>((items + kGenericWaves - 1) / kGenericWaves, kCUs * 8));
+  if (set_lds(k_gather, lds) != hipSuccess) return NWC_ERR_HIP;
+  k_gather<<<grid, kGenericWaves * kWave, lds, static_cast<hipStream_t>(stream)>>>(L.b, ids_dev, n_ids, out_dev, ld);
   return launched();
 }
 

@@ -191,6 +191,19 @@ nwc_status nwc_gemv_batched(int count, const nwc_info *infos, const void *const 
 nwc_status nwc_decode_batched(int count, const nwc_info *infos, const void *const *blobs_dev,
                               uint16_t *const *w_dev, const uint64_t *ld, void *stream);
 
+/* Rows of W by index ("NWC -- Neural Weight Compression", How it works,
+ * bullet "Dequantization and embedding lookup": the same decoder serves the
+ * embedding lookup, so a tied LM head's compressed matrix is also the
+ * embedding table): out row i (device, row stride ld >= cols elements) gets
+ * the exact BF16 bits of W row ids_dev[i] (device, n_ids uint32 ids).  An id
+ * >= rows gives a row of zeros (ids live on the device, so they are not
+ * checked on the host).  Each row costs the decode of its row block's
+ * chunks up to it (chunks are coded row after row).  Any geometry.  Async.
+ * Errors: INVALID_ARG, ALIGNMENT (out_dev not 2-byte or ids_dev not 4-byte
+ * aligned), UNSUPPORTED, HIP. */
+nwc_status nwc_gather_rows(const nwc_info *info, const void *blob_dev, const uint32_t *ids_dev,
+                           uint32_t n_ids, uint16_t *out_dev, uint64_t ld, void *stream);
+
 /* Skinny decode-GEMM for batch 2..16: Y[b, n] = sum_k X[b, k] W[n, k] with X
  * (device, batch x cols, row stride ldx) and Y (device, batch x rows, row
  * stride ldy, y_type).  Same decode as nwc_gemv; FP32 accumulation.  Async.

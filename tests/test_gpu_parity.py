@@ -377,6 +377,46 @@ def test_gemm_deterministic():
     assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
 
 
+# ----------------------------------------------------------- row gather ----
+
+@pytest.mark.parametrize("name,params", [("cfg1", None), ("127x1001", None), ("all_patterns", None),
+                                         ("cfg1", dict(tile_rows=16)), ("1000x256", dict(tile_rows=32)),
+                                         ("cfg1", dict(max_code_len=12)), ("1x1", None),
+                                         ("wide_odd", dict(tile_rows=3, tile_cols=7, chunks_per_tile=7,
+                                                           max_code_len=10))])
+def test_gather_rows_bit_exact(name, params):
+    # rows by index, the first and last among them, repeats, and ids past
+    # the matrix (a row of zeros)
+    w = _special(name)
+    rng = np.random.default_rng(21)
+    ids = np.concatenate([[0, w.shape[0] - 1], rng.integers(0, w.shape[0], 40), [w.shape[0] // 2] * 3,
+                          [w.shape[0], 2 ** 32 - 1]]).astype(np.uint32)
+    _say("gather %s %s %s" % (name, w.shape, params))
+    b = Blob(w, params)
+    ld = -(-w.shape[1] // 8) * 8 + 8
+    out = torch.full((len(ids), ld), 0x7E7E, dtype=torch.int16, device="cuda")
+    nwc.nwc_gather_rows(b.info, b.dev, dev(ids.view(np.int32)), out[:, :w.shape[1]])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    want = np.zeros((len(ids), w.shape[1]), np.uint16)
+    ok = ids < w.shape[0]
+    want[ok] = w[ids[ok]]
+    assert np.array_equal(got[:, :w.shape[1]], want)
+    assert np.all(got[:, w.shape[1]:] == 0x7E7E)  # nothing written past a row
+
+
+def test_gather_rows_lm_head():
+    # the tied LM head's compressed matrix as the embedding table: 16 tokens
+    w = _w(5, "lm_head")
+    ids = np.random.default_rng(3).integers(0, w.shape[0], 16).astype(np.uint32)
+    b = Blob(w)
+    out = torch.empty((16, w.shape[1]), dtype=torch.int16, device="cuda")
+    _say("gather lm_head 16 rows")
+    nwc.nwc_gather_rows(b.info, b.dev, dev(ids.view(np.int32)), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), w[ids])
+
+
 # ------------------------------------------- prefill: decode + hipBLASLt ----
 
 _BLAS = []

@@ -291,3 +291,19 @@ def test_prefill_validation():
         bad = nwc.nwc_info()
         nwc.nwc_prefill_workspace_size(bad)
 
+
+def test_gather_validation():
+    L = nwc._lib
+    blob = nwc.nwc_encode(workloads.gaussian_bits((64, 512), 0.02, 2))
+    info = nwc.nwc_inspect(blob)
+    A = 1 << 20
+    ok = ctypes.c_void_p(A)
+    call = lambda ids=ok, n=4, out=ok, ld=512: L.nwc_gather_rows(ctypes.byref(info), ok, ids, n, out, ld, None)
+    assert call(ids=None) == nwc.NWC_ERR_INVALID_ARG
+    assert call(out=None) == nwc.NWC_ERR_INVALID_ARG
+    assert call(n=0) == nwc.NWC_ERR_INVALID_ARG
+    assert call(ld=511) == nwc.NWC_ERR_INVALID_ARG
+    assert call(out=ctypes.c_void_p(A + 1)) == nwc.NWC_ERR_ALIGNMENT
+    assert call(ids=ctypes.c_void_p(A + 2)) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gather_rows(ctypes.byref(info), ctypes.c_void_p(A + 8), ok, 4, ok, 512, None) == nwc.NWC_ERR_ALIGNMENT
+
