@@ -1259,7 +1259,7 @@ constexpr int kCUs = 256;
 
 struct Launch {
   BlobDev b;
-  bool fast;  // S = 64, V = 8, TR in {8, 16, 32}, K % 8 == 0
+  bool fast;  // S = 64, V = 8, TR in {4, 8, 16, 32}, K % 8 == 0
   uint32_t max_chunk_bits;
 };
 
@@ -1292,7 +1292,7 @@ nwc_status prepare(const nwc_info* info, const void* blob_dev, Launch* L) {
   // 4-word block plus the bit reader's two words of look-ahead (in 16-byte
   // pieces), and 4 spare words that the reader may fetch past the end
   b.buf_words = 4 + ((info->max_tile_words + 3 + 2 + 3) / 4) * 4 + 4;
-  L->fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
+  L->fast = g.s == 64 && g.v == 8 && (g.tr == 4 || g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
   return NWC_OK;
 }
 
@@ -1588,7 +1588,7 @@ nwc_status nwc_inspect(const void* blob, size_t bytes, nwc_info* info) { return 
 nwc_status nwc_workspace_size(const nwc_info* info, int batch, size_t* bytes) {
   nwc::Geometry g;
   if (!info || !bytes || batch < 1 || batch > 16 || !nwc::info_geometry(info, &g)) return NWC_ERR_INVALID_ARG;
-  const bool fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
+  const bool fast = g.s == 64 && g.v == 8 && (g.tr == 4 || g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
   if (fast && batch == 1)
     *bytes = fused_ws_bytes(g);
   else if (skinny_fits(g, batch))
@@ -1616,6 +1616,7 @@ nwc_status nwc_decode(const nwc_info* info, const void* blob_dev, uint16_t* w_de
     const uint16_t* none = nullptr;
     void* out = w_dev;
     switch (L.b.tr) {
+      case 4: return launch_gemv<4, 16, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
       case 8: return launch_gemv<8, 16, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
       case 16: return launch_gemv<16, 8, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
       default: return launch_gemv<32, 4, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
@@ -1667,6 +1668,7 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
     void* yy = Y;
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     switch (L.b.tr) {
+      case 4: return launch_gemv<4, 16, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
       case 8: return launch_gemv<8, 16, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
       case 16: return launch_gemv<16, 8, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
       default: return launch_gemv<32, 4, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
@@ -1739,6 +1741,7 @@ nwc_status nwc_gemv_batched(int count, const nwc_info* infos, const void* const*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int y_f32 = y_type == NWC_OUT_F32 ? 1 : 0;
   switch (L[0].b.tr) {
+    case 4: return launch_gemv<4, 16, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
     case 8: return launch_gemv<8, 16, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
     case 16: return launch_gemv<16, 8, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
     default: return launch_gemv<32, 4, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
@@ -1762,6 +1765,7 @@ nwc_status nwc_decode_batched(int count, const nwc_info* infos, const void* cons
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (L[0].b.tr) {
+    case 4: return launch_gemv<4, 16, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
     case 8: return launch_gemv<8, 16, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
     case 16: return launch_gemv<16, 8, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
     default: return launch_gemv<32, 4, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);

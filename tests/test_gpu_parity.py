@@ -105,7 +105,8 @@ DECODE_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=16)), ("cfg1", dict(tile
                 ("all_patterns", None), ("127x1001", None), ("1x1", None), ("1000x256", None),
                 ("nan_payloads", None), ("subnormal", None), ("one_symbol", None), ("random_bits", None),
                 ("wide_odd", None), ("wide_odd", dict(tile_rows=3, tile_cols=7, chunks_per_tile=7, max_code_len=10)),
-                ("cfg1", dict(max_code_len=12)), ("all_patterns", dict(max_code_len=12))]
+                ("cfg1", dict(max_code_len=12)), ("all_patterns", dict(max_code_len=12)),
+                ("cfg1", dict(tile_rows=4)), ("1000x256", dict(tile_rows=4))]
 
 
 @pytest.mark.parametrize("name,params", DECODE_CASES)
@@ -171,7 +172,8 @@ GEMV_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=16)), ("cfg1", dict(tile_r
               ("127x1001", None), ("1x1", None), ("1000x256", None), ("subnormal", None),
               ("one_symbol", None), ("wide_odd", None), ("8x512", None), ("3000x512", None),
               ("20x40960", None), ("20x40960", dict(tile_rows=16)),
-              ("cfg1", dict(max_code_len=12)), ("3000x512", dict(max_code_len=12))]
+              ("cfg1", dict(max_code_len=12)), ("3000x512", dict(max_code_len=12)),
+              ("cfg1", dict(tile_rows=4)), ("3000x512", dict(tile_rows=4)), ("20x40960", dict(tile_rows=4))]
 
 
 @pytest.mark.parametrize("out_f32", [False, True])
