@@ -477,6 +477,49 @@ def test_gemm_prefill_workload_sampled(name):
         _check_y(Y[beta][idx], Y_ref[beta], A_ref[beta], False, "%s b%d" % (name, beta))
 
 
+# ------------------------------------------------------- torch module ----
+
+@pytest.mark.parametrize("shape,bias", [((256, 512), True), ((1000, 256), False), ((37, 104), True)])
+def test_nwclinear_matches_dense_layer(shape, bias):
+    from decode_gemv_byte_amd.linear import NWCLinear
+    out_f, in_f = shape
+    torch.manual_seed(0)
+    lin = torch.nn.Linear(in_f, out_f, bias=bias).to(torch.bfloat16)
+    m = NWCLinear.from_linear(lin)
+    w = lin.weight.detach().view(torch.int16).numpy().view(np.uint16)
+    assert torch.equal(m.dense_weight().cpu().view(torch.int16), lin.weight.detach().view(torch.int16))
+    for batch in (1, 3, 16, 40):
+        _say("NWCLinear %s batch %d" % (shape, batch))
+        x = workloads.gaussian_bits((batch, in_f), 1.0, 30 + batch)
+        y = m(torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16).reshape(batch, 1, in_f))
+        assert y.shape == (batch, 1, out_f) and y.dtype == torch.bfloat16
+        p_ref, a_ref = oracle.gemm(w, x)
+        got = _to_f64(y.reshape(batch, out_f))
+        y_ref = p_ref
+        if bias:
+            # the bias is added to the BF16-rounded product: besides the
+            # output rounding, one more rounding of 2^-8 |W x| (passed as
+            # 4 |W x| in the 2^-10 term)
+            y_ref = p_ref + lin.bias.detach().float().numpy().astype(np.float64)
+            a_ref = a_ref + 4.0 * np.abs(p_ref)
+        for beta in range(batch):
+            _check_y(got[beta], y_ref[beta], a_ref[beta], False, "%s b%d" % (shape, beta))
+
+
+def test_convert_replaces_every_linear():
+    from decode_gemv_byte_amd.linear import NWCLinear, convert
+    torch.manual_seed(1)
+    net = torch.nn.Sequential(torch.nn.Linear(512, 256), torch.nn.SiLU(),
+                              torch.nn.Sequential(torch.nn.Linear(256, 128, bias=False))).to(torch.bfloat16)
+    x = torch.randn(5, 512).to(torch.bfloat16)
+    ref = net(x).float()
+    convert(net)
+    assert isinstance(net[0], NWCLinear) and isinstance(net[2][0], NWCLinear)
+    _say("convert: 2-layer net")
+    got = net(x.cuda()).float().cpu()
+    assert torch.allclose(got, ref, rtol=0.05, atol=0.05)
+
+
 # ------------------------------------------------------ BF16 comparator ----
 
 @pytest.mark.parametrize("cid,name", [(1, "w"), (2, "q"), (2, "down")])
