@@ -28,6 +28,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -61,9 +62,156 @@ def parse():
     ap.add_argument("--skip-bf16", action="store_true", help="skip the plain-BF16 comparators")
     ap.add_argument("--tile-rows", type=int, default=0, help="encoder tile rows (0 = library default)")
     ap.add_argument("--max-code-len", type=int, default=0, help="encoder code length limit (0 = library default)")
+    ap.add_argument("--model-step", type=int, default=0, metavar="LAYERS",
+                    help="only time a whole decode step (tokens/s) through a Qwen3-4B-shaped stack of LAYERS "
+                         "layers on synthetic weights, compressed vs dense BF16")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB, 5 times (scales HBM byte counters)")
     return ap.parse_args()
+
+
+def model_step(args):
+    """One generated token through a Qwen3-4B-shaped decoder stack (hidden 2560,
+    32 query / 8 key-value heads of 128, MLP 9728): per layer RMSNorm, q/k/v in
+    one batched fused launch, attention over a fixed synthetic BF16 KV cache
+    of 512 positions (torch products), o, residual, RMSNorm, gate/up in
+    one launch, SiLU * up, down, residual.  The projections run compressed
+    (nwc_gemv_batched / nwc_gemv) or, for comparison, as torch.mv on the
+    same BF16 weights; everything else is the same torch code.  Weights are
+    the qwen3_4b_layer matrices, one device copy per layer (so every layer streams
+    from HBM); the KV cache is random and not appended to.  The step is
+    captured as one HIP graph.  Reports tokens/s (= steps/s, batch 1)."""
+    import torch
+    import torch.nn.functional as F
+
+    import decode_gemv_byte_amd as nwc
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    L, CTX, H, HQ, HKV, D = args.model_step, 512, 2560, 32, 8, 128
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    w = {n: workloads.weights(2, n) for n in names}
+    blob = {n: nwc.nwc_encode(w[n]) for n in names}
+    info = {n: nwc.nwc_inspect(blob[n]) for n in names}
+    lay = []
+    for l in range(L):
+        d = {n: torch.from_numpy(blob[n]).to(dev) for n in names}
+        d.update({"w_" + n: torch.from_numpy(w[n].view(np.int16)).to(dev).view(torch.bfloat16) for n in names})
+        lay.append(d)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    # KV cache in BF16 as a server keeps it: K^T [kv head, dim, position] with
+    # the 1/sqrt(head dim) score scale folded in, V [kv head, position, dim]
+    kt = [(torch.randn(HKV, D, CTX, generator=g) / math.sqrt(D)).to(torch.bfloat16).to(dev).contiguous()
+          for _ in range(L)]
+    vv = [torch.randn(HKV, CTX, D, generator=g).to(torch.bfloat16).to(dev).contiguous() for _ in range(L)]
+    x0 = torch.randn(H, generator=g).to(dev).to(torch.bfloat16)
+    bufs = {n: torch.empty(info[n].rows, dtype=torch.bfloat16, device=dev) for n in names}
+    ws_qkv = torch.zeros(nwc.gemv_batched_workspace_size([info[n] for n in ("q", "k", "v")]), dtype=torch.uint8, device=dev)
+    ws_gu = torch.zeros(nwc.gemv_batched_workspace_size([info["gate"], info["up"]]), dtype=torch.uint8, device=dev)
+    ws_o = torch.zeros(nwc.nwc_workspace_size(info["o"], 1), dtype=torch.uint8, device=dev)
+    ws_d = torch.zeros(nwc.nwc_workspace_size(info["down"], 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    act = torch.empty(9728, dtype=torch.bfloat16, device=dev)
+    x = x0.clone()
+    keep = []   # marshalled launch arguments referenced by the captured graph
+
+    def attention(l):
+        # one query token against the cache, 4 query heads per KV head; BF16
+        # operands (all contiguous), FP32 accumulation inside the products
+        q = bufs["q"].view(HKV, HQ // HKV, D)
+        p_ = torch.softmax(torch.matmul(q, kt[l]), dim=-1)               # [8, 4, CTX]
+        return torch.matmul(p_, vv[l]).view(-1)                          # [4096]
+
+    def step(dense):
+        for l in range(L):
+            d = lay[l]
+            h = F.rms_norm(x, (H,), eps=1e-6)
+            if dense:
+                for n in ("q", "k", "v"):
+                    torch.mv(d["w_" + n], h, out=bufs[n])
+            else:
+                b = nwc.GemvBatch([info[n] for n in ("q", "k", "v")], [d[n] for n in ("q", "k", "v")], [h, h, h],
+                                  [bufs["q"], bufs["k"], bufs["v"]], ws_qkv)
+                keep.append(b)
+                nwc.nwc_gemv_batched(b, stream=stream)
+            att = attention(l)
+            if dense:
+                torch.mv(d["w_o"], att, out=bufs["o"])
+            else:
+                keep.append(att)
+                nwc.nwc_gemv(info["o"], d["o"], att, bufs["o"], ws_o, stream=stream)
+            x.add_(bufs["o"])
+            h = F.rms_norm(x, (H,), eps=1e-6)
+            if dense:
+                torch.mv(d["w_gate"], h, out=bufs["gate"])
+                torch.mv(d["w_up"], h, out=bufs["up"])
+            else:
+                b = nwc.GemvBatch([info["gate"], info["up"]], [d["gate"], d["up"]], [h, h],
+                                  [bufs["gate"], bufs["up"]], ws_gu)
+                keep.append(b)
+                nwc.nwc_gemv_batched(b, stream=stream)
+            torch.mul(F.silu(bufs["gate"]), bufs["up"], out=act)
+            if dense:
+                torch.mv(d["w_down"], act, out=bufs["down"])
+            else:
+                nwc.nwc_gemv(info["down"], d["down"], act, bufs["down"], ws_d, stream=stream)
+            x.add_(bufs["down"])
+
+    res = {}
+    outs = {}
+    replays_match = {}
+    for dense in (False, True):
+        with torch.cuda.stream(stream):
+            x.copy_(x0)
+            step(dense)   # eager once (also fixes the workspaces' state)
+        torch.cuda.synchronize()
+        eager = x.float().cpu().clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step(dense)
+        with torch.cuda.stream(stream):
+            x.copy_(x0)
+            graph.replay()
+        torch.cuda.synchronize()
+        outs[dense] = x.float().cpu().clone()
+        for i in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(args.steps):
+                graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        res[dense] = e0.elapsed_time(e1) / args.steps
+        # a replay after many others still gives the eager step's bits
+        with torch.cuda.stream(stream):
+            x.copy_(x0)
+            graph.replay()
+        torch.cuda.synchronize()
+        replays_match[dense] = bool(torch.equal(eager, outs[dense]) and torch.equal(eager, x.float().cpu()))
+        del graph
+    # the two stacks run the same arithmetic up to rounding of the products:
+    # after L layers the hidden states still agree closely
+    rel = float((outs[False] - outs[True]).norm() / outs[True].norm())
+    comp = sum(b.size for b in blob.values()) * L
+    dense_bytes = sum(2 * w[n].size for n in names) * L
+    line = {
+        "metric": "decode step tokens/s, batch 1 (Qwen3-4B-shaped stack, synthetic weights)",
+        "value": round(1e3 / res[False], 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(res[False], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3_4b_stack", "layers": L, "context": CTX, "batch": 1, "hip_graph": True,
+                   "weights": "qwen3_4b_layer matrices, one device copy per layer"},
+        "dense_bf16_torch_mv": {"tokens_per_s": round(1e3 / res[True], 2), "ms_per_step": round(res[True], 4)},
+        "speedup_vs_dense": round(res[True] / res[False], 3),
+        "weight_bytes": {"compressed": int(comp), "bf16": int(dense_bytes)},
+        "final_hidden_rel_diff_vs_dense": round(rel, 5),
+        "graph_replays_match_eager": {"compressed": replays_match[False], "dense": replays_match[True]}}
+    print(json.dumps(line))
+    return line
 
 
 def copy_calibration(mib):
@@ -102,6 +250,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.model_step:
+        model_step(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
