@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--skip-bf16", action="store_true", help="skip the plain-BF16 comparators")
     ap.add_argument("--tile-rows", type=int, default=0, help="encoder tile rows (0 = library default)")
     ap.add_argument("--max-code-len", type=int, default=0, help="encoder code length limit (0 = library default)")
+    ap.add_argument("--geometry", choices=("default", "tuned"), default="default",
+                    help="tuned: time every candidate tile geometry per launch group on this GPU first "
+                         "(decode_gemv_byte_amd.tune) and encode each group with the fastest")
     ap.add_argument("--model-step", type=int, default=0, metavar="LAYERS",
                     help="only time a whole decode step (tokens/s) through a Qwen3-4B-shaped stack of LAYERS "
                          "layers on synthetic weights, compressed vs dense BF16")
@@ -272,6 +275,20 @@ def main():
         sys.exit("batch must be 1..8192 (above 16: decode + hipBLASLt GEMM)")
     params = {k: v for k, v in (("tile_rows", args.tile_rows), ("max_code_len", args.max_code_len)) if v}
     groups_named = [list(g) for g in wl.groups] if wl.groups else [[m.name] for m in wl.matrices]
+    tuned, enc_params = None, {m.name: params or None for m in wl.matrices}
+    if args.geometry == "tuned":
+        if params:
+            sys.exit("--geometry tuned chooses the tile rows and length limit itself")
+        if batch > 16:
+            sys.exit("--geometry tuned covers the fused paths (batch 1..16)")
+        from decode_gemv_byte_amd import tune
+        tuned = {}
+        for g in groups_named:   # layer 0's matrices stand for every layer of the same shape
+            r = tune.tune_geometry([workloads.weights(wl.cid, n) for n in g], batch=batch)
+            tuned["+".join(g)] = r.as_dict()
+            for n in g:
+                enc_params[n] = r.params()
+            print("[tune] %s: %s" % ("+".join(g), r.as_dict()), file=sys.stderr, flush=True)
     # the step: every layer's groups in order; a key is (layer, matrix name)
     groups = [[(l, n) for n in g] for l in range(wl.layers) for g in groups_named]
     keys = [k for g in groups for k in g]
@@ -283,7 +300,7 @@ def main():
     host_blob, info, check, wbf = {}, {}, {}, {}
     for (l, n) in keys:
         w = workloads.weights(wl.cid, n, layer=l)
-        blob = nwc.nwc_encode(w, params or None)
+        blob = nwc.nwc_encode(w, enc_params[n])
         host_blob[(l, n)] = blob
         info[(l, n)] = nwc.nwc_inspect(blob)
         rows = np.unique(np.concatenate([rng.choice(w.shape[0], min(CHECK_ROWS, w.shape[0]), replace=False),
@@ -453,9 +470,10 @@ def main():
     dom_us = time_dominant()
 
     # every GEMV of a one-layer batch-1 step in a single launch (they read
-    # independent activations here): what the launch boundaries cost
+    # independent activations here): what the launch boundaries cost (one
+    # launch takes one tile height)
     single = None
-    if batch == 1 and wl.layers == 1 and len(groups) > 1:
+    if batch == 1 and wl.layers == 1 and len(groups) > 1 and len({info[k].tile_rows for k in keys}) == 1:
         iws = zeroed(nwc.gemv_batched_workspace_size([info[k] for k in keys]))
         allb = [nwc.GemvBatch([info[k] for k in keys], [blobs[c][k] for k in keys], [xs[k][0] for k in keys],
                               [ys[k] for k in keys], iws) for c in range(copies)]
@@ -575,7 +593,7 @@ def main():
                    "matrices": {m.name: [m.rows, m.cols] for m in wl.matrices}, "batch": batch,
                    "launch_order": groups_named, "launches_per_step": len(groups),
                    "device_copies": copies, "hip_graph": graphs is not None, "output": "bf16",
-                   "encoder": params or "default",
+                   "encoder": ({"tuned": tuned} if tuned else params or "default"),
                    "path": ("fused decode-GEMV" if batch == 1 else "fused skinny decode-GEMM" if batch <= 16
                             else "decode to BF16 + hipBLASLt GEMM")},
         "compressed_GBps": round(value, 1),

@@ -22,6 +22,18 @@ if not os.path.exists(LIB_PATH):
     raise ImportError("libnwc.so is not built; run `python decode_gemv_byte_amd/build.py` "
                       "(or __graft_entry__.build())")
 
+# The binding hands torch tensors' device memory and streams to the library,
+# so both must run on one HIP runtime.  PyTorch ships its own copy of it;
+# with torch loaded first, the library's dependency on the runtime's soname
+# resolves to that copy.  Loaded the other way round, the library would map
+# the ROCm install's runtime and torch would then map its own beside it: two
+# runtimes (and two HSA runtimes) in one process, under which torch's
+# streams and allocations are foreign handles and launches fail.
+try:
+    import torch  # noqa: F401
+except ImportError:   # a torch-free caller of the C ABI: the ROCm install's runtime
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 NWC_OK = 0

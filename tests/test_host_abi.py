@@ -3,6 +3,7 @@ the oracle, blob validation, and argument checks that must fail before any
 device work."""
 import ctypes
 import os
+import sys
 import re
 import subprocess
 
@@ -307,3 +308,17 @@ def test_gather_validation():
     assert call(ids=ctypes.c_void_p(A + 2)) == nwc.NWC_ERR_ALIGNMENT
     assert L.nwc_gather_rows(ctypes.byref(info), ctypes.c_void_p(A + 8), ok, 4, ok, 512, None) == nwc.NWC_ERR_ALIGNMENT
 
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    # importing the package before torch must not map a second HIP (or HSA)
+    # runtime beside torch's own copy
+    code = ("import decode_gemv_byte_amd, torch\n"
+            "m = open('/proc/self/maps').read().splitlines()\n"
+            "print(sorted({l.split()[-1] for l in m if 'libamdhip64' in l}))\n"
+            "print(sorted({l.split()[-1] for l in m if 'libhsa-runtime64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr
+    hip, hsa = [eval(l) for l in out.stdout.strip().splitlines()[-2:]]
+    assert len(hip) == 1 and len(hsa) == 1, (hip, hsa)
