@@ -40,6 +40,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <tuple>
 
 #include "nwc_internal.hpp"
 
@@ -1316,9 +1317,22 @@ hipError_t set_lds(K kernel, size_t lds) {
                              static_cast<int>(lds));
 }
 
-nwc_status launched() {
-  const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? NWC_OK : NWC_ERR_HIP;
+// Launch a kernel and report that launch's own status (hipLaunchKernel
+// returns it; the triple-chevron form would leave it in the process-wide
+// last-error slot, where another library's error could be read as ours).
+// The arguments are converted to the kernel's parameter types first.
+template <typename... P, typename... A>
+nwc_status launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count");
+  std::tuple<P...> args{static_cast<P>(a)...};
+  void* argv[sizeof...(P)];
+  std::apply([&](auto&... e) {
+    int i = 0;
+    ((argv[i++] = static_cast<void*>(&e)), ...);
+  }, args);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, s) == hipSuccess
+             ? NWC_OK
+             : NWC_ERR_HIP;
 }
 
 // grid for a persistent loop over `items` work items of `waves` wavefronts
@@ -1538,8 +1552,7 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   g.batch = static_cast<uint32_t>(batch);
   const size_t lds = nw * per_wave + best.group_lds(sums);
   if (set_lds(k_gemv<TR, MAXW, NB>, lds) != hipSuccess) return NWC_ERR_HIP;
-  k_gemv<TR, MAXW, NB><<<groups, nw * kWave, lds, s>>>(g);
-  return launched();
+  return launch(k_gemv<TR, MAXW, NB>, dim3(groups), dim3(nw * kWave), lds, s, g);
 }
 
 // Whether a blob and batch take the skinny mode of the fused kernel (no
@@ -1623,9 +1636,8 @@ nwc_status nwc_decode(const nwc_info* info, const void* blob_dev, uint16_t* w_de
     }
   } else {
     if (set_lds(k_decode_generic, lds) != hipSuccess) return NWC_ERR_HIP;
-    k_decode_generic<<<grid, threads, lds, s>>>(L.b, w_dev, ld);
+    return launch(k_decode_generic, dim3(grid), dim3(threads), lds, s, L.b, w_dev, ld);
   }
-  return launched();
 }
 
 nwc_status nwc_gather_rows(const nwc_info* info, const void* blob_dev, const uint32_t* ids_dev, uint32_t n_ids,
@@ -1641,8 +1653,8 @@ nwc_status nwc_gather_rows(const nwc_info* info, const void* blob_dev, const uin
   const uint64_t items = static_cast<uint64_t>(n_ids) * L.b.n_tc;
   const unsigned grid = static_cast<unsigned>(std::min<uint64_t>((items + kGenericWaves - 1) / kGenericWaves, kCUs * 8));
   if (set_lds(k_gather, lds) != hipSuccess) return NWC_ERR_HIP;
-  k_gather<<<grid, kGenericWaves * kWave, lds, static_cast<hipStream_t>(stream)>>>(L.b, ids_dev, n_ids, out_dev, ld);
-  return launched();
+  return launch(k_gather, dim3(grid), dim3(kGenericWaves * kWave), lds, static_cast<hipStream_t>(stream), L.b, ids_dev,
+                n_ids, out_dev, ld);
 }
 
 static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const uint16_t* X, uint64_t ldx, int batch,
@@ -1703,13 +1715,12 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
   float* part = static_cast<float*>(ws);
   const uint64_t blocks = (L.b.n_tiles + kGenericWaves - 1) / kGenericWaves;
   const unsigned grid = static_cast<unsigned>(std::min<uint64_t>(blocks, kCUs * 8));
-  k_gemv_generic<<<grid, kGenericWaves * kWave, lds, s>>>(L.b, X, batch == 1 ? 0 : ldx, batch, part);
-  st = launched();
+  st = launch(k_gemv_generic, dim3(grid), dim3(kGenericWaves * kWave), lds, s, L.b, X, batch == 1 ? 0 : ldx, batch,
+              part);
   if (st) return st;
   const uint64_t n = L.b.rows * static_cast<uint64_t>(batch);
-  k_reduce<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(part, L.b.rows, L.b.n_tc, batch, Y,
-                                                                   batch == 1 ? 0 : ldy, y_f32);
-  return launched();
+  return launch(k_reduce, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, part, L.b.rows, L.b.n_tc,
+                batch, Y, batch == 1 ? 0 : ldy, y_f32);
 }
 
 nwc_status nwc_gemv(const nwc_info* info, const void* blob_dev, const uint16_t* x_dev, void* y_dev,
@@ -1796,9 +1807,8 @@ nwc_status nwc_gemv_bf16(const uint16_t* w_dev, uint64_t rows, uint64_t cols, ui
   const uint32_t n_tc = static_cast<uint32_t>((cols + 511) / 512);
   const uint64_t n_tr = (rows + 15) / 16;
   const Split sp = make_split(n_tr, n_tc, kMaxWaves);
-  k_gemv_bf16<16><<<grid_for(sp.items, sp.waves, 4096), sp.waves * kWave, 0, s>>>(
-      w_dev, rows, cols, ld, n_tc, n_tr, sp, x_dev, y_dev, y_type == NWC_OUT_F32 ? 1 : 0);
-  return launched();
+  return launch(k_gemv_bf16<16>, dim3(grid_for(sp.items, sp.waves, 4096)), dim3(sp.waves * kWave), 0, s, w_dev, rows,
+                cols, ld, n_tc, n_tr, sp, x_dev, y_dev, y_type == NWC_OUT_F32 ? 1 : 0);
 }
 
 }  // extern "C"
