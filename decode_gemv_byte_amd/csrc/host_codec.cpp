@@ -194,7 +194,7 @@ bool params_resolve(const nwc_params* p, Geometry* g) {
   g->s = (p && p->chunks_per_tile) ? p->chunks_per_tile : 64;
   g->lmax = (p && p->max_code_len) ? p->max_code_len : 8;
   if (g->tc % g->s) return false;
-  if (g->lmax < 8 || g->lmax > 12) return false;
+  if (g->lmax < 6 || g->lmax > 12) return false;
   g->v = g->tc / g->s;
   if (static_cast<uint64_t>(g->tr) * g->v * g->lmax > 65535u) return false;
   return true;

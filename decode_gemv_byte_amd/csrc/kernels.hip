@@ -251,11 +251,17 @@ struct LaneBits {
 };
 
 // Decode the next two exponents with either reader: returns a dword with
-// exponent 0 at bits 7..14 and exponent 1 at bits 23..30.
-template <class R>
+// exponent 0 at bits 7..14 and exponent 1 at bits 23..30.  FIT2: the code is
+// limited to 6 bits, so two codes always fit the 12-bit window and the
+// second lookup never happens.
+template <bool FIT2 = false, class R>
 __device__ __forceinline__ uint32_t decode_pair(R& rd, const uint32_t* tab) {
   const uint32_t win = rd.window();
   uint32_t ent = tab[(win & 0x3FFCu) >> 2];
+  if constexpr (FIT2) {
+    rd.advance(ent & 0x1Fu);
+    return ent;
+  }
   // Rarely the second code does not fit in the 12-bit window.  The test is
   // made for the whole wavefront, and inside the branch every lane does the
   // second lookup and keeps it only if it needs it, so the common path has no
@@ -648,7 +654,7 @@ __device__ __forceinline__ uint32_t interleave(const uint32_t* buf, uint32_t w0,
 // slot, raw bytes and x in registers) into this lane's row sums over its 8
 // columns.  Rows past the matrix edge (last row block only; a wave-uniform
 // test) are not decoded and keep their zero sums.
-template <int TR, int NX, int R0, int R1>
+template <int TR, int NX, int R0, int R1, bool FIT2 = false>
 __device__ __forceinline__ void gemv_rows(const TileRegs<TR, NX>& in, LaneBits& br, const uint32_t* tab,
                                           float (&acc)[TR * NX]) {
 #pragma unroll
@@ -660,25 +666,25 @@ __device__ __forceinline__ void gemv_rows(const TileRegs<TR, NX>& in, LaneBits& 
       // each product is pinned next to its decode step: left alone, the
       // compiler defers all of them to the end of the tile and keeps every
       // decoded pair live, which costs occupancy
-      const uint32_t p0 = assemble(decode_pair(br, tab), in.raw[r].x, false);
+      const uint32_t p0 = assemble(decode_pair<FIT2>(br, tab), in.raw[r].x, false);
 #pragma unroll
       for (int k = 0; k < NX; k++) {
         a[k] = dot2(p0, in.x[k].x, a[k]);
         asm volatile("" : "+v"(a[k]));
       }
-      const uint32_t p1 = assemble(decode_pair(br, tab), in.raw[r].x, true);
+      const uint32_t p1 = assemble(decode_pair<FIT2>(br, tab), in.raw[r].x, true);
 #pragma unroll
       for (int k = 0; k < NX; k++) {
         a[k] = dot2(p1, in.x[k].y, a[k]);
         asm volatile("" : "+v"(a[k]));
       }
-      const uint32_t p2 = assemble(decode_pair(br, tab), in.raw[r].y, false);
+      const uint32_t p2 = assemble(decode_pair<FIT2>(br, tab), in.raw[r].y, false);
 #pragma unroll
       for (int k = 0; k < NX; k++) {
         a[k] = dot2(p2, in.x[k].z, a[k]);
         asm volatile("" : "+v"(a[k]));
       }
-      const uint32_t p3 = assemble(decode_pair(br, tab), in.raw[r].y, true);
+      const uint32_t p3 = assemble(decode_pair<FIT2>(br, tab), in.raw[r].y, true);
 #pragma unroll
       for (int k = 0; k < NX; k++) {
         a[k] = dot2(p3, in.x[k].w, a[k]);
@@ -692,16 +698,16 @@ __device__ __forceinline__ void gemv_rows(const TileRegs<TR, NX>& in, LaneBits& 
 
 // Skinny mode: rows [R0, R1) of the tile decoded into registers, four BF16
 // pairs per row (rows past the matrix edge stay zero).
-template <int TR, int NX, int R0, int R1>
+template <int TR, int NX, int R0, int R1, bool FIT2 = false>
 __device__ __forceinline__ void decode_rows(const TileRegs<TR, NX>& in, LaneBits& br, const uint32_t* tab,
                                             uint32_t (&wv)[TR][4]) {
 #pragma unroll
   for (int r = R0; r < R1; r++) {
     if (static_cast<uint32_t>(r) < in.nrows) {
-      wv[r][0] = assemble(decode_pair(br, tab), in.raw[r].x, false);
-      wv[r][1] = assemble(decode_pair(br, tab), in.raw[r].x, true);
-      wv[r][2] = assemble(decode_pair(br, tab), in.raw[r].y, false);
-      wv[r][3] = assemble(decode_pair(br, tab), in.raw[r].y, true);
+      wv[r][0] = assemble(decode_pair<FIT2>(br, tab), in.raw[r].x, false);
+      wv[r][1] = assemble(decode_pair<FIT2>(br, tab), in.raw[r].x, true);
+      wv[r][2] = assemble(decode_pair<FIT2>(br, tab), in.raw[r].y, false);
+      wv[r][3] = assemble(decode_pair<FIT2>(br, tab), in.raw[r].y, true);
     }
   }
 }
@@ -754,7 +760,7 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 // W' (job.y, rows of g.ldy elements) once the next tile's data is in; 16
 // for Y = X W^T with up to 16 X rows on the matrix cores (8-row tiles: the
 // decoded tile goes through LDS into MFMA operand layout).
-template <int TR, int MAXW, int NB>
+template <int TR, int MAXW, int NB, bool FIT2 = false>
 __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   constexpr bool DECODE = NB < 0;
   constexpr bool MF = NB == 16;
@@ -886,7 +892,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       for (int k = 0; k < TR; k++) wv[k][0] = wv[k][1] = wv[k][2] = wv[k][3] = 0u;
       LaneBits br;
       br.init(slot, q0);
-      if (in.active) decode_rows<TR, NX, 0, TR>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, 0, TR, FIT2>(in, br, tab, wv);
       // Y block (16 weight rows x 16 X rows) += W block (16 x 32) x X^T block
       // (32 x 16), 16 times over the tile's 512 columns.  MFMA operands: lane
       // l holds row l % 16 of W (rows 8..15 zero) and row l % 16 of X (zero
@@ -973,9 +979,9 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     LaneBits br;
     br.init(slot, q0);
     if constexpr (NB <= 0) {
-      if (in.active) decode_rows<TR, NX, 0, TR / 2>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, 0, TR / 2, FIT2>(in, br, tab, wv);
     } else if constexpr (!MF) {
-      if (in.active) gemv_rows<TR, NX, 0, TR / 2>(in, br, tab, acc);
+      if (in.active) gemv_rows<TR, NX, 0, TR / 2, FIT2>(in, br, tab, acc);
     }
     // the second half's raw bytes, then the next tile's loads: they go out
     // halfway through this tile and nothing touches them before the next
@@ -997,7 +1003,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       nx.load_rest(b, ni, nj);
     }
     if constexpr (DECODE) {
-      if (in.active) decode_rows<TR, NX, TR / 2, TR>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, TR / 2, TR, FIT2>(in, br, tab, wv);
 #pragma unroll
       for (int rr = 0; rr < TR; rr++)
 #pragma unroll
@@ -1007,7 +1013,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       p_nrows = in.nrows;
       p_active = in.active;
     } else if constexpr (NB == 0) {
-      if (in.active) decode_rows<TR, NX, TR / 2, TR>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, TR / 2, TR, FIT2>(in, br, tab, wv);
       // X rows in groups of GB: TR GB sums per lane, reduced over the
       // wavefront at once; lanes 2v and 2v + 1 end with sum v (row v / GB,
       // batch row g GB + v % GB)
@@ -1029,7 +1035,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
         if ((lane & 1u) == 0 && beta < g.batch) gsum[((t - r0) * TR + vr) * g.batch + beta] = sv;
       }
     } else if constexpr (!MF) {
-      if (in.active) gemv_rows<TR, NX, TR / 2, TR>(in, br, tab, acc);
+      if (in.active) gemv_rows<TR, NX, TR / 2, TR, FIT2>(in, br, tab, acc);
       // lanes (64 / (TR NB)) v .. hold sum v: row v / NB, X row v % NB
       const float s = reduce_rows<TR * NA>(acc);
       constexpr uint32_t lanes_per_sum = kWave / (TR * NA);
@@ -1262,6 +1268,7 @@ struct Launch {
   BlobDev b;
   bool fast;  // S = 64, V = 8, TR in {4, 8, 16, 32}, K % 8 == 0
   uint32_t max_chunk_bits;
+  uint32_t max_code_len;
 };
 
 nwc_status prepare(const nwc_info* info, const void* blob_dev, Launch* L) {
@@ -1271,6 +1278,7 @@ nwc_status prepare(const nwc_info* info, const void* blob_dev, Launch* L) {
   if (info->max_tile_words > 65536u) return NWC_ERR_UNSUPPORTED;
   if (info->max_chunk_bits > static_cast<uint64_t>(g.tr) * g.v * g.lmax) return NWC_ERR_INVALID_ARG;
   L->max_chunk_bits = info->max_chunk_bits;
+  L->max_code_len = info->max_code_len;
   const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
   BlobDev& b = L->b;
   b.table = reinterpret_cast<const uint32_t*>(base + g.off_table);
@@ -1453,7 +1461,7 @@ GemvPlan plan_skinny(const Launch& L, int batch, uint64_t cap, size_t group_lds)
 // wavefronts per workgroup are the size with the most resident wavefronts
 // per CU (registers and LDS both count, the ranges' LDS included), the
 // larger size on a tie.
-template <int TR, int MAXW, int NB>
+template <int TR, int MAXW, int NB, bool FIT2 = false>
 nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y, uint8_t* const* ws, int count,
                        int y_f32, hipStream_t s, int batch = 1, uint64_t ldx = 0, uint64_t ldy = 0,
                        const uint64_t* ld_out = nullptr) {
@@ -1551,8 +1559,22 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   g.ldy = ldy;
   g.batch = static_cast<uint32_t>(batch);
   const size_t lds = nw * per_wave + best.group_lds(sums);
-  if (set_lds(k_gemv<TR, MAXW, NB>, lds) != hipSuccess) return NWC_ERR_HIP;
-  return launch(k_gemv<TR, MAXW, NB>, dim3(groups), dim3(nw * kWave), lds, s, g);
+  if (set_lds(k_gemv<TR, MAXW, NB, FIT2>, lds) != hipSuccess) return NWC_ERR_HIP;
+  return launch(k_gemv<TR, MAXW, NB, FIT2>, dim3(groups), dim3(nw * kWave), lds, s, g);
+}
+
+// The batch-1 (NB = 1) or decode (NB = -1) launch for the matrices' tile
+// height, with the second-lookup-free decode when every code is <= 6 bits.
+template <int NB, typename... A>
+nwc_status launch_fused(const Launch* L, int count, A... a) {
+  bool fit2 = true;
+  for (int j = 0; j < count; j++) fit2 = fit2 && L[j].max_code_len <= 6;
+  switch (L[0].b.tr) {
+    case 4: return fit2 ? launch_gemv<4, 16, NB, true>(L, a...) : launch_gemv<4, 16, NB>(L, a...);
+    case 8: return fit2 ? launch_gemv<8, 16, NB, true>(L, a...) : launch_gemv<8, 16, NB>(L, a...);
+    case 16: return fit2 ? launch_gemv<16, 8, NB, true>(L, a...) : launch_gemv<16, 8, NB>(L, a...);
+    default: return fit2 ? launch_gemv<32, 4, NB, true>(L, a...) : launch_gemv<32, 4, NB>(L, a...);
+  }
 }
 
 // Whether a blob and batch take the skinny mode of the fused kernel (no
@@ -1628,12 +1650,8 @@ nwc_status nwc_decode(const nwc_info* info, const void* blob_dev, uint16_t* w_de
   if (L.fast && vec) {
     const uint16_t* none = nullptr;
     void* out = w_dev;
-    switch (L.b.tr) {
-      case 4: return launch_gemv<4, 16, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
-      case 8: return launch_gemv<8, 16, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
-      case 16: return launch_gemv<16, 8, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
-      default: return launch_gemv<32, 4, -1>(&L, &none, &out, nullptr, 1, 0, s, 1, 0, 0, &ld);
-    }
+    return launch_fused<-1>(&L, 1, &none, &out, static_cast<uint8_t* const*>(nullptr), 1, 0, s, 1, uint64_t{0},
+                            uint64_t{0}, static_cast<const uint64_t*>(&ld));
   } else {
     if (set_lds(k_decode_generic, lds) != hipSuccess) return NWC_ERR_HIP;
     return launch(k_decode_generic, dim3(grid), dim3(threads), lds, s, L.b, w_dev, ld);
@@ -1679,12 +1697,7 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
     if (!xvec) return NWC_ERR_ALIGNMENT;
     void* yy = Y;
     uint8_t* w8 = static_cast<uint8_t*>(ws);
-    switch (L.b.tr) {
-      case 4: return launch_gemv<4, 16, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
-      case 8: return launch_gemv<8, 16, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
-      case 16: return launch_gemv<16, 8, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
-      default: return launch_gemv<32, 4, 1>(&L, &X, &yy, &w8, 1, y_f32, s);
-    }
+    return launch_fused<1>(&L, 1, &X, &yy, &w8, 1, y_f32, s);
   }
   if (need == 0) {
     // skinny mode of the fused kernel (nwc_workspace_size said so)
@@ -1751,12 +1764,7 @@ nwc_status nwc_gemv_batched(int count, const nwc_info* infos, const void* const*
   if (ws_bytes < used) return NWC_ERR_BUFFER_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int y_f32 = y_type == NWC_OUT_F32 ? 1 : 0;
-  switch (L[0].b.tr) {
-    case 4: return launch_gemv<4, 16, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
-    case 8: return launch_gemv<8, 16, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
-    case 16: return launch_gemv<16, 8, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
-    default: return launch_gemv<32, 4, 1>(L, x_dev, y_dev, w8, count, y_f32, s);
-  }
+  return launch_fused<1>(L, count, x_dev, y_dev, static_cast<uint8_t* const*>(w8), count, y_f32, s);
 }
 
 nwc_status nwc_decode_batched(int count, const nwc_info* infos, const void* const* blobs_dev, uint16_t* const* w_dev,
@@ -1775,12 +1783,8 @@ nwc_status nwc_decode_batched(int count, const nwc_info* infos, const void* cons
     out[j] = w_dev[j];
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (L[0].b.tr) {
-    case 4: return launch_gemv<4, 16, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
-    case 8: return launch_gemv<8, 16, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
-    case 16: return launch_gemv<16, 8, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
-    default: return launch_gemv<32, 4, -1>(L, none, out, nullptr, count, 0, s, 1, 0, 0, ld);
-  }
+  return launch_fused<-1>(L, count, none, out, static_cast<uint8_t* const*>(nullptr), count, 0, s, 1, uint64_t{0},
+                          uint64_t{0}, static_cast<const uint64_t*>(ld));
 }
 
 nwc_status nwc_gemm_skinny(const nwc_info* info, const void* blob_dev, const uint16_t* X_dev, uint64_t ldx, int batch,

@@ -28,9 +28,12 @@ import numpy as np
 from . import (GemvBatch, NwcError, nwc_decode, nwc_encode, nwc_gemm_skinny, nwc_gemv, nwc_gemv_batched,
                nwc_inspect, nwc_workspace_size)
 
-# (tile_rows, max_code_len): the tile heights the fused kernels run natively,
-# with the default length limit and one step above it
-DEFAULT_CANDIDATES: Tuple[Tuple[int, int], ...] = ((4, 8), (8, 8), (16, 8), (32, 8), (8, 9))
+# (tile_rows, max_code_len): the tile heights the fused kernels run natively
+# at the default length limit, one step above it, and the 6-bit limit under
+# which every decode step reads two codes with one lookup (about 0.4 bit per
+# weight more; only for tensors with at most 64 distinct exponents, else the
+# library rejects the candidate)
+DEFAULT_CANDIDATES: Tuple[Tuple[int, int], ...] = ((4, 8), (8, 8), (16, 8), (32, 8), (8, 9), (4, 6), (8, 6))
 STREAM_BYTES = 768 << 20   # device copies cycled per timing: well above the last-level cache
 MAX_COPIES = 32
 
@@ -65,14 +68,14 @@ class TuneResult:
 
 def check_candidates(candidates) -> List[Tuple[int, int]]:
     """Validate (tile_rows, max_code_len) pairs: tile_rows a power of two in
-    1..64, max_code_len 8..12 (what the encoder accepts)."""
+    1..64, max_code_len 6..12 (what the encoder accepts)."""
     out = []
     for c in candidates:
         tr, lmax = (int(c[0]), int(c[1]))
         if tr < 1 or tr > 64 or tr & (tr - 1):
             raise ValueError("tile_rows must be a power of two in 1..64, got %d" % tr)
-        if not 8 <= lmax <= 12:
-            raise ValueError("max_code_len must be in 8..12, got %d" % lmax)
+        if not 6 <= lmax <= 12:
+            raise ValueError("max_code_len must be in 6..12, got %d" % lmax)
         if (tr, lmax) not in out:
             out.append((tr, lmax))
     if not out:
@@ -170,7 +173,12 @@ def tune_geometry(w: Union[np.ndarray, Sequence[np.ndarray]], batch: int = 1, ca
     device = torch.device(device or "cuda")
     res, err = [], None
     for tr, lmax in check_candidates(candidates):
-        blobs = [nwc_encode(m, {"tile_rows": tr, "max_code_len": lmax}) for m in mats]
+        try:
+            blobs = [nwc_encode(m, {"tile_rows": tr, "max_code_len": lmax}) for m in mats]
+        except NwcError as e:       # e.g. more distinct exponents than a short limit codes
+            res.append(Candidate(tr, lmax, 0, float("inf")))
+            err = e
+            continue
         try:
             us = _time_candidate(mats, blobs, batch, reps, device)
         except NwcError as e:

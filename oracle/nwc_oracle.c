@@ -357,7 +357,7 @@ static int geom_check(uint64_t rows, uint64_t cols, uint32_t tr, uint32_t tc,
                       uint32_t s, uint32_t lmax) {
   if (rows < 1 || cols < 1) return ORC_EINVAL;
   if (tr < 1 || tc < 1 || s < 1 || tc % s != 0) return ORC_EINVAL;
-  if (lmax < 8 || lmax > 12) return ORC_EINVAL;
+  if (lmax < 6 || lmax > 12) return ORC_EINVAL;
   uint64_t v = tc / s;
   if ((uint64_t)tr * v * lmax > 65535u) return ORC_EINVAL;
   return ORC_OK;

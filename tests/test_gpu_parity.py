@@ -106,7 +106,11 @@ DECODE_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=16)), ("cfg1", dict(tile
                 ("nan_payloads", None), ("subnormal", None), ("one_symbol", None), ("random_bits", None),
                 ("wide_odd", None), ("wide_odd", dict(tile_rows=3, tile_cols=7, chunks_per_tile=7, max_code_len=10)),
                 ("cfg1", dict(max_code_len=12)), ("all_patterns", dict(max_code_len=12)),
-                ("cfg1", dict(tile_rows=4)), ("1000x256", dict(tile_rows=4))]
+                ("cfg1", dict(tile_rows=4)), ("1000x256", dict(tile_rows=4)),
+                # code limits below 8: at 6 the fused decode never takes a second lookup
+                ("cfg1", dict(max_code_len=6)), ("cfg1", dict(max_code_len=7)), ("subnormal", dict(max_code_len=6)),
+                ("1000x256", dict(tile_rows=4, max_code_len=6)), ("cfg1", dict(tile_rows=16, max_code_len=6)),
+                ("cfg1", dict(tile_rows=32, max_code_len=6)), ("127x1001", dict(max_code_len=6))]
 
 
 @pytest.mark.parametrize("name,params", DECODE_CASES)
@@ -173,7 +177,10 @@ GEMV_CASES = [("cfg1", None), ("cfg1", dict(tile_rows=16)), ("cfg1", dict(tile_r
               ("one_symbol", None), ("wide_odd", None), ("8x512", None), ("3000x512", None),
               ("20x40960", None), ("20x40960", dict(tile_rows=16)),
               ("cfg1", dict(max_code_len=12)), ("3000x512", dict(max_code_len=12)),
-              ("cfg1", dict(tile_rows=4)), ("3000x512", dict(tile_rows=4)), ("20x40960", dict(tile_rows=4))]
+              ("cfg1", dict(tile_rows=4)), ("3000x512", dict(tile_rows=4)), ("20x40960", dict(tile_rows=4)),
+              ("cfg1", dict(max_code_len=6)), ("cfg1", dict(max_code_len=7)), ("3000x512", dict(max_code_len=6)),
+              ("20x40960", dict(tile_rows=4, max_code_len=6)), ("20x40960", dict(tile_rows=32, max_code_len=6)),
+              ("1000x256", dict(tile_rows=16, max_code_len=6)), ("127x1001", dict(max_code_len=6))]
 
 
 @pytest.mark.parametrize("out_f32", [False, True])
@@ -332,7 +339,8 @@ def _gemm(blob: Blob, X: np.ndarray, out_f32: bool):
 @pytest.mark.parametrize("batch", [2, 3, 4, 5, 8, 13, 16])
 @pytest.mark.parametrize("name,params", [("cfg1", None), ("127x1001", None), ("1000x256", None),
                                          ("cfg1", dict(tile_rows=16)), ("1000x256", dict(tile_rows=16)),
-                                         ("cfg1", dict(tile_rows=32)), ("wide_odd", None)])
+                                         ("cfg1", dict(tile_rows=32)), ("wide_odd", None),
+                                         ("cfg1", dict(max_code_len=6)), ("1000x256", dict(tile_rows=16, max_code_len=6))])
 def test_gemm_small(name, params, batch):
     w = _special(name)
     X = workloads.gaussian_bits((batch, w.shape[1]), 1.0, 12)
@@ -540,3 +548,27 @@ def test_native_library_is_in_tree():
     assert os.path.dirname(os.path.abspath(nwc.LIB_PATH)).startswith(ROOT)
     maps = open("/proc/self/maps").read()
     assert nwc.LIB_PATH in maps
+
+
+def test_gemv_batched_short_codes_and_mixed_limits():
+    # all blobs at L = 6 take the second-lookup-free kernel; one blob at L = 8
+    # among them sends the whole launch through the general one
+    ws = [workloads.gaussian_bits((1000, 256), 0.02, 31), workloads.gaussian_bits((37, 1024), 0.05, 32),
+          workloads.gaussian_bits((300, 2048), 0.01, 33)]
+    xs = [dev(workloads.gaussian_bits((w.shape[1],), 1.0, 40 + i)) for i, w in enumerate(ws)]
+    for limits in ((6, 6, 6), (6, 8, 6)):
+        blobs = [Blob(w, dict(max_code_len=l)) for w, l in zip(ws, limits)]
+        ys = [torch.empty(w.shape[0], dtype=torch.float32, device="cuda") for w in ws]
+        wsp = _batched_ws(blobs)
+        _say("gemv_batched limits %s" % (limits,))
+        nwc.nwc_gemv_batched(nwc.GemvBatch([b.info for b in blobs], [b.dev for b in blobs], xs, ys, wsp))
+        torch.cuda.synchronize()
+        assert _counters_zero(blobs, wsp)
+        for b, x, y in zip(blobs, xs, ys):
+            y_ref, a_ref = oracle.gemv(b.w, x.cpu().numpy())
+            _check_y(_to_f64(y), y_ref, a_ref, True, "limits %s" % (limits,))
+        outs = [torch.empty(w.shape, dtype=torch.int16, device="cuda") for w in ws]
+        nwc.nwc_decode_batched(nwc.DecodeBatch([b.info for b in blobs], [b.dev for b in blobs], outs))
+        torch.cuda.synchronize()
+        for w, o in zip(ws, outs):
+            assert np.array_equal(o.cpu().numpy().view(np.uint16), w)

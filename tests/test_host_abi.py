@@ -136,7 +136,7 @@ def test_inspect_rejects_corruption():
 
 def test_encode_errors():
     w = workloads.gaussian_bits((10, 20), 0.02, 1)
-    for p in [dict(tile_cols=500), dict(max_code_len=13), dict(max_code_len=7),
+    for p in [dict(tile_cols=500), dict(max_code_len=13), dict(max_code_len=5),
               dict(tile_rows=4096, tile_cols=4096, chunks_per_tile=1)]:
         with pytest.raises(nwc.NwcError) as ei:
             nwc.nwc_encode(w, p)
@@ -152,6 +152,29 @@ def test_encode_errors():
     assert nwc._lib.nwc_encode(w.ctypes.data, 10, 20, 19, None, buf.ctypes.data, buf.size,
                                ctypes.byref(used)) == nwc.NWC_ERR_INVALID_ARG
     assert nwc.nwc_encode_bound(10, 20) >= need
+    # limits below 8 hold at most 2^L distinct exponents
+    many = workloads.random_bits((64, 64), 3)
+    for lmax in (6, 7):
+        with pytest.raises(nwc.NwcError) as ei:
+            nwc.nwc_encode(many, dict(max_code_len=lmax))
+        assert ei.value.status == nwc.NWC_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("geom", [dict(max_code_len=6), dict(max_code_len=7), dict(tile_rows=4, max_code_len=6)])
+@pytest.mark.parametrize("name", ["cfg1", "127x1001", "subnormal", "one_symbol", "1x1"])
+def test_encoder_bytes_equal_oracle_short_codes(name, geom):
+    # tensors with at most 64 distinct exponent values
+    rng = np.random.default_rng(6)
+    w = {
+        "cfg1": lambda: workloads.weights(1, "w"),
+        "127x1001": lambda: workloads.gaussian_bits((127, 1001), 0.05, 3),
+        "subnormal": lambda: (rng.integers(1, 128, (48, 70)) | (rng.integers(0, 2, (48, 70)) << 15)).astype(np.uint16),
+        "one_symbol": lambda: (0x3C00 | rng.integers(0, 128, (50, 60))).astype(np.uint16),
+        "1x1": lambda: workloads.gaussian_bits((1, 1), 0.02, 1),
+    }[name]()
+    blob = nwc.nwc_encode(w, geom)
+    assert np.array_equal(blob, _oracle_blob(w, geom))
+    assert nwc.nwc_inspect(blob).max_code_len == geom["max_code_len"]
 
 
 def test_workspace_sizes():

@@ -256,7 +256,28 @@ def test_stream_corruption_detected_by_length_check():
 
 def test_encode_rejects_bad_geometry():
     w = SPECIALS["1x1"]
-    for geom in [(0, 512, 64, 12), (16, 500, 64, 12), (16, 512, 64, 13), (16, 512, 64, 7),
+    for geom in [(0, 512, 64, 12), (16, 500, 64, 12), (16, 512, 64, 13), (16, 512, 64, 5),
                  (512, 4096, 1, 12)]:
         with pytest.raises(ValueError):
             oracle.encode(w, *geom)
+
+
+@pytest.mark.parametrize("lmax", [6, 7])
+@pytest.mark.parametrize("tr", [8, 4])
+def test_short_code_limits_round_trip(lmax, tr):
+    # limits below 8 take tensors with at most 2^lmax distinct exponents
+    for name in ("1x1", "one_symbol", "subnormal"):
+        w = SPECIALS[name]
+        assert np.array_equal(oracle.decode(oracle.encode(w, tr, 512, 64, lmax)), w)
+    w = workloads.gaussian_bits((37, 1100), 0.02, 21)
+    blob = oracle.encode(w, tr, 512, 64, lmax)
+    assert oracle.header(blob)["max_code_len"] == lmax
+    assert np.array_equal(oracle.decode(blob), w)
+
+
+def test_short_code_limit_rejects_too_many_exponents():
+    w = workloads.random_bits((64, 64), 3)          # all 256 exponent values
+    for lmax in (6, 7):
+        with pytest.raises(ValueError):
+            oracle.encode(w, 8, 512, 64, lmax)
+    assert np.array_equal(oracle.decode(oracle.encode(w, 8, 512, 64, 8)), w)
