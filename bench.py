@@ -95,7 +95,17 @@ def model_step(args):
     L, CTX, H, HQ, HKV, D = args.model_step, 512, 2560, 32, 8, 128
     names = ["q", "k", "v", "o", "gate", "up", "down"]
     w = {n: workloads.weights(2, n) for n in names}
-    blob = {n: nwc.nwc_encode(w[n]) for n in names}
+    enc = {n: None for n in names}
+    tuned = None
+    if getattr(args, "geometry", "default") == "tuned":   # per launch group, as the main bench does
+        from decode_gemv_byte_amd import tune
+        tuned = {}
+        for grp in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+            r = tune.tune_geometry([w[n] for n in grp])
+            tuned["+".join(grp)] = r.params()
+            for n in grp:
+                enc[n] = r.params()
+    blob = {n: nwc.nwc_encode(w[n], enc[n]) for n in names}
     info = {n: nwc.nwc_inspect(blob[n]) for n in names}
     lay = []
     for l in range(L):
@@ -207,6 +217,7 @@ def model_step(args):
         "warmup": args.warmup, "ms_per_step": round(res[False], 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "qwen3_4b_stack", "layers": L, "context": CTX, "batch": 1, "hip_graph": True,
+                   "encoder": {"tuned": tuned} if tuned else "default",
                    "weights": "qwen3_4b_layer matrices, one device copy per layer"},
         "dense_bf16_torch_mv": {"tokens_per_s": round(1e3 / res[True], 2), "ms_per_step": round(res[True], 4)},
         "speedup_vs_dense": round(res[True] / res[False], 3),
