@@ -572,3 +572,42 @@ def test_gemv_batched_short_codes_and_mixed_limits():
         torch.cuda.synchronize()
         for w, o in zip(ws, outs):
             assert np.array_equal(o.cpu().numpy().view(np.uint16), w)
+
+
+# ------------------------------------------------------- seeded shape sweep --
+
+def _sweep_cases(n=24, seed=2026):
+    # rows, cols, tile rows, code limit, batch: ragged edges in both
+    # dimensions, every fast tile height and limits 6 / 8 / 12
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        rows = int(rng.integers(1, 3000))
+        cols = int(rng.choice([int(rng.integers(1, 5000)), 8 * int(rng.integers(1, 640))]))
+        tr = int(rng.choice([4, 8, 16, 32]))
+        lmax = int(rng.choice([6, 8, 12]))
+        batch = int(rng.integers(2, 17))
+        out.append((i, rows, cols, tr, lmax, batch))
+    return out
+
+
+@pytest.mark.parametrize("i,rows,cols,tr,lmax,batch", _sweep_cases())
+def test_seeded_shape_sweep(i, rows, cols, tr, lmax, batch):
+    w = workloads.gaussian_bits((rows, cols), float(np.exp(-4 + i % 3)), 500 + i)
+    _say("sweep %d: %dx%d TR %d L %d batch %d" % (i, rows, cols, tr, lmax, batch))
+    b = Blob(w, dict(tile_rows=tr, max_code_len=lmax))
+    out = torch.full(w.shape, 0x5A5A, dtype=torch.int16, device="cuda")
+    nwc.nwc_decode(b.info, b.dev, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), w)
+    x = workloads.gaussian_bits((cols,), 1.0, 900 + i)
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    nwc.nwc_gemv(b.info, b.dev, dev(x), y, b.ws(1))
+    torch.cuda.synchronize()
+    y_ref, a_ref = oracle.gemv(w, x)
+    _check_y(_to_f64(y), y_ref, a_ref, True, "sweep %d gemv" % i)
+    X = workloads.gaussian_bits((batch, cols), 1.0, 1300 + i)
+    Y = _to_f64(_gemm(b, X, False))
+    Y_ref, A_ref = oracle.gemm(w, X)
+    for beta in range(batch):
+        _check_y(Y[beta], Y_ref[beta], A_ref[beta], False, "sweep %d b%d" % (i, beta))
