@@ -746,9 +746,8 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 // Each workgroup owns a contiguous range of a matrix's tiles (whole row
 // blocks when that keeps the ranges even).  Its wavefronts start on the
 // range's first tiles, then claim the rest one at a time from an LDS
-// counter partway through their current tile (7/8 of its rows in the
-// batch-1 mode, half in the others), so a tile goes to whichever wavefront
-// is furthest along.  While tile t decodes from the slot, the next
+// counter 7/8 of the way through their current tile, so a tile goes to
+// whichever wavefront is furthest along.  While tile t decodes from the slot, the next
 // tile's stream lands in the linear buffer.  Every tile sum goes to LDS;
 // after one barrier the workgroup adds each row's sums in column order.  A
 // row block cut by a range edge has its tile sums added through the
@@ -858,7 +857,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
 
   // decode mode: the tile decoded last, stored right after the next tile's
   // data is in, as exactly TR stores (rows past the matrix edge write row 0
-  // again, the same bytes), so that the wait halfway through the tile can
+  // again, the same bytes), so that the wait partway through the tile can
   // leave just those stores outstanding: memory operations of a wavefront
   // complete in the order they were issued
   uint32_t pv[TR][4];
@@ -959,12 +958,12 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       t = tn;
       continue;
     }
-    // rows [0, PRE) decode before the next tile's loads go out: half the tile
-    // in the skinny and decode modes, 7/8 of it in the batch-1 mode (issuing
-    // loads stalls a wavefront while HBM is saturated, and with the loads
-    // later the first tiles of a launch decode sooner; measured 5% faster on
-    // 9728 x 2560 pairs, no change on smaller or larger launches)
-    constexpr int PRE = NB == 1 ? TR * 7 / 8 : TR / 2;
+    // rows [0, PRE) decode before the next tile's loads go out: 7/8 of the
+    // tile (issuing loads stalls a wavefront while HBM is saturated, and with
+    // the loads later the first tiles of a launch decode sooner; measured
+    // against half the tile: batch 1 on 9728 x 2560 pairs 5% faster, the
+    // skinny modes 1-5% and the standalone decode 2%, nothing slower)
+    constexpr int PRE = TR * 7 / 8;
     // every raw row below PRE is in: all but the last TR - PRE of the second
     // half's TR / 2 row loads (issued last, in row order)
     wait_vmem_but<(TR - PRE < TR / 2 ? TR - PRE : TR / 2)>();
@@ -988,7 +987,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     LaneBits br;
     br.init(slot, q0);
     if constexpr (NB <= 0) {
-      if (in.active) decode_rows<TR, NX, 0, TR / 2, FIT2>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, 0, PRE, FIT2>(in, br, tab, wv);
     } else if constexpr (!MF) {
       if (in.active) gemv_rows<TR, NX, 0, PRE, FIT2>(in, br, tab, acc);
     }
@@ -1012,7 +1011,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       nx.load_rest(b, ni, nj);
     }
     if constexpr (DECODE) {
-      if (in.active) decode_rows<TR, NX, TR / 2, TR, FIT2>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, PRE, TR, FIT2>(in, br, tab, wv);
 #pragma unroll
       for (int rr = 0; rr < TR; rr++)
 #pragma unroll
@@ -1022,7 +1021,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       p_nrows = in.nrows;
       p_active = in.active;
     } else if constexpr (NB == 0) {
-      if (in.active) decode_rows<TR, NX, TR / 2, TR, FIT2>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, PRE, TR, FIT2>(in, br, tab, wv);
       // X rows in groups of GB: TR GB sums per lane, reduced over the
       // wavefront at once; lanes 2v and 2v + 1 end with sum v (row v / GB,
       // batch row g GB + v % GB)
