@@ -269,8 +269,8 @@ def main():
         model_step(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(row sharding across GPUs is described in DESIGN.md but not built)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (a matrix would shard by row "
+              "blocks, one blob per GPU, with no cross-GPU reduction at batch 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -60,7 +60,7 @@ typedef enum {
   NWC_ERR_INVALID_ARG = -1,      /* null pointer, bad size, bad parameter */
   NWC_ERR_BUFFER_TOO_SMALL = -2, /* output or workspace capacity too small */
   NWC_ERR_BAD_FORMAT = -3,       /* blob fails validation */
-  NWC_ERR_UNSUPPORTED = -4,      /* valid request this build cannot run */
+  NWC_ERR_UNSUPPORTED = -4,      /* valid request the library cannot run */
   NWC_ERR_ALIGNMENT = -5,        /* pointer or leading dimension misaligned */
   NWC_ERR_HIP = -6               /* a HIP runtime call or launch failed */
 } nwc_status;
