@@ -1715,18 +1715,24 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
     // through the tile decoded into registers, and from 10 X rows on (8-row
     // tiles) through the matrix cores, which then cost less than the
     // vector products they replace
+    // (with codes of at most 6 bits, the second-lookup-free decode)
+    const bool fit2 = L.max_code_len <= 6;
+#define NWC_SKINNY(TR_, MAXW_, NB_)                                                                      \
+  return fit2 ? launch_gemv<TR_, MAXW_, NB_, true>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy) \
+              : launch_gemv<TR_, MAXW_, NB_>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy)
     if (L.b.tr == 8) {
       switch (batch) {
-        case 2: return launch_gemv<8, 16, 2>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+        case 2: NWC_SKINNY(8, 16, 2);
         case 3:  // a power-of-two count of sums per lane: X row 3 is zero
-        case 4: return launch_gemv<8, 16, 4>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+        case 4: NWC_SKINNY(8, 16, 4);
         default:
-          if (batch < 10) return launch_gemv<8, 16, 0>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+          if (batch < 10) NWC_SKINNY(8, 16, 0);
           return launch_gemv<8, 16, 16>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
       }
     }
-    if (batch == 2) return launch_gemv<16, 8, 2>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
-    return launch_gemv<16, 8, 0>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+    if (batch == 2) NWC_SKINNY(16, 8, 2);
+    NWC_SKINNY(16, 8, 0);
+#undef NWC_SKINNY
   }
   // generic path: partial sums per column tile, then a reduction
   const size_t lds = (static_cast<size_t>(kGenericWaves) * L.b.buf_words) * 4 +
