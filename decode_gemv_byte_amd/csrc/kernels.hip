@@ -1727,7 +1727,7 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
         case 4: NWC_SKINNY(8, 16, 4);
         default:
           if (batch < 10) NWC_SKINNY(8, 16, 0);
-          return launch_gemv<8, 16, 16>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy);
+          NWC_SKINNY(8, 16, 16);
       }
     }
     if (batch == 2) NWC_SKINNY(16, 8, 2);
