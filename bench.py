@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--skip-bf16", action="store_true", help="skip the plain-BF16 comparators")
     ap.add_argument("--tile-rows", type=int, default=0, help="encoder tile rows (0 = library default)")
     ap.add_argument("--max-code-len", type=int, default=0, help="encoder code length limit (0 = library default)")
+    ap.add_argument("--pair-fit", type=int, default=0, metavar="K",
+                    help="encoder: exponents held by at least 1/K of the weights get codes of at most 6 bits")
     ap.add_argument("--geometry", choices=("default", "tuned"), default="default",
                     help="tuned: time every candidate tile geometry per launch group on this GPU first "
                          "(decode_gemv_byte_amd.tune) and encode each group with the fastest")
@@ -284,7 +286,8 @@ def main():
     batch = args.batch or wl.batches[0]
     if not 1 <= batch <= 8192:
         sys.exit("batch must be 1..8192 (above 16: decode + hipBLASLt GEMM)")
-    params = {k: v for k, v in (("tile_rows", args.tile_rows), ("max_code_len", args.max_code_len)) if v}
+    params = {k: v for k, v in (("tile_rows", args.tile_rows), ("max_code_len", args.max_code_len),
+                                ("pair_fit", args.pair_fit)) if v}
     groups_named = [list(g) for g in wl.groups] if wl.groups else [[m.name] for m in wl.matrices]
     tuned, enc_params = None, {m.name: params or None for m in wl.matrices}
     if args.geometry == "tuned":
@@ -703,8 +706,8 @@ def cpu_baseline(wl, keys, info, batch, seconds):
         n_rows = info[(layer, name)].rows
         r0 = (i // len(keys)) * nb % n_rows
         sub = workloads.weights(wl.cid, name, layer=layer, rows=slice(r0, min(r0 + nb, n_rows)))
-        li = info[(layer, name)]  # the library blob's geometry and code length limit
-        blob = oracle.encode(sub, li.tile_rows, li.tile_cols, li.chunks_per_tile, li.max_code_len)
+        li = info[(layer, name)]  # the library blob's geometry and code length limit (and the default 6-bit cap)
+        blob = oracle.encode(sub, li.tile_rows, li.tile_cols, li.chunks_per_tile, li.max_code_len, 1024)
         x = workloads.activations(wl.cid, name, batch=batch, layer=layer)
         t = time.perf_counter()
         wd = oracle.decode(blob)

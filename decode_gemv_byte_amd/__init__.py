@@ -49,7 +49,8 @@ NWC_OUT_F32 = 1
 
 class nwc_params(ctypes.Structure):
     _fields_ = [("tile_rows", ctypes.c_uint32), ("tile_cols", ctypes.c_uint32),
-                ("chunks_per_tile", ctypes.c_uint32), ("max_code_len", ctypes.c_uint32)]
+                ("chunks_per_tile", ctypes.c_uint32), ("max_code_len", ctypes.c_uint32),
+                ("pair_fit", ctypes.c_uint32)]
 
 
 class nwc_info(ctypes.Structure):
@@ -123,7 +124,7 @@ def _params(p) -> Optional[nwc_params]:
     if isinstance(p, nwc_params):
         return p
     return nwc_params(*[int(p.get(k, 0)) for k in ("tile_rows", "tile_cols", "chunks_per_tile",
-                                                    "max_code_len")])
+                                                    "max_code_len", "pair_fit")])
 
 
 def _ptr_params(p):

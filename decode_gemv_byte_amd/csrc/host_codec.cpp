@@ -83,7 +83,7 @@ void parallel_blocks(uint64_t n, uint64_t min_per_worker, F fn) {
 // packages downwards selects, at every list, a prefix; the leaves inside the
 // prefix of each list are the first `a_j` sorted leaves, and each such
 // selection adds one bit to those symbols' lengths.
-bool build_lengths(const uint64_t hist[256], int lmax, uint8_t len[256]) {
+bool build_lengths(const uint64_t hist[256], int lmax, uint8_t len[256], uint32_t pair_fit) {
   std::memset(len, 0, 256);
   std::vector<int> sym;
   for (int s = 0; s < 256; s++)
@@ -98,21 +98,34 @@ bool build_lengths(const uint64_t hist[256], int lmax, uint8_t len[256]) {
   std::stable_sort(sym.begin(), sym.end(), [&](int a, int b) { return hist[a] < hist[b]; });
   std::vector<uint64_t> leafw(n);
   for (int i = 0; i < n; i++) leafw[i] = hist[sym[i]];
+  // Per-symbol caps (pair_fit): symbols with count * pair_fit >= total may
+  // use at most 6 bits, the others lmax.  The capped ones are the heaviest,
+  // so the leaves whose cap reaches a level deeper than 6 are the first
+  // n_deep sorted leaves: list j (level lmax - j) merges leaves
+  // [0, leaves_at(j)) only, and the expansion below stays a prefix count.
+  int n_deep = n;
+  if (pair_fit && lmax > 6) {
+    uint64_t total = 0;
+    for (int s = 0; s < 256; s++) total += hist[s];
+    n_deep = 0;
+    while (n_deep < n && static_cast<double>(leafw[n_deep]) * pair_fit < static_cast<double>(total)) n_deep++;
+  }
+  auto leaves_at = [&](int j) { return lmax - j > 6 ? n_deep : n; };
 
   // lists[j] holds weights and a leaf flag per item, in merged order
   std::vector<std::vector<uint64_t>> w(lmax);
   std::vector<std::vector<uint8_t>> is_leaf(lmax);
-  w[0] = leafw;
-  is_leaf[0].assign(n, 1);
+  w[0].assign(leafw.begin(), leafw.begin() + leaves_at(0));
+  is_leaf[0].assign(leaves_at(0), 1);
   for (int j = 1; j < lmax; j++) {
     const auto& prev = w[j - 1];
     const size_t npk = prev.size() / 2;
-    w[j].reserve(n + npk);
-    is_leaf[j].reserve(n + npk);
+    const size_t nl = static_cast<size_t>(leaves_at(j));
+    w[j].reserve(nl + npk);
+    is_leaf[j].reserve(nl + npk);
     size_t a = 0, b = 0;
-    while (a < static_cast<size_t>(n) || b < npk) {
-      const bool take_pkg =
-          b < npk && (a >= static_cast<size_t>(n) || prev[2 * b] + prev[2 * b + 1] < leafw[a]);
+    while (a < nl || b < npk) {
+      const bool take_pkg = b < npk && (a >= nl || prev[2 * b] + prev[2 * b + 1] < leafw[a]);
       if (take_pkg) {
         w[j].push_back(prev[2 * b] + prev[2 * b + 1]);
         is_leaf[j].push_back(0);
@@ -126,6 +139,8 @@ bool build_lengths(const uint64_t hist[256], int lmax, uint8_t len[256]) {
   }
   std::vector<int> bits(n, 0);
   size_t take = static_cast<size_t>(2 * n - 2);
+  // the caps leave no complete code (over 64 common symbols): the plain limit
+  if (take > w[lmax - 1].size()) return pair_fit ? build_lengths(hist, lmax, len, 0) : false;
   for (int j = lmax - 1; j >= 0; j--) {
     size_t leaves = 0;
     for (size_t i = 0; i < take; i++) leaves += is_leaf[j][i];
@@ -193,6 +208,7 @@ bool params_resolve(const nwc_params* p, Geometry* g) {
   g->tc = (p && p->tile_cols) ? p->tile_cols : 512;
   g->s = (p && p->chunks_per_tile) ? p->chunks_per_tile : 64;
   g->lmax = (p && p->max_code_len) ? p->max_code_len : 8;
+  g->pair_fit = (p && p->pair_fit) ? p->pair_fit : 1024;
   if (g->tc % g->s) return false;
   if (g->lmax < 6 || g->lmax > 12) return false;
   g->v = g->tc / g->s;
@@ -260,7 +276,7 @@ nwc_status encode(const uint16_t* w, uint64_t rows, uint64_t cols, uint64_t ld, 
 
   uint8_t len[256];
   uint16_t code[256];
-  if (!build_lengths(hist, static_cast<int>(g.lmax), len) || !canonical(len, code))
+  if (!build_lengths(hist, static_cast<int>(g.lmax), len, g.pair_fit) || !canonical(len, code))
     return NWC_ERR_INVALID_ARG;
   // codes bit-reversed so that emitting low bits first sends the MSB first
   uint32_t rev[256];
@@ -481,7 +497,7 @@ nwc_status inspect(const void* blob_v, size_t bytes, nwc_info* info) {
 // Re-derive the geometry of an nwc_info (for the device entry points).
 bool info_geometry(const nwc_info* info, Geometry* g) {
   if (!info) return false;
-  nwc_params p{info->tile_rows, info->tile_cols, info->chunks_per_tile, info->max_code_len};
+  nwc_params p{info->tile_rows, info->tile_cols, info->chunks_per_tile, info->max_code_len, 0};
   if (!p.tile_rows || !p.tile_cols || !p.chunks_per_tile || !p.max_code_len) return false;
   if (!params_resolve(&p, g)) return false;
   if (info->rows < 1 || info->cols < 1) return false;

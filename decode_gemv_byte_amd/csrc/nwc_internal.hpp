@@ -12,6 +12,7 @@ namespace nwc {
 // Tile geometry and section layout of one blob.
 struct Geometry {
   uint32_t tr = 0, tc = 0, s = 0, lmax = 0, v = 0;  // tile rows/cols, chunks, max code length, chunk cols
+  uint32_t pair_fit = 0;                             // encoder only: 6-bit cap for common exponents
   uint64_t rows = 0, cols = 0;
   uint64_t n_tr = 0, n_tc = 0, n_tiles = 0, n_chunks = 0;
   uint64_t raw_ld = 0, stream_words = 0;
@@ -19,7 +20,7 @@ struct Geometry {
            off_stream = 0, total = 0;
 };
 
-bool build_lengths(const uint64_t hist[256], int lmax, uint8_t len[256]);
+bool build_lengths(const uint64_t hist[256], int lmax, uint8_t len[256], uint32_t pair_fit = 0);
 bool canonical(const uint8_t len[256], uint16_t code[256]);
 void build_table(const uint8_t len[256], uint32_t table[4096]);
 bool params_resolve(const nwc_params* p, Geometry* g);

@@ -76,12 +76,22 @@ typedef enum {
  * A limit of 8 codes any tensor (all 256 exponent values fit); below 8 the
  * tensor may hold at most 2^max_code_len distinct exponent values.  At 6, two
  * codes always fit one 12-bit table lookup, and the fused kernels decode
- * every pair with one lookup, for about 0.4 bit per weight more than at 8. */
+ * every pair with one lookup, for about 0.4 bit per weight more than at 8.
+ * pair_fit trades a little size for fewer decode steps that need a second
+ * lookup (two codes longer than 12 bits together): with the common exponents
+ * capped at 6 bits, only pairs involving a rare exponent can overflow.  At
+ * the default (1024) it costs 0.3-0.6% of the blob on the synthetic workloads.
+ * The blob stores only the code lengths, so decoders need no such flag. */
 typedef struct {
   uint32_t tile_rows;       /* TR rows per tile [8] */
   uint32_t tile_cols;       /* TC columns per tile [512] */
   uint32_t chunks_per_tile; /* S column-strip chunks per tile [64] */
   uint32_t max_code_len;    /* L, longest code in bits [8] */
+  uint32_t pair_fit;        /* K: every exponent value held by at least 1/K of
+                               the weights gets a code of at most 6 bits, the
+                               rest keep the limit L; 1 turns it off (unless
+                               more than 64 values are that common, then the
+                               plain limit applies) [1024] */
 } nwc_params;
 
 /* Everything a device call needs, read from a validated blob. */

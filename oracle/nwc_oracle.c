@@ -115,17 +115,23 @@ static void pm_count(pm_item **lists, int lv, int idx, int *len) {
   pm_count(lists, lv - 1, it->child + 1, len);
 }
 
-/* Optimal prefix-code lengths of at most lmax bits for the symbol counts h.
- * Symbols with h = 0 get length 0.  One present symbol gets length 1.
- * For n >= 2 present symbols:
+/* Optimal prefix-code lengths for the symbol counts h, symbol s at most
+ * cap[s] bits (every cap[s] <= lmax).  Symbols with h = 0 get length 0.  One
+ * present symbol gets length 1.  For n >= 2 present symbols (package-merge,
+ * the coin-collector form: a symbol has one coin of width 2^-d for every
+ * d = 1 .. cap[s]):
  *   leaves are sorted by (count, symbol) ascending;
- *   starting from the leaf list, lmax-1 times: pair consecutive items of the
- *   current list into packages (an odd last item is dropped) and merge the
- *   packages with the leaves by weight, a leaf going first on equal weight;
+ *   list 0 holds the leaves whose cap reaches lmax; then lmax-1 times: pair
+ *   consecutive items of the current list into packages (an odd last item is
+ *   dropped) and merge the packages with the leaves whose cap reaches the
+ *   list's level (lmax - list index) by weight, a leaf going first on equal
+ *   weight;
  *   the first 2n-2 items of the final list are selected and a symbol's length
  *   is the number of selected items that contain it.
- * Returns ORC_EINVAL if no symbol is present or n > 2^lmax. */
-int orc_code_lengths(const uint64_t *h, int lmax, uint8_t *len_out) {
+ * Returns ORC_EINVAL if no symbol is present or the caps leave no prefix code
+ * (the sum of 2^-cap over the present symbols exceeds 1; the final list then
+ * holds fewer than 2n-2 items). */
+static int code_lengths_capped(const uint64_t *h, int lmax, const int *cap, uint8_t *len_out) {
   int n = 0;
   int syms[256];
   for (int s = 0; s < 256; s++) {
@@ -165,23 +171,29 @@ int orc_code_lengths(const uint64_t *h, int lmax, uint8_t *len_out) {
     free(sizes);
     return ORC_EINVAL;
   }
+  /* leaves of list lv: those whose cap reaches level lmax - lv */
+  pm_item lv_leaves[256];
   lists[0] = (pm_item *)malloc(sizeof(pm_item) * (size_t)n);
-  memcpy(lists[0], leaves, sizeof(pm_item) * (size_t)n);
-  sizes[0] = n;
+  sizes[0] = 0;
+  for (int i = 0; i < n; i++)
+    if (cap[leaves[i].sym] >= lmax) lists[0][sizes[0]++] = leaves[i];
   for (int lv = 1; lv < lmax; lv++) {
+    int nl = 0;
+    for (int i = 0; i < n; i++)
+      if (cap[leaves[i].sym] >= lmax - lv) lv_leaves[nl++] = leaves[i];
     int prev = sizes[lv - 1];
     int npk = prev / 2;
-    pm_item *out = (pm_item *)malloc(sizeof(pm_item) * (size_t)(n + npk));
+    pm_item *out = (pm_item *)malloc(sizeof(pm_item) * (size_t)(nl + npk));
     int i = 0, j = 0, k = 0;
-    while (i < n || j < npk) {
+    while (i < nl || j < npk) {
       int take_leaf;
       uint64_t pw = 0;
       if (j < npk) pw = lists[lv - 1][2 * j].weight + lists[lv - 1][2 * j + 1].weight;
-      if (i >= n) take_leaf = 0;
+      if (i >= nl) take_leaf = 0;
       else if (j >= npk) take_leaf = 1;
-      else take_leaf = leaves[i].weight <= pw;
+      else take_leaf = lv_leaves[i].weight <= pw;
       if (take_leaf) {
-        out[k++] = leaves[i++];
+        out[k++] = lv_leaves[i++];
       } else {
         out[k].weight = pw;
         out[k].leaf = 0;
@@ -197,12 +209,43 @@ int orc_code_lengths(const uint64_t *h, int lmax, uint8_t *len_out) {
   int len[256];
   memset(len, 0, sizeof(len));
   int take = 2 * n - 2;
+  if (take > sizes[lmax - 1]) {  /* the caps leave no complete code */
+    for (int lv = 0; lv < lmax; lv++) free(lists[lv]);
+    free(lists);
+    free(sizes);
+    return ORC_EINVAL;
+  }
   for (int idx = 0; idx < take; idx++) pm_count(lists, lmax - 1, idx, len);
   for (int s = 0; s < 256; s++) len_out[s] = (uint8_t)len[s];
   for (int lv = 0; lv < lmax; lv++) free(lists[lv]);
   free(lists);
   free(sizes);
   return ORC_OK;
+}
+
+/* Optimal prefix-code lengths of at most lmax bits for the counts h. */
+int orc_code_lengths(const uint64_t *h, int lmax, uint8_t *len_out) {
+  int cap[256];
+  for (int s = 0; s < 256; s++) cap[s] = lmax;
+  return code_lengths_capped(h, lmax, cap, len_out);
+}
+
+/* As orc_code_lengths, with pair_fit > 0: every symbol whose count is at
+ * least 1/pair_fit of all counts (count * pair_fit >= total) is capped at 6
+ * bits, so that two such codes always fit a 12-bit window; the rest keep the
+ * lmax limit.  If those caps leave no prefix code (more than 64 symbols that
+ * common), the plain limit applies.  pair_fit = 0 is orc_code_lengths. */
+int orc_code_lengths_pair_fit(const uint64_t *h, int lmax, uint32_t pair_fit, uint8_t *len_out) {
+  if (pair_fit == 0) return orc_code_lengths(h, lmax, len_out);
+  uint64_t total = 0;
+  for (int s = 0; s < 256; s++) total += h[s];
+  int cap[256];
+  for (int s = 0; s < 256; s++) {
+    cap[s] = lmax;
+    if (lmax > 6 && h[s] > 0 && (double)h[s] * (double)pair_fit >= (double)total) cap[s] = 6;
+  }
+  if (code_lengths_capped(h, lmax, cap, len_out) == ORC_OK) return ORC_OK;
+  return orc_code_lengths(h, lmax, len_out);
 }
 
 /* ------------------------------------------------------------------ */
@@ -438,8 +481,8 @@ int orc_encode_bound(uint64_t rows, uint64_t cols, uint32_t tr, uint32_t tc, uin
  * in row-major order; record each chunk's bit length, start every tile on a
  * 32-bit word boundary, and store the raw bytes row-major. */
 int orc_encode(const uint16_t *w, uint64_t rows, uint64_t cols, uint64_t ld, uint32_t tr,
-               uint32_t tc, uint32_t s, uint32_t lmax, uint8_t *blob, uint64_t cap,
-               uint64_t *used) {
+               uint32_t tc, uint32_t s, uint32_t lmax, uint32_t pair_fit, uint8_t *blob,
+               uint64_t cap, uint64_t *used) {
   int rc = geom_check(rows, cols, tr, tc, s, lmax);
   if (rc) return rc;
   if (ld < cols || !w || !blob || !used) return ORC_EINVAL;
@@ -454,7 +497,7 @@ int orc_encode(const uint16_t *w, uint64_t rows, uint64_t cols, uint64_t ld, uin
   orc_histogram(e, n, h);
   uint8_t len[256];
   uint16_t code[256];
-  rc = orc_code_lengths(h, (int)lmax, len);
+  rc = orc_code_lengths_pair_fit(h, (int)lmax, pair_fit, len);
   if (!rc) rc = orc_canonical_codes(len, code);
   if (rc) { free(e); free(r); return rc; }
 

@@ -611,3 +611,30 @@ def test_seeded_shape_sweep(i, rows, cols, tr, lmax, batch):
     Y_ref, A_ref = oracle.gemm(w, X)
     for beta in range(batch):
         _check_y(Y[beta], Y_ref[beta], A_ref[beta], False, "sweep %d b%d" % (i, beta))
+
+
+@pytest.mark.parametrize("name,params", [("cfg1", dict(pair_fit=1024)), ("3000x512", dict(pair_fit=64)),
+                                         ("20x40960", dict(tile_rows=4, pair_fit=1024)),
+                                         ("1000x256", dict(tile_rows=16, pair_fit=256))])
+def test_pair_fit_blobs_decode_and_multiply(name, params):
+    # codes capped at 6 bits for the common exponents: same decoders, exact
+    w = _special(name)
+    _say("pair_fit %s %s" % (name, params))
+    b = Blob(w, params)
+    assert np.array_equal(b.host, oracle.encode(w, params.get("tile_rows", 8), 512, 64, 8, params["pair_fit"]))
+    out = torch.full(w.shape, 0x5A5A, dtype=torch.int16, device="cuda")
+    nwc.nwc_decode(b.info, b.dev, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), w)
+    x = workloads.gaussian_bits((w.shape[1],), 1.0, 77)
+    y = torch.empty(w.shape[0], dtype=torch.float32, device="cuda")
+    nwc.nwc_gemv(b.info, b.dev, dev(x), y, b.ws(1))
+    torch.cuda.synchronize()
+    y_ref, a_ref = oracle.gemv(w, x)
+    _check_y(_to_f64(y), y_ref, a_ref, True, "pair_fit gemv")
+    for batch in (4, 8, 16):
+        X = workloads.gaussian_bits((batch, w.shape[1]), 1.0, 80 + batch)
+        Y = _to_f64(_gemm(b, X, True))
+        Y_ref, A_ref = oracle.gemm(w, X)
+        for beta in range(batch):
+            _check_y(Y[beta], Y_ref[beta], A_ref[beta], True, "pair_fit b%d" % beta)

@@ -17,7 +17,7 @@ import workloads
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nwc.h")
 
-DEFAULT = dict(tile_rows=8, tile_cols=512, chunks_per_tile=64, max_code_len=8)
+DEFAULT = dict(tile_rows=8, tile_cols=512, chunks_per_tile=64, max_code_len=8, pair_fit=1024)
 
 
 def _declared_functions():
@@ -47,7 +47,7 @@ def test_status_strings():
 def _oracle_blob(w, p):
     q = dict(DEFAULT)
     q.update(p or {})
-    return oracle.encode(w, q["tile_rows"], q["tile_cols"], q["chunks_per_tile"], q["max_code_len"])
+    return oracle.encode(w, q["tile_rows"], q["tile_cols"], q["chunks_per_tile"], q["max_code_len"], q["pair_fit"])
 
 
 GEOMS = [None, dict(tile_rows=16), dict(tile_rows=32), dict(tile_rows=5, tile_cols=24, chunks_per_tile=3,
@@ -345,3 +345,32 @@ def test_one_hip_runtime_whatever_the_import_order():
     assert out.returncode == 0, out.stderr
     hip, hsa = [eval(l) for l in out.stdout.strip().splitlines()[-2:]]
     assert len(hip) == 1 and len(hsa) == 1, (hip, hsa)
+
+
+@pytest.mark.parametrize("pair_fit", [64, 1024])
+@pytest.mark.parametrize("cid,name", [(1, "w"), (2, "q"), (2, "down"), (3, "gate"), (5, "lm_head")])
+def test_encoder_bytes_equal_oracle_pair_fit(cid, name, pair_fit):
+    w = workloads.weights(cid, name)
+    if w.shape[0] > 4096:
+        w = np.ascontiguousarray(w[:4096])
+    blob = nwc.nwc_encode(w, dict(pair_fit=pair_fit))
+    assert np.array_equal(blob, oracle.encode(w, 8, 512, 64, 8, pair_fit))
+    info = nwc.nwc_inspect(blob)
+    e, _ = oracle.split(w)
+    h = oracle.histogram(e)
+    common = h * pair_fit >= h.sum()
+    assert np.all(np.asarray(info.code_len)[common] <= 6)
+    assert np.array_equal(oracle.decode(blob), w)
+
+
+def test_pair_fit_infeasible_caps_fall_back_like_the_oracle():
+    w = workloads.random_bits((64, 64), 3)     # ~1/256 of the weights per exponent value
+    # all 256 values would be capped at 6 bits, which no prefix code allows:
+    # both sides fall back to the plain limit
+    blob = nwc.nwc_encode(w, dict(pair_fit=1024))
+    assert np.array_equal(blob, oracle.encode(w, 8, 512, 64, 8, 1024))
+    assert np.array_equal(blob, oracle.encode(w, 8, 512, 64, 8, 1))
+    assert np.array_equal(nwc.nwc_encode(w, dict(pair_fit=128)), oracle.encode(w, 8, 512, 64, 8, 128))
+    # pair_fit 1 caps nothing: the plain limit
+    w2 = workloads.weights(1, "w")
+    assert np.array_equal(nwc.nwc_encode(w2, dict(pair_fit=1)), oracle.encode(w2, 8, 512, 64, 8, 0))

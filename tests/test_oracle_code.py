@@ -232,3 +232,46 @@ def _deflate_block_with_slot(data, lmax, slot):
     # next value in canonical order because slot was the last of its length)
     w.code(int(codes[slot]), int(ln[slot]))
     return w.tobytes()
+
+
+def _brute_min_capped(counts, caps):
+    # every length vector with l_s <= caps[s] under Kraft's inequality
+    syms = sorted(counts)
+    c = np.array([counts[s] for s in syms], np.int64)
+    grids = np.array(list(itertools.product(*[range(1, caps[s] + 1) for s in syms])), np.int64)
+    ok = (2.0 ** (-grids)).sum(axis=1) <= 1.0 + 1e-12
+    return int((grids[ok] @ c).min())
+
+
+PAIR_FIT_CASES = []
+_rng2 = np.random.default_rng(4321)
+for n in range(2, 8):
+    for trial in range(4):
+        cnt = np.maximum(1, (10000 * _rng2.random(n) ** 6).astype(int))    # a few heavy, several light
+        syms = _rng2.choice(256, n, replace=False)
+        PAIR_FIT_CASES.append(({int(s): int(c) for s, c in zip(syms, cnt)}, int(_rng2.choice([4, 16, 64]))))
+
+
+@pytest.mark.parametrize("counts,pair_fit", PAIR_FIT_CASES)
+def test_pair_fit_lengths_are_optimal_under_their_caps(counts, pair_fit):
+    # lmax 8; symbols with count * pair_fit >= total are capped at 6 bits
+    h = _hist(counts)
+    total = sum(counts.values())
+    caps = {s: (6 if c * pair_fit >= total else 8) for s, c in counts.items()}
+    ln = oracle.code_lengths(h, 8, pair_fit)
+    assert all(0 < ln[s] <= caps[s] for s in counts)
+    assert abs(sum(2.0 ** -int(ln[s]) for s in counts) - 1.0) < 1e-12
+    assert _cost(h, ln) == _brute_min_capped(counts, caps)
+
+
+def test_pair_fit_zero_is_the_plain_limit_and_caps_can_be_infeasible():
+    rng = np.random.default_rng(9)
+    h = np.zeros(256, np.uint64)
+    h[rng.choice(256, 40, replace=False)] = rng.integers(1, 10 ** 6, 40)
+    assert np.array_equal(oracle.code_lengths(h, 8, 0), oracle.code_lengths(h, 8))
+    # 65 equally common symbols all capped at 6 bits cannot form a prefix code:
+    # the plain limit applies instead
+    h = np.zeros(256, np.uint64)
+    h[:65] = 1000
+    assert np.array_equal(oracle.code_lengths(h, 8, 65), oracle.code_lengths(h, 8))
+    assert int(oracle.code_lengths(h, 8, 65).max()) == 7
