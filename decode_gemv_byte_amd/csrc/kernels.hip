@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDe
 // Rows of W by index (an embedding lookup from the compressed table of a tied
 // LM head): work item (i, tj) decodes column tile tj of the row block that
 // holds row ids[i], each chunk up to that row (the rows of a chunk follow
-// one another in its code stream), one symbol at a time, and writes that
+// one another in its code stream), two codes per table lookup, and writes that
 // row's columns of the tile to out row i.  Any geometry.  An id past the
 // matrix gives a row of zeros.
 __global__ __launch_bounds__(kGenericWaves * kWave) void k_gather(BlobDev b, const uint32_t* __restrict__ ids,
@@ -484,12 +484,22 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_gather(BlobDev b, con
           const uint64_t cc1 = umin64(tile_c1, cc0 + b.v);
           Bits br;
           br.init(buf, bit);
-          for (uint64_t n = (id - row0) * (cc1 - cc0); n > 0; n--) br.one(tab);  // the rows before it
-          for (uint64_t k = cc0; k < cc1; k++) {
-            const uint32_t e = br.one(tab);
-            const uint32_t rb = b.raw[id * b.raw_ld + k];
+          // the rows before it, two codes per table lookup
+          uint64_t skip = (id - row0) * (cc1 - cc0);
+          for (; skip >= 2; skip -= 2) br.pair(tab);
+          if (skip) br.one(tab);
+          const uint8_t* rr = b.raw + id * b.raw_ld;
+          auto put = [&](uint64_t k, uint32_t e) __attribute__((always_inline)) {
+            const uint32_t rb = rr[k];
             orow[k] = static_cast<uint16_t>(((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu));
+          };
+          uint64_t k = cc0;
+          for (; k + 1 < cc1; k += 2) {
+            const uint32_t ent = br.pair(tab);
+            put(k, (ent >> 7) & 0xFFu);
+            put(k + 1, (ent >> 23) & 0xFFu);
           }
+          if (k < cc1) put(k, br.one(tab));
         }
       }
     }
