@@ -387,7 +387,7 @@ struct TileIn {
 
 // ------------------------------------------------------------------ decode
 
-// Generic path: any geometry, one symbol at a time, scalar stores.
+// Generic path: any geometry, two codes per table lookup, scalar stores.
 __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDev b, uint16_t* __restrict__ out,
                                                                           uint64_t ld) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
@@ -422,12 +422,21 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_decode_generic(BlobDe
           const uint64_t cc1 = umin64(tile_c1, cc0 + b.v);
           Bits br;
           br.init(buf, bit);
-          for (uint64_t r = row0; r < r1; r++)
-            for (uint64_t k = cc0; k < cc1; k++) {
-              const uint32_t e = br.one(tab);
-              const uint32_t rb = b.raw[r * b.raw_ld + k];
-              out[r * ld + k] = static_cast<uint16_t>(((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu));
-            }
+          // the chunk's symbols in row order, two codes per table lookup
+          const uint32_t wdt = static_cast<uint32_t>(cc1 - cc0);
+          const uint32_t nsym = static_cast<uint32_t>(r1 - row0) * wdt;
+          auto put = [&](uint32_t idx, uint32_t e) __attribute__((always_inline)) {
+            const uint64_t r = row0 + idx / wdt, k = cc0 + idx % wdt;
+            const uint32_t rb = b.raw[r * b.raw_ld + k];
+            out[r * ld + k] = static_cast<uint16_t>(((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu));
+          };
+          uint32_t idx = 0;
+          for (; idx + 1 < nsym; idx += 2) {
+            const uint32_t ent = br.pair(tab);
+            put(idx, (ent >> 7) & 0xFFu);
+            put(idx + 1, (ent >> 23) & 0xFFu);
+          }
+          if (idx < nsym) put(idx, br.one(tab));
         }
       }
     }
@@ -1175,16 +1184,35 @@ __global__ __launch_bounds__(kGenericWaves * kWave) void k_gemv_generic(BlobDev 
           const uint64_t cc1 = cc0 < tile_c1 ? umin64(tile_c1, cc0 + b.v) : cc0;
           Bits br;
           br.init(buf, bit);
-          for (uint32_t r = 0; r < nrows; r++) {
+          // the chunk's symbols in row order, two codes per table lookup; each
+          // row's products added in column order
+          const uint32_t wdt = static_cast<uint32_t>(cc1 - cc0);
+          if (wdt == 0) {
+            for (uint32_t r = 0; r < nrows; r++) rowsum[r * b.s + c] = 0.0f;
+          } else {
+            const uint32_t nsym = nrows * wdt;
+            uint32_t r = 0, kk = 0;  // row and column of the next symbol
             float a = 0.0f;
-            for (uint64_t k = cc0; k < cc1; k++) {
-              const uint32_t e = br.one(tab);
+            auto add = [&](uint32_t e) __attribute__((always_inline)) {
+              const uint64_t k = cc0 + kk;
               const uint32_t rb = b.raw[(row0 + r) * b.raw_ld + k];
               const uint32_t wbits = (((rb & 0x80u) << 8) | (e << 7) | (rb & 0x7Fu)) << 16;
               const float xf = __builtin_bit_cast(float, static_cast<uint32_t>(x[k]) << 16);
               a = __builtin_fmaf(__builtin_bit_cast(float, wbits), xf, a);
+              if (++kk == wdt) {
+                rowsum[r * b.s + c] = a;
+                a = 0.0f;
+                kk = 0;
+                r++;
+              }
+            };
+            uint32_t idx = 0;
+            for (; idx + 1 < nsym; idx += 2) {
+              const uint32_t ent = br.pair(tab);
+              add((ent >> 7) & 0xFFu);
+              add((ent >> 23) & 0xFFu);
             }
-            rowsum[r * b.s + c] = a;
+            if (idx < nsym) add(br.one(tab));
           }
         }
       }
