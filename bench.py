@@ -1,12 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark: fused decode-GEMV on compressed BF16 weights, one MI355X.
 
-Default workload (2): one batch-1 decode step of a Qwen3-4B-shaped decoder
-layer (q, k, v, o, gate, up, down; seeded synthetic weights, x ~ N(0, 1)),
+Default workload (3): one batch-1 decode step of a Llama-3.1-8B-shaped
+model, the largest single-GPU batch-1 workload: 32 layers of q, k, v, o,
+gate, up, down (seeded synthetic weights with 0.1% outliers, x ~ N(0, 1)),
 launched in the order a decode step needs them, GEMVs that read the same
-activations sharing a launch.  Other workloads:
+activations sharing a launch (128 launches, one graph).  Other workloads:
   1  one 1024x1024 matrix, batch 1
-  3  a Llama-3.1-8B-shaped full step: 32 layers, 128 launches in one graph
+  2  one Qwen3-4B-shaped decoder layer, batch 1
   4  skinny decode-GEMM, 4096x14336 and 14336x4096, --batch 2..16
   5  LM head 128256x4096, --batch 1 or 8
 
@@ -17,8 +18,10 @@ a HIP graph and replayed.
 
 Prints ONE JSON line.  `value` is compressed GB/s (blob + x + y bytes per step
 / step time); the uncompressed-equivalent rate, % of HBM peak, the same GEMVs
-reading plain BF16 (our kernel and torch's), the roofline figure of the
-dominant kernel and the CPU oracle's rate on a bounded sample sit beside it.
+reading plain BF16 (our kernel and torch's), the HBM read rate a plain
+streaming kernel reaches on this GPU (read probe), the roofline figure of the
+dominant kernel and the CPU oracle's rate on a bounded sample (one thread and
+all host cores) sit beside it.
 
 --roofline-only runs just the dominant launch (warm-up + timed repetitions),
 so that a profiler's per-kernel statistics cover exactly that launch.
@@ -32,6 +35,7 @@ import math
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -42,8 +46,40 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0   # dense BF16 matrix-core peak
 STREAM_BYTES = 1.0e9          # device copies cycled per pass, well above the Infinity Cache
 CHECK_ROWS = 256              # rows per matrix checked against an FP64 product
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemv_qwen3_4b_gate_up_traffic.txt")
+PROBE_BYTES = 4 << 30         # read-probe buffer, 16x the Infinity Cache
+DEFAULT_PAIR_FIT = 1024       # the library's default 6-bit cap of common exponents (nwc_params.pair_fit)
 KERNEL_SRC = os.path.join(ROOT, "decode_gemv_byte_amd", "csrc", "kernels.hip")
+
+
+def note(msg):
+    """A progress line on stderr (the JSON result is the one stdout line)."""
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def traffic_file(workload_name, group):
+    return os.path.join(ROOT, "profiles", "k_gemv_%s_%s_traffic.txt" % (workload_name, "_".join(group)))
+
+
+def host_threads():
+    """Host threads this process may use: the cores it is pinned to, capped
+    by OMP_NUM_THREADS when that is set (a shared GPU machine sets it to its
+    CPU share)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ["OMP_NUM_THREADS"]))
+    except (KeyError, ValueError):
+        pass
+    return max(1, n)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def parse():
@@ -51,12 +87,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, help="1..5; 2 = Qwen3-4B-shaped layer (default)")
+    ap.add_argument("--workload", type=int, default=3, help="1..5; 3 = Llama-3.1-8B-shaped step (default)")
     ap.add_argument("--batch", type=int, default=0, help="batch size (0 = the workload's first)")
     ap.add_argument("--copies", type=int, default=0, help="device copies cycled (0 = enough for >= 1 GB)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time of each oracle baseline leg (one thread; all host cores)")
     ap.add_argument("--roofline-reps", type=int, default=200)
     ap.add_argument("--roofline-only", action="store_true", help="time only the dominant launch")
     ap.add_argument("--skip-bf16", action="store_true", help="skip the plain-BF16 comparators")
@@ -72,6 +109,7 @@ def parse():
                          "layers on synthetic weights, compressed vs dense BF16")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB, 5 times (scales HBM byte counters)")
+    ap.add_argument("--probe-only", action="store_true", help="only run the HBM read probe")
     return ap.parse_args()
 
 
@@ -244,12 +282,12 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "reps": 5}))
 
 
-def traffic_from_profile():
+def traffic_from_profile(path):
     """Measured HBM bytes per dominant launch (FETCH_SIZE + WRITE_SIZE, each
     scaled by a copy kernel of known size), if the kernels have not changed
     since the counters were taken; else None."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     fields = dict(l.split(":", 1) for l in text.splitlines() if ":" in l and not l.startswith("#"))
@@ -260,6 +298,35 @@ def traffic_from_profile():
         return int(float(fields["hbm bytes per launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def read_probe(torch, nwc, stream, reps=20):
+    """HBM read rate of a plain streaming kernel (nwc_read_probe) over a 4 GiB
+    buffer, 16x the Infinity Cache: the fastest of three launch sizes, each
+    averaged over `reps` back-to-back launches timed with HIP events on the
+    probe's stream."""
+    buf = torch.ones(PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best = None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for per_cu in (4, 8, 16):
+        groups = cus * per_cu
+        with torch.cuda.stream(stream):
+            for i in range(3):
+                nwc.nwc_read_probe(buf, sink, groups, stream=stream)
+            e0.record(stream)
+            for i in range(reps):
+                nwc.nwc_read_probe(buf, sink, groups, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbps = PROBE_BYTES / (us * 1e-6) / 1e9
+        if best is None or gbps > best["GBps"]:
+            best = {"GBps": round(gbps, 1), "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+                    "bytes": PROBE_BYTES, "workgroups": groups, "avg_launch_us": round(us, 2)}
+    del buf
+    return best
 
 
 def main():
@@ -282,6 +349,9 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.probe_only:
+        print(json.dumps({"read_probe": read_probe(torch, nwc, torch.cuda.Stream())}))
+        return
     wl = workloads.WORKLOADS[args.workload]
     batch = args.batch or wl.batches[0]
     if not 1 <= batch <= 8192:
@@ -305,25 +375,42 @@ def main():
             print("[tune] %s: %s" % ("+".join(g), r.as_dict()), file=sys.stderr, flush=True)
     # the step: every layer's groups in order; a key is (layer, matrix name)
     groups = [[(l, n) for n in g] for l in range(wl.layers) for g in groups_named]
+    # the dominant launch: the group with the most weights, the first such in
+    # step order (layer 0's gate+up in a full step)
+    mats = {m.name: m for m in wl.matrices}
+    gw = [sum(mats[n].rows * mats[n].cols for (_, n) in g) for g in groups]
+    gi = int(np.argmax(gw))
+    if args.roofline_only:   # only the dominant launch's matrices are needed
+        groups = [groups[gi]]
+        gi = 0
     keys = [k for g in groups for k in g]
-    rng = np.random.default_rng(1)
     want_bf16 = not args.skip_bf16 and not args.roofline_only
 
     # ---------------------------------------------------------------- setup
+    # weights drawn and encoded on the host, matrices in parallel (numpy's
+    # generators and the encoder release the interpreter lock)
     t0 = time.time()
     host_blob, info, check, wbf = {}, {}, {}, {}
-    for (l, n) in keys:
+
+    def prepare(k):
+        l, n = k
         w = workloads.weights(wl.cid, n, layer=l)
         blob = nwc.nwc_encode(w, enc_params[n])
-        host_blob[(l, n)] = blob
-        info[(l, n)] = nwc.nwc_inspect(blob)
+        rng = np.random.default_rng(np.random.SeedSequence([1, l, mats[n].mid]))
         rows = np.unique(np.concatenate([rng.choice(w.shape[0], min(CHECK_ROWS, w.shape[0]), replace=False),
                                          [0, w.shape[0] - 1]]))
-        check[(l, n)] = (rows, w[rows].copy())
-        if want_bf16:
-            wbf[(l, n)] = torch.from_numpy(w.view(np.int16)).to(dev)
-        del w
+        return k, w, blob, (rows, w[rows].copy())
+
+    with ThreadPoolExecutor(max_workers=min(8, host_threads())) as ex:
+        for k, w, blob, chk in ex.map(prepare, keys):
+            host_blob[k] = blob
+            info[k] = nwc.nwc_inspect(blob)
+            check[k] = chk
+            if want_bf16:
+                wbf[k] = torch.from_numpy(w.view(np.int16)).to(dev)
+            del w
     enc_s = time.time() - t0
+    note("encoded %d matrices in %.1f s" % (len(keys), enc_s))
 
     def cbytes(k):  # compressed bytes of one GEMV / GEMM: blob + x + y
         return host_blob[k].size + 2 * batch * (info[k].cols + info[k].rows)
@@ -377,8 +464,6 @@ def main():
         for i in range(len(groups)):
             launch(c, i)
 
-    # the dominant launch: the one that moves the most bytes
-    gi = int(np.argmax(gbytes))
     reps = args.roofline_reps
 
     def time_dominant():
@@ -402,9 +487,11 @@ def main():
             a = gbytes[gi] / (us * 1e-6) / 1e9
             return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(a / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic_from_profile() if (args.workload == 2 and batch == 1) else None,
+                    "traffic": (traffic_from_profile(traffic_file(wl.name, [n for (_, n) in groups[gi]]))
+                                if batch == 1 and not params and tuned is None else None),
                     "kernel": "%s (%s)" % (kernel, dom_name), "bytes_per_launch": int(gbytes[gi]),
-                    "avg_launch_us": round(us, 3)}
+                    "avg_launch_us": round(us, 3),
+                    "frac_of_read_probe": (round(a / probe["GBps"], 4) if probe else None)}
         # prefill: the decode writes W' once and the GEMM reads it back, so
         # its bytes are blob + 4 N K + X + Y; past the ridge point the GEMM's
         # flops bound it instead
@@ -423,6 +510,7 @@ def main():
                 "kernel": "%s (%s)" % (kernel, dom_name), "bytes_per_launch": int(g_bytes),
                 "avg_launch_us": round(us, 3)}
 
+    probe = None
     if args.roofline_only:
         us = time_dominant()
         print(json.dumps({"roofline": roofline(us), "config": {"workload": wl.name, "batch": batch}}))
@@ -447,6 +535,7 @@ def main():
         step(0)
     torch.cuda.synchronize()
     verify("after an eager step")
+    note("eager step verified (%d copies on the device)" % copies)
 
     graphs = None
     if not args.no_graph:
@@ -481,7 +570,10 @@ def main():
     verify("after the timed steps")
     value = bytes_c / (ms_per_step * 1e-3) / 1e9
     value_u = bytes_u / (ms_per_step * 1e-3) / 1e9
+    note("timed %d steps: %.4f ms per step" % (args.steps, ms_per_step))
     dom_us = time_dominant()
+    probe = read_probe(torch, nwc, stream)
+    note("dominant launch %.2f us; read probe %.0f GB/s" % (dom_us, probe["GBps"]))
 
     # every GEMV of a one-layer batch-1 step in a single launch (they read
     # independent activations here): what the launch boundaries cost (one
@@ -582,13 +674,14 @@ def main():
     bf16 = None
     if want_bf16:
         bf16 = bf16_comparators(torch, nwc, args, keys, info, wbf, xs, ys, batch, bytes_u, ms_per_step, stream,
-                                zeroed)
+                                zeroed, groups[gi], dom_us, probe)
         wbf.clear()
 
     # ------------------------------------------------------- CPU baseline
+    note("comparators and standalone decode done")
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, keys, info, batch, args.cpu_seconds)
+        cpu = cpu_baseline(wl, keys, info, batch, args.cpu_seconds, args.pair_fit or DEFAULT_PAIR_FIT)
 
     out = {
         "metric": "fused decode-GEMV GB/s (compressed + uncompressed-equiv), % HBM peak, batch 1",
@@ -618,6 +711,8 @@ def main():
         "single_launch_all_gemvs": single,
         "standalone_decode": decode,
         "embedding_gather": gather,
+        "read_probe": probe,
+        "pct_read_probe": round(100.0 * value / probe["GBps"], 2),
         "roofline": roofline(dom_us),
         "cpu_baseline": cpu,
         "wall_s": round(t_wall, 3),
@@ -626,11 +721,14 @@ def main():
     print(json.dumps(out))
 
 
-def bf16_comparators(torch, nwc, args, keys, info, wbf, xs, ys, batch, bytes_u, ms_per_step, stream, zeroed):
+def bf16_comparators(torch, nwc, args, keys, info, wbf, xs, ys, batch, bytes_u, ms_per_step, stream, zeroed,
+                     dom_keys, dom_us, probe):
     """The same GEMVs reading plain BF16 weights: our kernel with the same
     skeleton (batch 1) and the vendor library's product (torch.mv /
     F.linear), same matrices, same launch order, graph-captured, cycling
-    enough device copies to stream from HBM."""
+    enough device copies to stream from HBM.  At batch 1 also the dominant
+    launch's matrices alone through our comparator (one launch each, copies
+    cycled past the Infinity Cache), against the read probe."""
     ub = sum(2 * info[k].rows * info[k].cols for k in keys)
     bcopies = max(1, int(np.ceil(STREAM_BYTES / ub)))
     wdev = [{k: (wbf[k] if c == 0 else wbf[k].clone()) for k in keys} for c in range(bcopies)]
@@ -686,41 +784,90 @@ def bf16_comparators(torch, nwc, args, keys, info, wbf, xs, ys, batch, bytes_u, 
     res["torch"] = dict(op="torch.mv" if batch == 1 else "torch.nn.functional.linear",
                         ms_per_step=round(ms_t, 5), GBps=round(bytes_u / (ms_t * 1e-3) / 1e9, 1),
                         speedup_fused_vs_torch=round(ms_t / ms_per_step, 3))
+    if batch == 1:
+        # the dominant launch's matrices: our comparator alone, copies cycled
+        db = sum(2 * info[k].rows * info[k].cols for k in dom_keys)
+        dcopies = max(2, int(np.ceil(STREAM_BYTES / db)))
+        dw = [{k: (wbf[k] if c == 0 else wbf[k].clone()) for k in dom_keys} for c in range(dcopies)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = args.roofline_reps
+        with torch.cuda.stream(stream):
+            for i in range(10 + reps):
+                if i == 10:
+                    e0.record(stream)
+                for k in dom_keys:
+                    nwc.nwc_gemv_bf16(dw[i % dcopies][k], xs[k][0], yb[k], wsb[k], stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        moved = sum(2 * info[k].rows * info[k].cols + 2 * (info[k].rows + info[k].cols) for k in dom_keys)
+        gbps = moved / (us * 1e-6) / 1e9
+        res["dominant_launch_matrices"] = {
+            "matrices": ["%s@%d" % (n, l) for (l, n) in dom_keys], "launches": len(dom_keys),
+            "us": round(us, 3), "GBps": round(gbps, 1), "frac_of_read_probe": round(gbps / probe["GBps"], 4),
+            "speedup_fused_vs_bf16": round(us / dom_us, 3)}
+        del dw
     return res
 
 
-def cpu_baseline(wl, keys, info, batch, seconds):
-    """The oracle (single-threaded C: bit-serial decode and FP64 GEMV/GEMM) on a
-    bounded sample: 256-row blocks of the workload's matrices, round robin,
-    until `seconds` of CPU work; rate in compressed bytes (blob + x + y) per
-    second of the sampled rows, the same definition as the GPU figure."""
+def cpu_baseline(wl, keys, info, batch, seconds, pair_fit):
+    """The oracle (plain C: bit-serial decode and FP64 GEMV/GEMM) on a bounded
+    sample of the workload: 256-row blocks of its matrices taken round robin
+    (each matrix's first rows first), each encoded by the oracle with the
+    library blob's geometry, code length limit and 6-bit cap (encoding is not
+    timed: the GPU figure excludes it too), then decoded and multiplied.  The
+    blocks are timed on one thread until about `seconds` of work, then the
+    same blocks again through a pool of all the host threads this process may
+    use (wall clock; the oracle's C calls release the interpreter lock).
+    Rate in compressed bytes (blob + x + y) per second, the same definition as
+    the GPU figure."""
     import oracle
     import workloads
 
-    t_total = 0.0
-    bytes_done = 0.0
-    i = 0
     nb = 256
-    while t_total < seconds and i < 1000:
+    threads = host_threads()
+
+    def sample(i):
         layer, name = keys[i % len(keys)]
-        n_rows = info[(layer, name)].rows
-        r0 = (i // len(keys)) * nb % n_rows
-        sub = workloads.weights(wl.cid, name, layer=layer, rows=slice(r0, min(r0 + nb, n_rows)))
-        li = info[(layer, name)]  # the library blob's geometry and code length limit (and the default 6-bit cap)
-        blob = oracle.encode(sub, li.tile_rows, li.tile_cols, li.chunks_per_tile, li.max_code_len, 1024)
+        li = info[(layer, name)]
+        r0 = (i // len(keys)) * nb % li.rows
+        sub = workloads.weights(wl.cid, name, layer=layer, rows=slice(r0, min(r0 + nb, li.rows)))
+        blob = oracle.encode(sub, li.tile_rows, li.tile_cols, li.chunks_per_tile, li.max_code_len, pair_fit)
         x = workloads.activations(wl.cid, name, batch=batch, layer=layer)
-        t = time.perf_counter()
+        return blob, x, blob.size + 2 * batch * (sub.shape[1] + sub.shape[0])
+
+    def work(item):
+        blob, x, _ = item
         wd = oracle.decode(blob)
         if batch == 1:
             oracle.gemv(wd, x[0])
         else:
             oracle.gemm(wd, x)
-        t_total += time.perf_counter() - t
-        bytes_done += blob.size + 2 * batch * (sub.shape[1] + sub.shape[0])
-        i += 1
-    return {"value": round(bytes_done / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d row blocks of 256 rows from the workload's matrices, oracle decode + FP64 %s, "
-                      "%.1f s of single-thread CPU time" % (i, "GEMV" if batch == 1 else "GEMM", t_total)}
+
+    # one thread: blocks prepared `threads` at a time, worked until `seconds`
+    items, t_one = [], 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while t_one < seconds and len(items) < 2000:
+            fresh = list(ex.map(sample, range(len(items), len(items) + threads)))
+            for it in fresh:
+                t = time.perf_counter()
+                work(it)
+                t_one += time.perf_counter() - t
+                items.append(it)
+                if t_one >= seconds:
+                    break
+        # all threads: the same blocks through the pool
+        t = time.perf_counter()
+        list(ex.map(work, items))
+        t_all = time.perf_counter() - t
+    moved = float(sum(it[2] for it in items))
+    return {"value": round(moved / t_all / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(), "logical_cpus_visible": os.cpu_count(),
+            "single_thread": {"value": round(moved / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "seconds": round(t_one, 2)},
+            "sample": "%d row blocks of 256 rows from the workload's matrices (round robin), oracle decode + FP64 "
+                      "%s: %.1f s on one thread, then %.2f s wall on %d threads"
+                      % (len(items), "GEMV" if batch == 1 else "GEMM", t_one, t_all, threads)}
 
 
 if __name__ == "__main__":

@@ -100,17 +100,18 @@ _lib.nwc_blas_create.argtypes = [ctypes.POINTER(_vp)]
 _lib.nwc_blas_destroy.argtypes = [_vp]
 _lib.nwc_prefill_workspace_size.argtypes = [ctypes.POINTER(nwc_info), ctypes.POINTER(_sz)]
 _lib.nwc_gemm_prefill.argtypes = [_vp, ctypes.POINTER(nwc_info), _vp, _vp, _u64, _i, _vp, _u64, _i, _vp, _sz, _vp]
+_lib.nwc_read_probe.argtypes = [_vp, _sz, _vp, _u32, _vp]
 for _f in ("nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode", "nwc_workspace_size", "nwc_gemv",
            "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched", "nwc_decode_batched",
            "nwc_blas_create", "nwc_blas_destroy", "nwc_prefill_workspace_size", "nwc_gemm_prefill",
-           "nwc_gather_rows"):
+           "nwc_gather_rows", "nwc_read_probe"):
     getattr(_lib, _f).restype = _st
 
 # the exported C symbols, for checks against include/nwc.h
 EXPORTS = ("nwc_status_str", "nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode",
            "nwc_workspace_size", "nwc_gemv", "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16",
            "nwc_gemv_batched", "nwc_decode_batched", "nwc_blas_create", "nwc_blas_destroy",
-           "nwc_prefill_workspace_size", "nwc_gemm_prefill", "nwc_gather_rows")
+           "nwc_prefill_workspace_size", "nwc_gemm_prefill", "nwc_gather_rows", "nwc_read_probe")
 
 
 def _check(st: int, where: str):
@@ -346,12 +347,20 @@ def nwc_gemm_prefill(blas: Blas, info: nwc_info, blob_dev, X_dev, Y_dev, ws, str
                                  int(ws.numel() * ws.element_size()), _stream(stream)), "nwc_gemm_prefill")
 
 
-def nwc_gemv_bf16(w_dev, x_dev, y_dev, ws=None, stream=None):
-    """Uncompressed comparator: y = W x with W a device BF16 matrix [rows, cols]."""
+def nwc_gemv_bf16(w_dev, x_dev, y_dev, ws, stream=None):
+    """Uncompressed comparator: y = W x with W a device BF16 matrix [rows, cols]; ws a device byte
+    tensor of nwc_bf16_workspace_size(rows, cols) bytes, zero-filled before its first use."""
     rows, cols = int(w_dev.shape[0]), int(w_dev.shape[1])
     wp, wn = _ws(ws)
     _check(_lib.nwc_gemv_bf16(_dptr(w_dev), rows, cols, int(w_dev.stride(0)), _dptr(x_dev), _dptr(y_dev),
                               _ytype(y_dev), wp, wn, _stream(stream)), "nwc_gemv_bf16")
+
+
+def nwc_read_probe(buf_dev, sink_dev, groups: int = 0, stream=None):
+    """Stream-read every byte of the device tensor buf_dev (HBM read probe); sink_dev a device tensor
+    of at least 4 bytes."""
+    _check(_lib.nwc_read_probe(_dptr(buf_dev), int(buf_dev.numel() * buf_dev.element_size()), _dptr(sink_dev),
+                               int(groups), _stream(stream)), "nwc_read_probe")
 
 
 def info_dict(info: nwc_info) -> dict:

@@ -157,7 +157,7 @@ nwc_status nwc_decode(const nwc_info *info, const void *blob_dev, uint16_t *w_de
  *    zero-filled.
  *  - Fused skinny path (tile_rows 8 or 16, batch 2..16): 0 (ws may be NULL).
  *  - Otherwise FP32 partial sums, one per (column tile, batch row, output
- *    row), for the one-symbol-at-a-time path, which runs a second reduction
+ *    row), for the generic path (any geometry), which runs a second reduction
  *    kernel; contents need not be initialised. */
 nwc_status nwc_workspace_size(const nwc_info *info, int batch, size_t *bytes);
 
@@ -177,7 +177,12 @@ nwc_status nwc_gemv(const nwc_info *info, const void *blob_dev, const uint16_t *
                     void *y_dev, nwc_out_type y_type, void *ws, size_t ws_bytes,
                     void *stream);
 
-/* Several independent fused decode-GEMVs in one launch (count <= 8):
+/* Several independent fused decode-GEMVs in one launch (count <= 8)
+ * ("Unweight: how we compressed an LLM 22% without sacrificing quality",
+ * Direct GPU Decompression: weights decompressed on chip right before the
+ * product, with the execution strategy chosen per weight matrix and batch;
+ * The GPU Memory Bottleneck: decompression must overlap the product or token
+ * generation slows down):
  * y_i = W_i x_i with blob i described by infos[i] and stored at blobs_dev[i],
  * x_dev[i] / y_dev[i] as for nwc_gemv, all outputs of y_type.  For the GEMVs
  * of one decode step that need no result of each other (q/k/v from the same
@@ -195,7 +200,12 @@ nwc_status nwc_gemv_batched(int count, const nwc_info *infos, const void *const 
                             const uint16_t *const *x_dev, void *const *y_dev,
                             nwc_out_type y_type, void *ws, size_t ws_bytes, void *stream);
 
-/* Several independent standalone decodes in one launch (count <= 8): blob i
+/* Several independent standalone decodes in one launch (count <= 8)
+ * ("NWC -- Neural Weight Compression", How it works, bullet
+ * "Dequantization and embedding lookup": dequantization runs on the same
+ * decoder as the fused product; "Unweight ...", Direct GPU Decompression:
+ * the conventional alternative decompresses whole matrices back to HBM):
+ * blob i
  * (infos[i], blobs_dev[i]) written to w_dev[i] with row stride ld[i] >= its
  * cols, exactly as nwc_decode would.  Every blob must have the default chunk
  * geometry (64 chunks of 8 columns, cols % 8 == 0) and all must share
@@ -219,9 +229,15 @@ nwc_status nwc_decode_batched(int count, const nwc_info *infos, const void *cons
 nwc_status nwc_gather_rows(const nwc_info *info, const void *blob_dev, const uint32_t *ids_dev,
                            uint32_t n_ids, uint16_t *out_dev, uint64_t ld, void *stream);
 
-/* Skinny decode-GEMM for batch 2..16: Y[b, n] = sum_k X[b, k] W[n, k] with X
- * (device, batch x cols, row stride ldx) and Y (device, batch x rows, row
- * stride ldy, y_type).  Same decode as nwc_gemv; FP32 accumulation.  Async.
+/* Skinny decode-GEMM for batch 2..16 ("Unweight ...", Direct GPU
+ * Decompression: weights decompressed in on-chip memory feed the matrix
+ * units directly, with a strategy per batch size; "NWC -- Neural Weight
+ * Compression", Status and limitations: batch 1 is the fast path there and a
+ * matrix-core accumulation path is the planned next step):
+ * Y[b, n] = sum_k X[b, k] W[n, k] with X (device, batch x cols, row stride
+ * ldx) and Y (device, batch x rows, row stride ldy, y_type).  Same decode as
+ * nwc_gemv; FP32 accumulation.  From 10 batch rows on (8-row tiles) the
+ * products run on the matrix cores.  Async.
  * Errors: INVALID_ARG (batch outside 2..16), BUFFER_TOO_SMALL, ALIGNMENT, HIP. */
 nwc_status nwc_gemm_skinny(const nwc_info *info, const void *blob_dev, const uint16_t *X_dev,
                            uint64_t ldx, int batch, void *Y_dev, uint64_t ldy,
@@ -256,15 +272,35 @@ nwc_status nwc_gemm_prefill(nwc_blas *h, const nwc_info *info, const void *blob_
                             uint64_t ldy, nwc_out_type y_type, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* Uncompressed comparator: the same GEMV on a plain BF16 matrix (device,
- * rows x cols, row stride ld, cols and ld multiples of 8), with the same
- * tiling, work split, loads and summation order as the fused kernel, reading
- * 2 bytes per weight instead of decoding.  nwc_bf16_workspace_size reports
- * its workspace (currently 0: ws may be NULL).  Async. */
+/* Uncompressed comparator ("NWC -- Neural Weight Compression", opening
+ * section: the fused kernel is measured against the uncompressed matvec):
+ * y = W x on a plain BF16 matrix (device, rows x cols, row stride ld; cols
+ * and ld multiples of 8, W and x 16-byte aligned).  It runs the fused batch-1
+ * kernel itself in a mode that loads each tile's 16 bytes per lane per row of
+ * BF16 weights in place of the raw bytes and exponent codes: the same 8 x 512
+ * tiles, the same equal workgroup ranges, tile claims, next-tile loads 7/8 of
+ * the way through a tile, reductions and exchange chain, so the two differ
+ * only in the bytes they read and the decode.  ws (device, 256-byte aligned,
+ * at least nwc_bf16_workspace_size bytes: one 64-bit slot per tile row) must
+ * be zero-filled before its first use; every call leaves it zero-filled.
+ * Same concurrency rule as nwc_gemv.  Async.
+ * Errors: INVALID_ARG, BUFFER_TOO_SMALL, ALIGNMENT, UNSUPPORTED, HIP. */
 nwc_status nwc_bf16_workspace_size(uint64_t rows, uint64_t cols, size_t *bytes);
 nwc_status nwc_gemv_bf16(const uint16_t *w_dev, uint64_t rows, uint64_t cols, uint64_t ld,
                          const uint16_t *x_dev, void *y_dev, nwc_out_type y_type, void *ws,
                          size_t ws_bytes, void *stream);
+
+/* HBM read probe ("Unweight ...", The GPU Memory Bottleneck: every generated
+ * token reads the weights from HBM, so the achievable read rate bounds
+ * decoding): a plain streaming read of `bytes` (rounded down to 16) from
+ * buf_dev (device, 16-byte aligned), 8 loads of 16 bytes in flight per lane,
+ * in `groups` workgroups of 256 lanes (0 = 8 per compute unit).  sink_dev
+ * (device, 4 bytes, 4-byte aligned) is written only for a value no realistic
+ * input produces, so the loads cannot be optimised away.  The caller times
+ * it (bytes / duration) to know what a kernel can reach on this GPU.  Async.
+ * Errors: INVALID_ARG, ALIGNMENT, HIP. */
+nwc_status nwc_read_probe(const void *buf_dev, size_t bytes, uint32_t *sink_dev, uint32_t groups,
+                          void *stream);
 
 #ifdef __cplusplus
 }

@@ -201,7 +201,8 @@ def test_workspace_sizes():
     tr32 = nwc.nwc_inspect(nwc.nwc_encode(workloads.gaussian_bits((100, 1504), 0.02, 2), dict(tile_rows=32)))
     assert nwc.nwc_workspace_size(tr32, 1) == up(4 * 3 * 32 * 8)
     assert nwc.nwc_workspace_size(tr32, 8) == 3 * 8 * 100 * 4
-    assert nwc.nwc_bf16_workspace_size(100, 1500) == 0
+    # the comparator: one 64-bit exchange slot per 8-row tile row (13 x 3 tiles of 8 x 512)
+    assert nwc.nwc_bf16_workspace_size(100, 1500) == up(13 * 3 * 8 * 8)
 
 
 def test_device_calls_validate_before_launch():
@@ -239,7 +240,7 @@ def test_device_calls_validate_before_launch():
     bad = nwc.nwc_info.from_buffer_copy(info)
     bad.n_tiles += 1
     assert L.nwc_gemv(ctypes.byref(bad), A, A, A, 0, A, W, None) == nwc.NWC_ERR_INVALID_ARG
-    # the one-symbol-at-a-time path needs its workspace
+    # the generic path (odd geometry) needs its workspace
     gblob = nwc.nwc_encode(workloads.gaussian_bits((64, 500), 0.02, 2))
     ginfo = nwc.nwc_inspect(gblob)
     gws = nwc.nwc_workspace_size(ginfo, 1)
@@ -248,9 +249,18 @@ def test_device_calls_validate_before_launch():
     assert L.nwc_gemv(gref, A, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
     assert L.nwc_gemv(gref, A, A, A, 0, A, gws - 4, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
     assert L.nwc_gemv(gref, A, A, A, 0, A + 4, gws, None) == nwc.NWC_ERR_ALIGNMENT
-    assert L.nwc_gemv_bf16(A, 64, 512, 500, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_gemv_bf16(A, 64, 500, 512, A, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
-    assert L.nwc_gemv_bf16(A, 64, 512, 512, A + 8, A, 0, None, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    BW = nwc.nwc_bf16_workspace_size(64, 512)
+    assert L.nwc_gemv_bf16(A, 64, 512, 500, A, A, 0, A, BW, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_bf16(A, 64, 512, 512, A, A, 0, None, BW, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_gemv_bf16(A, 64, 500, 512, A, A, 0, A, BW, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_bf16(A, 64, 512, 512, A + 8, A, 0, A, BW, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_bf16(A, 64, 512, 512, A, A, 0, A + 16, BW, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_gemv_bf16(A, 64, 512, 512, A, A, 0, A, BW - 8, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
+    # the read probe
+    assert L.nwc_read_probe(None, 1 << 20, A, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_read_probe(A, 8, A, 0, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_read_probe(A + 8, 1 << 20, A, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_read_probe(A, 1 << 20, A + 2, 0, None) == nwc.NWC_ERR_ALIGNMENT
     # grouped launch: count, NULL arrays, per-entry checks, geometry mix
     infos = (nwc.nwc_info * 2)(info, info)
     V2 = ctypes.c_void_p * 2

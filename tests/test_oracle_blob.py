@@ -183,13 +183,19 @@ def test_decode_table_entries():
             assert ent >> 31 == 1 and ent & 0xF == l0 and (ent >> 23) & 0xFF == 0
 
 
-@pytest.mark.parametrize("cid,name", [(1, "w"), (2, "k"), (3, "k"), (5, "lm_head")])
-def test_exponent_bits_within_one_bit_of_entropy(cid, name):
+# (tile rows, length limit, 6-bit cap of common exponents): the shipped
+# default, the short-code variant, and the plain optimal code at limit 12
+CODES = [(8, 8, 1024), (8, 6, 0), (16, 12, 0)]
+
+
+@pytest.mark.parametrize("tr,lmax,pair_fit", CODES)
+@pytest.mark.parametrize("cid,name", [(1, "w"), (2, "k"), (3, "k"), (3, "gate"), (5, "lm_head")])
+def test_exponent_bits_within_one_bit_of_entropy(cid, name, tr, lmax, pair_fit):
     wl = workloads.WORKLOADS[cid]
     m = wl.matrix(name)
     rows = slice(0, min(m.rows, 1024))
     w = workloads.weights(cid, name, rows=rows)
-    blob = oracle.encode(w, 16, 512, 64, 12)
+    blob = oracle.encode(w, tr, 512, 64, lmax, pair_fit)
     e, _ = oracle.split(w)
     H = oracle.entropy_bits(oracle.histogram(e))
     rep = oracle.size_report(blob)
