@@ -43,6 +43,7 @@ NWC_ERR_BAD_FORMAT = -3
 NWC_ERR_UNSUPPORTED = -4
 NWC_ERR_ALIGNMENT = -5
 NWC_ERR_HIP = -6
+NWC_ERR_SCRATCH_LIMIT = -7
 NWC_OUT_BF16 = 0
 NWC_OUT_F32 = 1
 
@@ -101,17 +102,20 @@ _lib.nwc_blas_destroy.argtypes = [_vp]
 _lib.nwc_prefill_workspace_size.argtypes = [ctypes.POINTER(nwc_info), ctypes.POINTER(_sz)]
 _lib.nwc_gemm_prefill.argtypes = [_vp, ctypes.POINTER(nwc_info), _vp, _vp, _u64, _i, _vp, _u64, _i, _vp, _sz, _vp]
 _lib.nwc_read_probe.argtypes = [_vp, _sz, _vp, _u32, _vp]
+_lib.nwc_noalloc_scratch_bytes.argtypes = [ctypes.POINTER(_sz)]
+_lib.nwc_gemv_noalloc.argtypes = [ctypes.POINTER(nwc_info), _vp, _vp, _vp, _i, _vp]
 for _f in ("nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode", "nwc_workspace_size", "nwc_gemv",
            "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched", "nwc_decode_batched",
            "nwc_blas_create", "nwc_blas_destroy", "nwc_prefill_workspace_size", "nwc_gemm_prefill",
-           "nwc_gather_rows", "nwc_read_probe"):
+           "nwc_gather_rows", "nwc_read_probe", "nwc_noalloc_scratch_bytes", "nwc_gemv_noalloc"):
     getattr(_lib, _f).restype = _st
 
 # the exported C symbols, for checks against include/nwc.h
 EXPORTS = ("nwc_status_str", "nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode",
            "nwc_workspace_size", "nwc_gemv", "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16",
            "nwc_gemv_batched", "nwc_decode_batched", "nwc_blas_create", "nwc_blas_destroy",
-           "nwc_prefill_workspace_size", "nwc_gemm_prefill", "nwc_gather_rows", "nwc_read_probe")
+           "nwc_prefill_workspace_size", "nwc_gemm_prefill", "nwc_gather_rows", "nwc_read_probe",
+           "nwc_noalloc_scratch_bytes", "nwc_gemv_noalloc")
 
 
 def _check(st: int, where: str):
@@ -257,6 +261,19 @@ def nwc_gemv(info: nwc_info, blob_dev, x_dev, y_dev, ws=None, stream=None):
     wp, wn = _ws(ws)
     _check(_lib.nwc_gemv(ctypes.byref(info), _dptr(blob_dev), _dptr(x_dev), _dptr(y_dev), _ytype(y_dev),
                          wp, wn, _stream(stream)), "nwc_gemv")
+
+
+def nwc_noalloc_scratch_bytes() -> int:
+    out = _sz(0)
+    _check(_lib.nwc_noalloc_scratch_bytes(ctypes.byref(out)), "nwc_noalloc_scratch_bytes")
+    return out.value
+
+
+def nwc_gemv_noalloc(info: nwc_info, blob_dev, x_dev, y_dev, stream=None):
+    """y = W x like nwc_gemv, with no workspace: the library's static per-device scratch holds the
+    exchange slots (calls that overlap on one GPU race)."""
+    _check(_lib.nwc_gemv_noalloc(ctypes.byref(info), _dptr(blob_dev), _dptr(x_dev), _dptr(y_dev), _ytype(y_dev),
+                                 _stream(stream)), "nwc_gemv_noalloc")
 
 
 def gemv_batched_workspace_size(infos) -> int:

@@ -1376,6 +1376,24 @@ __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p,
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// ------------------------------------------ static scratch (no allocation)
+
+// Device memory of nwc_gemv_noalloc: the batch-1 exchange-chain slots live in
+// this file-scope array instead of a caller's workspace.  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it only stands in for the
+// symbol); it uses the address hipGetSymbolAddress returns for the device.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
+
+// Zero n 64-bit words (a kernel rather than a memset, so that a captured
+// graph replays it correctly).
+__global__ __launch_bounds__(256) void k_zero(uint64_t* __restrict__ p, uint64_t n) {
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<uint64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
 // ------------------------------------------------------------- host glue
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -1714,6 +1732,7 @@ const char* nwc_status_str(nwc_status s) {
     case NWC_ERR_UNSUPPORTED: return "NWC_ERR_UNSUPPORTED";
     case NWC_ERR_ALIGNMENT: return "NWC_ERR_ALIGNMENT";
     case NWC_ERR_HIP: return "NWC_ERR_HIP";
+    case NWC_ERR_SCRATCH_LIMIT: return "NWC_ERR_SCRATCH_LIMIT";
   }
   return "NWC_ERR_UNKNOWN";
 }
@@ -1862,6 +1881,64 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
 nwc_status nwc_gemv(const nwc_info* info, const void* blob_dev, const uint16_t* x_dev, void* y_dev,
                     nwc_out_type y_type, void* ws, size_t ws_bytes, void* stream) {
   return gemm_common(info, blob_dev, x_dev, 0, 1, y_dev, 0, y_type, ws, ws_bytes, stream);
+}
+
+// Per-device address of `scratch`, looked up once per device with that
+// device current (each GPU holds its own copy of the array).
+namespace {
+constexpr int kMaxDevices = 64;
+struct ScratchAddr {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+nwc_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return NWC_ERR_HIP;
+  if (dev >= kMaxDevices) return NWC_ERR_UNSUPPORTED;
+  ScratchAddr& sa = g_scratch[dev];
+  std::call_once(sa.once, [&sa] { sa.err = hipGetSymbolAddress(&sa.ptr, HIP_SYMBOL(scratch)); });
+  if (sa.err != hipSuccess || !sa.ptr) return NWC_ERR_HIP;
+  *out = sa.ptr;
+  return NWC_OK;
+}
+}  // namespace
+
+nwc_status nwc_noalloc_scratch_bytes(size_t* bytes) {
+  if (!bytes) return NWC_ERR_INVALID_ARG;
+  *bytes = kScratchBytes;
+  return NWC_OK;
+}
+
+nwc_status nwc_gemv_noalloc(const nwc_info* info, const void* blob_dev, const uint16_t* x_dev, void* y_dev,
+                            nwc_out_type y_type, void* stream) {
+  size_t need = 0;
+  if (!info || nwc_workspace_size(info, 1, &need) != NWC_OK) return NWC_ERR_INVALID_ARG;
+  nwc::Geometry g;
+  nwc::info_geometry(info, &g);
+  const bool fast = g.s == 64 && g.v == 8 && (g.tr == 4 || g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
+  if (!fast) return NWC_ERR_UNSUPPORTED;          // only the fused path: its slots start and end zero
+  if (need > kScratchBytes) return NWC_ERR_SCRATCH_LIMIT;
+  // every check of nwc_gemv before anything is looked up or enqueued (an
+  // aligned placeholder stands for the scratch's address)
+  nwc_status st = gemm_common(info, blob_dev, x_dev, 0, 1, y_dev, 0, y_type, reinterpret_cast<void*>(uintptr_t{256}),
+                              need, stream, true);
+  if (st) return st;
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st) return st;
+  // the slots this call uses start at zero whatever an earlier call left
+  // (one that raced with another, say): clear them on the caller's stream
+  const uint64_t words = need / 8;
+  const int cus = cu_count();
+  if (cus < 1) return NWC_ERR_HIP;
+  const unsigned grid = static_cast<unsigned>(std::min<uint64_t>((words + 255) / 256, static_cast<uint64_t>(cus) * 4));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch(k_zero, dim3(grid), dim3(256), 0, s, static_cast<uint64_t*>(ws), words);
+  if (st) return st;
+  return gemm_common(info, blob_dev, x_dev, 0, 1, y_dev, 0, y_type, ws, need, stream);
 }
 
 nwc_status nwc_gemv_batched(int count, const nwc_info* infos, const void* const* blobs_dev,

@@ -43,7 +43,8 @@
  *    read to the blob, so it yields wrong numbers, never a memory fault.
  *  - Results are deterministic: a fixed summation order, no floating-point
  *    atomics, so repeated calls give bitwise-identical outputs.
- *  - Functions are reentrant; the library holds no mutable global state.
+ *  - Functions are reentrant; the library holds no mutable global state,
+ *    except nwc_gemv_noalloc's per-device static scratch (see there).
  */
 #ifndef NWC_H
 #define NWC_H
@@ -62,7 +63,8 @@ typedef enum {
   NWC_ERR_BAD_FORMAT = -3,       /* blob fails validation */
   NWC_ERR_UNSUPPORTED = -4,      /* valid request the library cannot run */
   NWC_ERR_ALIGNMENT = -5,        /* pointer or leading dimension misaligned */
-  NWC_ERR_HIP = -6               /* a HIP runtime call or launch failed */
+  NWC_ERR_HIP = -6,              /* a HIP runtime call or launch failed */
+  NWC_ERR_SCRATCH_LIMIT = -7     /* needs more than the static scratch holds */
 } nwc_status;
 
 typedef enum {
@@ -176,6 +178,27 @@ nwc_status nwc_workspace_size(const nwc_info *info, int batch, size_t *bytes);
 nwc_status nwc_gemv(const nwc_info *info, const void *blob_dev, const uint16_t *x_dev,
                     void *y_dev, nwc_out_type y_type, void *ws, size_t ws_bytes,
                     void *stream);
+
+/* nwc_gemv without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same fused kernel and launch as nwc_gemv, with its
+ * exchange slots in a static device array of the library, `scratch`
+ * (nwc_noalloc_scratch_bytes: 16 MiB), that each GPU the library runs on
+ * holds until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); it clears the slots it needs with a small
+ * kernel on `stream`, then runs the product, so y has the same bits as
+ * nwc_gemv's.  The first call on a device looks the array's address up.
+ * Only the fused path: default chunk geometry (64 chunks of 8 columns),
+ * tile_rows 4, 8, 16 or 32, cols % 8 == 0.  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (different streams, or
+ * different host threads) race and give wrong results; order them on one
+ * stream or with events.  Async.
+ * Errors: as nwc_gemv, plus UNSUPPORTED (another geometry) and SCRATCH_LIMIT
+ * (nwc_workspace_size(info, 1) above the scratch size; the LM head of
+ * 128256 x 4096 at 8-row tiles needs 7.8 MiB). */
+nwc_status nwc_noalloc_scratch_bytes(size_t *bytes);
+nwc_status nwc_gemv_noalloc(const nwc_info *info, const void *blob_dev, const uint16_t *x_dev,
+                            void *y_dev, nwc_out_type y_type, void *stream);
 
 /* Several independent fused decode-GEMVs in one launch (count <= 8)
  * ("Unweight: how we compressed an LLM 22% without sacrificing quality",
