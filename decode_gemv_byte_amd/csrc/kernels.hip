@@ -287,6 +287,29 @@ __device__ __forceinline__ uint32_t decode_pair(R& rd, const uint32_t* tab) {
 }
 __device__ __forceinline__ uint32_t Bits::pair(const uint32_t* tab) { return decode_pair(*this, tab); }
 
+// Four exponents (two pair entries) from one window read: the second lookup
+// reads the window shifted by the first entry's total length (a 32-bit shift
+// uses only the low 5 bits of its amount, which hold that length).  The
+// window holds 30 stream bits, so this needs every pair to fit 18 bits:
+// codes of at most 9 bits.  When some lane's first or second entry holds a
+// single code (its pair did not fit the 12-bit window), the wavefront redoes
+// both pairs one lookup chain at a time; with codes of at most 6 bits (FIT2)
+// every pair fits and that test is dropped.
+template <bool FIT2, class R>
+__device__ __forceinline__ void decode_quad(R& rd, const uint32_t* tab, uint32_t& e1, uint32_t& e2) {
+  const uint32_t win = rd.window();
+  e1 = tab[(win & 0x3FFCu) >> 2];
+  e2 = tab[((win >> e1) & 0x3FFCu) >> 2];
+  if constexpr (!FIT2) {
+    if (__builtin_amdgcn_ballot_w64(static_cast<int32_t>(e1 | e2) < 0)) {
+      e1 = decode_pair<false>(rd, tab);
+      e2 = decode_pair<false>(rd, tab);
+      return;
+    }
+  }
+  rd.advance((e1 & 0x1Fu) + (e2 & 0x1Fu));
+}
+
 // Two BF16 weights from a pair entry and 4 raw bytes; `hi` selects raw bytes
 // 2,3 instead of 0,1.
 __device__ __forceinline__ uint32_t assemble(uint32_t ent, uint32_t raw4, bool hi) {
@@ -594,6 +617,11 @@ struct TileRegs {
   // of rows [0, TR / 2): no dependence on the tile's word offsets
   __device__ __forceinline__ void load_planes(const BlobDev& b, const uint16_t* xp, uint64_t ldx, uint32_t nxr,
                                               uint64_t ti, uint32_t tj) {
+    load_meta(b, xp, ldx, nxr, ti, tj);
+    load_raw<0, TR / 2>(b, ti, tj);
+  }
+  __device__ __forceinline__ void load_meta(const BlobDev& b, const uint16_t* xp, uint64_t ldx, uint32_t nxr,
+                                            uint64_t ti, uint32_t tj) {
     const uint32_t lane = lane_id();
     const uint64_t t = ti * b.n_tc + tj;
     const uint64_t row0 = ti * TR;
@@ -610,7 +638,6 @@ struct TileRegs {
         x[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                              buf_rsrc(xp + k * ldx + col0, (b.cols - col0) * 2), lane * 16, 0, 0));
     }
-    load_raw<0, TR / 2>(b, ti, tj);
   }
   __device__ __forceinline__ void load_rest(const BlobDev& b, uint64_t ti, uint32_t tj) {
     load_raw<TR / 2, TR>(b, ti, tj);
@@ -739,7 +766,7 @@ __device__ __forceinline__ uint32_t interleave(const uint32_t* buf, uint32_t w0,
 // slot, raw bytes and x in registers) into this lane's row sums over its 8
 // columns.  Rows past the matrix edge (last row block only; a wave-uniform
 // test) are not decoded and keep their zero sums.
-template <int TR, int NX, int R0, int R1, bool FIT2 = false>
+template <int TR, int NX, int R0, int R1, bool FIT2 = false, bool QUAD = false>
 __device__ __forceinline__ void gemv_rows(const TileRegs<TR, NX>& in, LaneBits& br, const uint32_t* tab,
                                           float (&acc)[TR * NX]) {
 #pragma unroll
@@ -751,25 +778,32 @@ __device__ __forceinline__ void gemv_rows(const TileRegs<TR, NX>& in, LaneBits& 
       // each product is pinned next to its decode step: left alone, the
       // compiler defers all of them to the end of the tile and keeps every
       // decoded pair live, which costs occupancy
-      const uint32_t p0 = assemble(decode_pair<FIT2>(br, tab), in.raw[r].x, false);
+      uint32_t e0, e1, e2, e3;
+      if constexpr (QUAD) decode_quad<FIT2>(br, tab, e0, e1);
+      else e0 = decode_pair<FIT2>(br, tab);
+      const uint32_t p0 = assemble(e0, in.raw[r].x, false);
 #pragma unroll
       for (int k = 0; k < NX; k++) {
         a[k] = dot2(p0, in.x[k].x, a[k]);
         asm volatile("" : "+v"(a[k]));
       }
-      const uint32_t p1 = assemble(decode_pair<FIT2>(br, tab), in.raw[r].x, true);
+      if constexpr (!QUAD) e1 = decode_pair<FIT2>(br, tab);
+      const uint32_t p1 = assemble(e1, in.raw[r].x, true);
 #pragma unroll
       for (int k = 0; k < NX; k++) {
         a[k] = dot2(p1, in.x[k].y, a[k]);
         asm volatile("" : "+v"(a[k]));
       }
-      const uint32_t p2 = assemble(decode_pair<FIT2>(br, tab), in.raw[r].y, false);
+      if constexpr (QUAD) decode_quad<FIT2>(br, tab, e2, e3);
+      else e2 = decode_pair<FIT2>(br, tab);
+      const uint32_t p2 = assemble(e2, in.raw[r].y, false);
 #pragma unroll
       for (int k = 0; k < NX; k++) {
         a[k] = dot2(p2, in.x[k].z, a[k]);
         asm volatile("" : "+v"(a[k]));
       }
-      const uint32_t p3 = assemble(decode_pair<FIT2>(br, tab), in.raw[r].y, true);
+      if constexpr (!QUAD) e3 = decode_pair<FIT2>(br, tab);
+      const uint32_t p3 = assemble(e3, in.raw[r].y, true);
 #pragma unroll
       for (int k = 0; k < NX; k++) {
         a[k] = dot2(p3, in.x[k].w, a[k]);
@@ -845,9 +879,10 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 // W' (job.y, rows of g.ldy elements) once the next tile's data is in; 16
 // for Y = X W^T with up to 16 X rows on the matrix cores (8-row tiles: the
 // decoded tile goes through LDS into MFMA operand layout).
-template <int TR, int MAXW, int NB, bool FIT2 = false>
+template <int TR, int MAXW, int NB, bool FIT2 = false, bool QUAD = false>
 __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   constexpr bool RAW16 = NB == kRawBf16;
+  static_assert(!QUAD || NB == 1, "two pairs per window: batch 1");
   constexpr bool DECODE = NB < 0;
   constexpr bool MF = NB == 16;
   constexpr bool SKINNY = !RAW16 && (NB == 0 || NB > 1);
@@ -1118,7 +1153,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     if constexpr (NB <= 0) {
       if (in.active) decode_rows<TR, NX, 0, PRE, FIT2>(in, br, tab, wv);
     } else if constexpr (!MF) {
-      if (in.active) gemv_rows<TR, NX, 0, PRE, FIT2>(in, br, tab, acc);
+      if (in.active) gemv_rows<TR, NX, 0, PRE, FIT2, QUAD>(in, br, tab, acc);
     }
     // the rest of the raw bytes, then the next tile's loads: they go out
     // PRE rows into this tile and nothing touches them before the next
@@ -1172,7 +1207,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
         if ((lane & 1u) == 0 && beta < g.batch) gsum[((t - r0) * TR + vr) * g.batch + beta] = sv;
       }
     } else if constexpr (!MF) {
-      if (in.active) gemv_rows<TR, NX, PRE, TR, FIT2>(in, br, tab, acc);
+      if (in.active) gemv_rows<TR, NX, PRE, TR, FIT2, QUAD>(in, br, tab, acc);
       // lanes (64 / (TR NB)) v .. hold sum v: row v / NB, X row v % NB
       const float s = reduce_rows<TR * NA>(acc);
       constexpr uint32_t lanes_per_sum = kWave / (TR * NA);
@@ -1588,7 +1623,7 @@ GemvPlan plan_skinny(const Launch& L, int batch, uint64_t cap, size_t group_lds)
 // wavefronts per workgroup are the size with the most resident wavefronts
 // per CU (registers and LDS both count, the ranges' LDS included), the
 // larger size on a tie.
-template <int TR, int MAXW, int NB, bool FIT2 = false>
+template <int TR, int MAXW, int NB, bool FIT2 = false, bool QUAD = false>
 nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y, uint8_t* const* ws, int count,
                        int y_f32, hipStream_t s, int batch = 1, uint64_t ldx = 0, uint64_t ldy = 0,
                        const uint64_t* ld_out = nullptr) {
@@ -1619,8 +1654,9 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
       *k = 0;
       return hipSuccess;
     }
-    hipError_t e = set_lds(k_gemv<TR, MAXW, NB>, lds);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(k, k_gemv<TR, MAXW, NB>, n * kWave, lds);
+    hipError_t e = set_lds(k_gemv<TR, MAXW, NB, FIT2, QUAD>, lds);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(k, k_gemv<TR, MAXW, NB, FIT2, QUAD>, n * kWave, lds);
     return e;
   };
   // the LDS a workgroup has for its ranges' sums when k workgroups of n
@@ -1686,21 +1722,45 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   g.ldy = ldy;
   g.batch = static_cast<uint32_t>(batch);
   const size_t lds = nw * per_wave + best.group_lds(sums);
-  if (set_lds(k_gemv<TR, MAXW, NB, FIT2>, lds) != hipSuccess) return NWC_ERR_HIP;
-  return launch(k_gemv<TR, MAXW, NB, FIT2>, dim3(groups), dim3(nw * kWave), lds, s, g);
+  if (set_lds(k_gemv<TR, MAXW, NB, FIT2, QUAD>, lds) != hipSuccess) return NWC_ERR_HIP;
+  return launch(k_gemv<TR, MAXW, NB, FIT2, QUAD>, dim3(groups), dim3(nw * kWave), lds, s, g);
+}
+
+// The batch-1 launch for the matrices' tile height: two pairs per window
+// read when every code is <= 9 bits, and without the second-lookup test when
+// every code is <= 6 bits.
+template <int TR, int MAXW, typename... A>
+nwc_status launch_batch1(const Launch* L, int count, A... a) {
+  bool fit2 = true, quad = true;
+  for (int j = 0; j < count; j++) {
+    fit2 = fit2 && L[j].max_code_len <= 6;
+    quad = quad && L[j].max_code_len <= 9;
+  }
+  if (fit2) return launch_gemv<TR, MAXW, 1, true, true>(L, a...);
+  if (quad) return launch_gemv<TR, MAXW, 1, false, true>(L, a...);
+  return launch_gemv<TR, MAXW, 1, false, false>(L, a...);
 }
 
 // The batch-1 (NB = 1) or decode (NB = -1) launch for the matrices' tile
 // height, with the second-lookup-free decode when every code is <= 6 bits.
 template <int NB, typename... A>
 nwc_status launch_fused(const Launch* L, int count, A... a) {
-  bool fit2 = true;
-  for (int j = 0; j < count; j++) fit2 = fit2 && L[j].max_code_len <= 6;
-  switch (L[0].b.tr) {
-    case 4: return fit2 ? launch_gemv<4, 16, NB, true>(L, a...) : launch_gemv<4, 16, NB>(L, a...);
-    case 8: return fit2 ? launch_gemv<8, 16, NB, true>(L, a...) : launch_gemv<8, 16, NB>(L, a...);
-    case 16: return fit2 ? launch_gemv<16, 8, NB, true>(L, a...) : launch_gemv<16, 8, NB>(L, a...);
-    default: return fit2 ? launch_gemv<32, 4, NB, true>(L, a...) : launch_gemv<32, 4, NB>(L, a...);
+  if constexpr (NB == 1) {
+    switch (L[0].b.tr) {
+      case 4: return launch_batch1<4, 16>(L, count, a...);
+      case 8: return launch_batch1<8, 16>(L, count, a...);
+      case 16: return launch_batch1<16, 8>(L, count, a...);
+      default: return launch_batch1<32, 4>(L, count, a...);
+    }
+  } else {
+    bool fit2 = true;
+    for (int j = 0; j < count; j++) fit2 = fit2 && L[j].max_code_len <= 6;
+    switch (L[0].b.tr) {
+      case 4: return fit2 ? launch_gemv<4, 16, NB, true>(L, a...) : launch_gemv<4, 16, NB>(L, a...);
+      case 8: return fit2 ? launch_gemv<8, 16, NB, true>(L, a...) : launch_gemv<8, 16, NB>(L, a...);
+      case 16: return fit2 ? launch_gemv<16, 8, NB, true>(L, a...) : launch_gemv<16, 8, NB>(L, a...);
+      default: return fit2 ? launch_gemv<32, 4, NB, true>(L, a...) : launch_gemv<32, 4, NB>(L, a...);
+    }
   }
 }
 
