@@ -64,10 +64,12 @@ def lib() -> ctypes.CDLL:
         L.orc_histogram.argtypes = [u8p, u64, u64p]
         L.orc_code_lengths.argtypes = [u64p, ctypes.c_int, u8p]
         L.orc_code_lengths_pair_fit.argtypes = [u64p, ctypes.c_int, u32, u8p]
+        L.orc_code_lengths_unary.argtypes = [u64p, ctypes.c_int, u8p]
         L.orc_canonical_codes.argtypes = [u8p, u16p]
         L.orc_decode_table.argtypes = [u8p, u32p]
         L.orc_encode_bound.argtypes = [u64, u64, u32, u32, u32, u32, u64p]
         L.orc_encode.argtypes = [u16p, u64, u64, u64, u32, u32, u32, u32, u32, u8p, u64, u64p]
+        L.orc_encode_family.argtypes = [u16p, u64, u64, u64, u32, u32, u32, u32, u32, u32, u8p, u64, u64p]
         L.orc_decode.argtypes = [u8p, u64, u16p, u64]
         L.orc_decode_chunk.argtypes = [u8p, u64, u64, u32, u8p, u64]
         L.orc_decode_chunk.restype = ctypes.c_int64
@@ -152,6 +154,19 @@ def code_lengths(h, lmax: int, pair_fit: int = 0) -> np.ndarray:
     return out
 
 
+def code_lengths_unary(h, lmax: int) -> np.ndarray:
+    """Lengths of the ranked unary code with an escape of at most lmax bits
+    (see orc_code_lengths_unary)."""
+    h = np.ascontiguousarray(h, np.uint64)
+    if h.shape != (256,):
+        raise ValueError("histogram must have 256 bins")
+    out = np.zeros(256, np.uint8)
+    rc = lib().orc_code_lengths_unary(_p(h, ctypes.c_uint64), int(lmax), _p(out, ctypes.c_uint8))
+    if rc:
+        raise ValueError("code_lengths_unary failed (%d)" % rc)
+    return out
+
+
 def canonical_codes(lengths) -> np.ndarray:
     ln = np.ascontiguousarray(lengths, np.uint8)
     out = np.zeros(256, np.uint16)
@@ -180,10 +195,11 @@ def encode_bound(rows, cols, tile_rows, tile_cols, chunks_per_tile, max_code_len
 
 
 def encode(w, tile_rows: int, tile_cols: int, chunks_per_tile: int,
-           max_code_len: int, pair_fit: int = 0) -> np.ndarray:
+           max_code_len: int, pair_fit: int = 0, family: int = 0) -> np.ndarray:
     """Encode a 2-D uint16 BF16 matrix into a blob (uint8 array); pair_fit > 0
     caps the codes of exponents with at least 1/pair_fit of the weights at 6
-    bits (see code_lengths)."""
+    bits (see code_lengths); family 1 takes the ranked unary code with an
+    escape instead (see code_lengths_unary)."""
     w = _u16(w)
     if w.ndim != 2:
         raise ValueError("expected a 2-D matrix")
@@ -191,9 +207,9 @@ def encode(w, tile_rows: int, tile_cols: int, chunks_per_tile: int,
     cap = encode_bound(rows, cols, tile_rows, tile_cols, chunks_per_tile, max_code_len)
     blob = np.zeros(cap, np.uint8)
     used = ctypes.c_uint64(0)
-    rc = lib().orc_encode(_p(w, ctypes.c_uint16), rows, cols, cols, tile_rows, tile_cols,
-                          chunks_per_tile, max_code_len, int(pair_fit), _p(blob, ctypes.c_uint8), cap,
-                          ctypes.byref(used))
+    rc = lib().orc_encode_family(_p(w, ctypes.c_uint16), rows, cols, cols, tile_rows, tile_cols,
+                                 chunks_per_tile, max_code_len, int(pair_fit), int(family),
+                                 _p(blob, ctypes.c_uint8), cap, ctypes.byref(used))
     if rc:
         raise ValueError("encode failed (%d)" % rc)
     return blob[: used.value].copy()

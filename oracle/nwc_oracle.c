@@ -248,6 +248,59 @@ int orc_code_lengths_pair_fit(const uint64_t *h, int lmax, uint32_t pair_fit, ui
   return orc_code_lengths(h, lmax, len_out);
 }
 
+/* Lengths of the ranked unary code with an escape ("NWC -- Neural Weight
+ * Compression", How it works, bullet "Prefix code instead of rANS"): the
+ * present symbols are ranked by count (most frequent first, ties by
+ * increasing symbol); rank r < R is written as r one bits and a zero (r + 1
+ * bits); every other symbol is an escape: R one bits, then the symbol's index
+ * among the escaped symbols in b = ceil(log2(number escaped)) bits, R + b
+ * bits in all.  Our reading of the escape: an index rather than the raw
+ * exponent byte, so that every code fits lmax bits (the decode table of the
+ * format reads lmax <= 12 bits at a time) -- with the canonical code built
+ * from these lengths, the escaped symbols of equal length take consecutive
+ * code values in symbol order, i.e. exactly "prefix, then index".  R is the
+ * value in 0 .. n - 1 with R + b <= lmax that minimises the total bits (the
+ * smallest such R on a tie).  One present symbol gets length 1. */
+int orc_code_lengths_unary(const uint64_t *h, int lmax, uint8_t *len_out) {
+  int sym[256], n = 0;
+  for (int v = 0; v < 256; v++) {
+    len_out[v] = 0;
+    if (h[v] > 0) sym[n++] = v;
+  }
+  if (n == 0 || lmax < 1) return ORC_EINVAL;
+  if (n == 1) {
+    len_out[sym[0]] = 1;
+    return ORC_OK;
+  }
+  /* rank order: count descending, then symbol ascending (insertion sort) */
+  for (int i = 1; i < n; i++) {
+    int t = sym[i], j = i - 1;
+    while (j >= 0 && (h[sym[j]] < h[t] || (h[sym[j]] == h[t] && sym[j] > t))) {
+      sym[j + 1] = sym[j];
+      j--;
+    }
+    sym[j + 1] = t;
+  }
+  int best_r = -1;
+  double best_bits = 0.0;
+  for (int R = 0; R < n; R++) {
+    int rest = n - R, b = 0;
+    while ((1 << b) < rest) b++;
+    if (R + b > lmax || R + b == 0) continue;
+    double bits = 0.0;
+    for (int r = 0; r < n; r++) bits += (double)h[sym[r]] * (double)(r < R ? r + 1 : R + b);
+    if (best_r < 0 || bits < best_bits) {
+      best_r = R;
+      best_bits = bits;
+    }
+  }
+  if (best_r < 0) return ORC_EINVAL;
+  int rest = n - best_r, b = 0;
+  while ((1 << b) < rest) b++;
+  for (int r = 0; r < n; r++) len_out[sym[r]] = (uint8_t)(r < best_r ? r + 1 : best_r + b);
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ */
 /* Canonical codes  [RFC] 3.2.2                                        */
 /* ------------------------------------------------------------------ */
@@ -480,9 +533,23 @@ int orc_encode_bound(uint64_t rows, uint64_t cols, uint32_t tr, uint32_t tc, uin
  * tile order and each chunk in order write the codes of the chunk's exponents
  * in row-major order; record each chunk's bit length, start every tile on a
  * 32-bit word boundary, and store the raw bytes row-major. */
+int orc_encode_family(const uint16_t *w, uint64_t rows, uint64_t cols, uint64_t ld, uint32_t tr,
+                      uint32_t tc, uint32_t s, uint32_t lmax, uint32_t pair_fit, uint32_t family,
+                      uint8_t *blob, uint64_t cap, uint64_t *used);
+
+/* Encode with the length-limited Huffman code (family 0). */
 int orc_encode(const uint16_t *w, uint64_t rows, uint64_t cols, uint64_t ld, uint32_t tr,
                uint32_t tc, uint32_t s, uint32_t lmax, uint32_t pair_fit, uint8_t *blob,
                uint64_t cap, uint64_t *used) {
+  return orc_encode_family(w, rows, cols, ld, tr, tc, s, lmax, pair_fit, 0, blob, cap, used);
+}
+
+/* Encode with the code family `family`: 0 = length-limited Huffman (with the
+ * pair_fit caps), 1 = ranked unary code with an escape (pair_fit unused). */
+int orc_encode_family(const uint16_t *w, uint64_t rows, uint64_t cols, uint64_t ld, uint32_t tr,
+                      uint32_t tc, uint32_t s, uint32_t lmax, uint32_t pair_fit, uint32_t family,
+                      uint8_t *blob, uint64_t cap, uint64_t *used) {
+  if (family > 1) return ORC_EINVAL;
   int rc = geom_check(rows, cols, tr, tc, s, lmax);
   if (rc) return rc;
   if (ld < cols || !w || !blob || !used) return ORC_EINVAL;
@@ -497,7 +564,7 @@ int orc_encode(const uint16_t *w, uint64_t rows, uint64_t cols, uint64_t ld, uin
   orc_histogram(e, n, h);
   uint8_t len[256];
   uint16_t code[256];
-  rc = orc_code_lengths_pair_fit(h, (int)lmax, pair_fit, len);
+  rc = family == 1 ? orc_code_lengths_unary(h, (int)lmax, len) : orc_code_lengths_pair_fit(h, (int)lmax, pair_fit, len);
   if (!rc) rc = orc_canonical_codes(len, code);
   if (rc) { free(e); free(r); return rc; }
 

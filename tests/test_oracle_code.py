@@ -275,3 +275,86 @@ def test_pair_fit_zero_is_the_plain_limit_and_caps_can_be_infeasible():
     h[:65] = 1000
     assert np.array_equal(oracle.code_lengths(h, 8, 65), oracle.code_lengths(h, 8))
     assert int(oracle.code_lengths(h, 8, 65).max()) == 7
+
+
+# -------------------------------------------- ranked unary code with escape --
+# ("NWC -- Neural Weight Compression", How it works, bullet "Prefix code
+# instead of rANS": exponents ranked by frequency, a unary rank code, an
+# escape for rare values; the escape carries an index into the escaped
+# symbols so every code fits the length limit)
+
+def test_unary_worked_example_by_hand():
+    # counts 1000, 500, 250 and ten symbols of 10 (1850 in all), lmax 8.
+    # Cost of R unary ranks (rank r: r + 1 bits) plus an escape of R bits and
+    # a ceil(log2(13 - R))-bit index for the rest, worked out by hand:
+    #   R = 0: 13 escaped, 4-bit index          1850 * 4               = 7400
+    #   R = 1: 12 escaped, 5 bits               1000 + 850 * 5         = 5250
+    #   R = 2: 11 escaped, 6 bits               1000 + 1000 + 350 * 6  = 4100
+    #   R = 3: 10 escaped, 7 bits               1000 + 1000 + 750 + 700 = 3450
+    #   R = 4:  9 escaped, 8 bits               2750 + 40 + 90 * 8     = 3510
+    #   R = 5:  8 escaped, 8 bits               2750 + 40 + 50 + 640   = 3480
+    #   R >= 6: escapes over 8 bits, not allowed
+    # so R = 3: lengths 1, 2, 3 and 7 for the ten rare symbols.
+    counts = {10: 1000, 20: 500, 30: 250}
+    counts.update({s: 10 for s in range(40, 50)})
+    h = _hist(counts)
+    ln = oracle.code_lengths_unary(h, 8)
+    assert (ln[10], ln[20], ln[30]) == (1, 2, 3)
+    assert all(ln[s] == 7 for s in range(40, 50))
+    assert int(sum(int(h[s]) * int(ln[s]) for s in counts)) == 3450
+    assert int(np.count_nonzero(ln)) == 13
+    # the canonical code is the unary code, then the escape prefix 111 and a
+    # 4-bit index in symbol order: 0, 10, 110, 1110000 .. 1111001
+    code = oracle.canonical_codes(ln)
+    assert (int(code[10]), int(code[20]), int(code[30])) == (0b0, 0b10, 0b110)
+    assert [int(code[s]) for s in range(40, 50)] == [0b1110000 + i for i in range(10)]
+
+
+def test_unary_is_optimal_for_dyadic_geometric_counts():
+    # counts halving rank by rank: the unary code is a Huffman code and its
+    # cost equals the entropy exactly (lengths 1 .. 7, 7)
+    counts = {3 * i + 1: 2 ** (6 - i) for i in range(7)}
+    counts[200] = 1
+    h = _hist(counts)
+    ln = oracle.code_lengths_unary(h, 12)
+    assert [int(ln[3 * i + 1]) for i in range(7)] == list(range(1, 8)) and int(ln[200]) == 7
+    n = sum(counts.values())
+    H = oracle.entropy_bits(h) * n
+    assert abs(_cost(h, ln) - H) < 1e-9
+    assert _cost(h, ln) == _cost(h, oracle.code_lengths(h, 12))
+
+
+@pytest.mark.parametrize("lmax", [8, 10, 12])
+def test_unary_never_beats_the_length_limited_optimum(lmax):
+    # the package-merge lengths are optimal among all prefix codes of at most
+    # lmax bits, and the unary code is one of them: never cheaper, always a
+    # prefix code, lengths by rank
+    rng = np.random.default_rng(77 + lmax)
+    for trial in range(40):
+        n = int(rng.integers(2, 40))
+        syms = rng.choice(256, n, replace=False)
+        cnt = np.maximum(1, (10 ** 6 * rng.random(n) ** 4).astype(np.int64))
+        h = np.zeros(256, np.uint64)
+        h[syms] = cnt
+        lu = oracle.code_lengths_unary(h, lmax)
+        lh = oracle.code_lengths(h, lmax)
+        assert _cost(h, lh) <= _cost(h, lu)
+        present = np.flatnonzero(h)
+        assert np.all(lu[present] >= 1) and np.all(lu[present] <= lmax)
+        assert sum(2.0 ** -int(lu[s]) for s in present) <= 1.0 + 1e-12
+        # more frequent symbols never get longer codes (ties by symbol)
+        order = sorted(present, key=lambda s: (-int(h[s]), int(s)))
+        assert all(int(lu[a]) <= int(lu[b]) for a, b in zip(order, order[1:]))
+
+
+def test_unary_one_symbol_and_round_trip():
+    h = np.zeros(256, np.uint64)
+    h[127] = 5
+    ln = oracle.code_lengths_unary(h, 8)
+    assert int(ln[127]) == 1 and int(np.count_nonzero(ln)) == 1
+    for w in (workloads.weights(1, "w", rows=slice(0, 200)), workloads.all_patterns(),
+              workloads.gaussian_bits((37, 1001), 0.05, 3)):
+        for lmax in (8, 12):
+            blob = oracle.encode(w, 8, 512, 64, lmax, 0, family=1)
+            assert oracle.validate(blob) == 0
+            assert np.array_equal(oracle.decode(blob), w)
