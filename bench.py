@@ -101,6 +101,9 @@ def parse():
     ap.add_argument("--max-code-len", type=int, default=0, help="encoder code length limit (0 = library default)")
     ap.add_argument("--pair-fit", type=int, default=0, metavar="K",
                     help="encoder: exponents held by at least 1/K of the weights get codes of at most 6 bits")
+    ap.add_argument("--code-family", choices=("huffman", "unary"), default="huffman",
+                    help="encoder code family: length-limited Huffman (default) or the ranked unary code with an "
+                         "escape (with --max-code-len 0 it takes a 12-bit limit)")
     ap.add_argument("--geometry", choices=("default", "tuned"), default="default",
                     help="tuned: time every candidate tile geometry per launch group on this GPU first "
                          "(decode_gemv_byte_amd.tune) and encode each group with the fastest")
@@ -358,6 +361,9 @@ def main():
         sys.exit("batch must be 1..8192 (above 16: decode + hipBLASLt GEMM)")
     params = {k: v for k, v in (("tile_rows", args.tile_rows), ("max_code_len", args.max_code_len),
                                 ("pair_fit", args.pair_fit)) if v}
+    if args.code_family == "unary":
+        params["code_family"] = 1
+        params.setdefault("max_code_len", 12)
     groups_named = [list(g) for g in wl.groups] if wl.groups else [[m.name] for m in wl.matrices]
     tuned, enc_params = None, {m.name: params or None for m in wl.matrices}
     if args.geometry == "tuned":
@@ -700,7 +706,8 @@ def main():
     note("comparators and standalone decode done")
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, keys, info, batch, args.cpu_seconds, args.pair_fit or DEFAULT_PAIR_FIT)
+        cpu = cpu_baseline(wl, keys, info, batch, args.cpu_seconds, args.pair_fit or DEFAULT_PAIR_FIT,
+                           1 if args.code_family == "unary" else 0)
 
     out = {
         "metric": "fused decode-GEMV GB/s (compressed + uncompressed-equiv), % HBM peak, batch 1",
@@ -829,7 +836,7 @@ def bf16_comparators(torch, nwc, args, keys, info, wbf, xs, ys, batch, bytes_u, 
     return res
 
 
-def cpu_baseline(wl, keys, info, batch, seconds, pair_fit):
+def cpu_baseline(wl, keys, info, batch, seconds, pair_fit, family=0):
     """The oracle (plain C: bit-serial decode and FP64 GEMV/GEMM) on a bounded
     sample of the workload: 256-row blocks of its matrices taken round robin
     (each matrix's first rows first), each encoded by the oracle with the
@@ -851,7 +858,7 @@ def cpu_baseline(wl, keys, info, batch, seconds, pair_fit):
         li = info[(layer, name)]
         r0 = (i // len(keys)) * nb % li.rows
         sub = workloads.weights(wl.cid, name, layer=layer, rows=slice(r0, min(r0 + nb, li.rows)))
-        blob = oracle.encode(sub, li.tile_rows, li.tile_cols, li.chunks_per_tile, li.max_code_len, pair_fit)
+        blob = oracle.encode(sub, li.tile_rows, li.tile_cols, li.chunks_per_tile, li.max_code_len, pair_fit, family)
         x = workloads.activations(wl.cid, name, batch=batch, layer=layer)
         return blob, x, blob.size + 2 * batch * (sub.shape[1] + sub.shape[0])
 

@@ -51,7 +51,7 @@ NWC_OUT_F32 = 1
 class nwc_params(ctypes.Structure):
     _fields_ = [("tile_rows", ctypes.c_uint32), ("tile_cols", ctypes.c_uint32),
                 ("chunks_per_tile", ctypes.c_uint32), ("max_code_len", ctypes.c_uint32),
-                ("pair_fit", ctypes.c_uint32)]
+                ("pair_fit", ctypes.c_uint32), ("code_family", ctypes.c_uint32)]
 
 
 class nwc_info(ctypes.Structure):
@@ -129,7 +129,7 @@ def _params(p) -> Optional[nwc_params]:
     if isinstance(p, nwc_params):
         return p
     return nwc_params(*[int(p.get(k, 0)) for k in ("tile_rows", "tile_cols", "chunks_per_tile",
-                                                    "max_code_len", "pair_fit")])
+                                                    "max_code_len", "pair_fit", "code_family")])
 
 
 def _ptr_params(p):

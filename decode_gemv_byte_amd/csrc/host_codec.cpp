@@ -83,6 +83,49 @@ void parallel_blocks(uint64_t n, uint64_t min_per_worker, F fn) {
 // packages downwards selects, at every list, a prefix; the leaves inside the
 // prefix of each list are the first `a_j` sorted leaves, and each such
 // selection adds one bit to those symbols' lengths.
+// Ranked unary code with an escape ("NWC -- Neural Weight Compression", How
+// it works, bullet "Prefix code instead of rANS"): exponents ranked by count
+// (ties: smaller value first); rank r < R takes r + 1 bits (r ones, a zero);
+// the others an escape of R ones and a ceil(log2(#escaped))-bit index, so
+// every code stays within lmax bits and the canonical code built from these
+// lengths is exactly "unary rank, or escape prefix + index in symbol order".
+// R minimises the total bits (smallest R on a tie).
+bool build_unary_lengths(const uint64_t hist[256], int lmax, uint8_t len[256]) {
+  std::memset(len, 0, 256);
+  std::vector<int> sym;
+  for (int v = 0; v < 256; v++)
+    if (hist[v]) sym.push_back(v);
+  const int n = static_cast<int>(sym.size());
+  if (n == 0 || lmax < 1) return false;
+  if (n == 1) {
+    len[sym[0]] = 1;
+    return true;
+  }
+  std::stable_sort(sym.begin(), sym.end(), [&](int a, int b) { return hist[a] > hist[b]; });
+  // bits(R) = sum over ranks < R of count * (rank + 1) + (count of the rest) * (R + index bits)
+  std::vector<uint64_t> suffix(n + 1, 0);
+  for (int r = n - 1; r >= 0; r--) suffix[r] = suffix[r + 1] + hist[sym[r]];
+  int best = -1;
+  unsigned __int128 best_bits = 0, head = 0;
+  for (int R = 0; R < n; R++) {
+    if (R > 0) head += static_cast<unsigned __int128>(hist[sym[R - 1]]) * static_cast<unsigned>(R);
+    int b = 0;
+    while ((1 << b) < n - R) b++;
+    if (R + b <= lmax && R + b > 0) {
+      const unsigned __int128 bits = head + static_cast<unsigned __int128>(suffix[R]) * static_cast<unsigned>(R + b);
+      if (best < 0 || bits < best_bits) {
+        best = R;
+        best_bits = bits;
+      }
+    }
+  }
+  if (best < 0) return false;
+  int b = 0;
+  while ((1 << b) < n - best) b++;
+  for (int r = 0; r < n; r++) len[sym[r]] = static_cast<uint8_t>(r < best ? r + 1 : best + b);
+  return true;
+}
+
 bool build_lengths(const uint64_t hist[256], int lmax, uint8_t len[256], uint32_t pair_fit) {
   std::memset(len, 0, 256);
   std::vector<int> sym;
@@ -209,6 +252,8 @@ bool params_resolve(const nwc_params* p, Geometry* g) {
   g->s = (p && p->chunks_per_tile) ? p->chunks_per_tile : 64;
   g->lmax = (p && p->max_code_len) ? p->max_code_len : 8;
   g->pair_fit = (p && p->pair_fit) ? p->pair_fit : 1024;
+  g->family = p ? p->code_family : 0;
+  if (g->family > 1) return false;
   if (g->tc % g->s) return false;
   if (g->lmax < 6 || g->lmax > 12) return false;
   g->v = g->tc / g->s;
@@ -276,7 +321,9 @@ nwc_status encode(const uint16_t* w, uint64_t rows, uint64_t cols, uint64_t ld, 
 
   uint8_t len[256];
   uint16_t code[256];
-  if (!build_lengths(hist, static_cast<int>(g.lmax), len, g.pair_fit) || !canonical(len, code))
+  const bool lengths_ok = g.family == 1 ? build_unary_lengths(hist, static_cast<int>(g.lmax), len)
+                                        : build_lengths(hist, static_cast<int>(g.lmax), len, g.pair_fit);
+  if (!lengths_ok || !canonical(len, code))
     return NWC_ERR_INVALID_ARG;
   // codes bit-reversed so that emitting low bits first sends the MSB first
   uint32_t rev[256];
@@ -411,7 +458,7 @@ nwc_status inspect(const void* blob_v, size_t bytes, nwc_info* info) {
     return NWC_ERR_BAD_FORMAT;
   const uint64_t rows = load_le<uint64_t>(b + 8), cols = load_le<uint64_t>(b + 16);
   if (rows < 1 || cols < 1 || rows > (1ull << 32) || cols > (1ull << 32)) return NWC_ERR_BAD_FORMAT;
-  nwc_params p;
+  nwc_params p{};  // fields the header does not hold (encoder-only choices) stay zero
   p.tile_rows = load_le<uint32_t>(b + 24);
   p.tile_cols = load_le<uint32_t>(b + 28);
   p.chunks_per_tile = load_le<uint32_t>(b + 32);

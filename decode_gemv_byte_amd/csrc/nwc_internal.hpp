@@ -13,6 +13,7 @@ namespace nwc {
 struct Geometry {
   uint32_t tr = 0, tc = 0, s = 0, lmax = 0, v = 0;  // tile rows/cols, chunks, max code length, chunk cols
   uint32_t pair_fit = 0;                             // encoder only: 6-bit cap for common exponents
+  uint32_t family = 0;                               // encoder only: 0 Huffman, 1 ranked unary + escape
   uint64_t rows = 0, cols = 0;
   uint64_t n_tr = 0, n_tc = 0, n_tiles = 0, n_chunks = 0;
   uint64_t raw_ld = 0, stream_words = 0;

@@ -94,6 +94,17 @@ typedef struct {
                                rest keep the limit L; 1 turns it off (unless
                                more than 64 values are that common, then the
                                plain limit applies) [1024] */
+  uint32_t code_family;     /* 0: the length-limited Huffman code above [0];
+                               1: the ranked unary code with an escape ("NWC
+                               -- Neural Weight Compression", How it works,
+                               bullet "Prefix code instead of rANS"):
+                               exponents ranked by count, rank r < R coded
+                               as r one bits and a zero, the rest as R one
+                               bits and an index among them, R chosen for the
+                               fewest bits within L (pair_fit unused).  Both
+                               are canonical prefix codes of at most L bits:
+                               the blob stores only the lengths and every
+                               decoder reads both alike. */
 } nwc_params;
 
 /* Everything a device call needs, read from a validated blob. */

@@ -5,7 +5,7 @@
 // free or undefined behaviour aborts the run.
 //
 // For `iters` random cases: draw a BF16 matrix (a random shape and one of
-// several value distributions) and encoding parameters; encode it with
+// several value distributions) and encoding parameters (either code family); encode it with
 // nwc_encode and with the oracle; the two must agree on success and write
 // the same bytes; the oracle must decode the blob to the input bits.  (The
 // C-ABI entry points nwc_encode / nwc_inspect forward to these functions.)  Then
@@ -25,8 +25,9 @@
 extern "C" {
 int orc_encode_bound(uint64_t rows, uint64_t cols, uint32_t tr, uint32_t tc, uint32_t s, uint32_t lmax,
                      uint64_t* bytes);
-int orc_encode(const uint16_t* w, uint64_t rows, uint64_t cols, uint64_t ld, uint32_t tr, uint32_t tc, uint32_t s,
-               uint32_t lmax, uint32_t pair_fit, uint8_t* blob, uint64_t cap, uint64_t* used);
+int orc_encode_family(const uint16_t* w, uint64_t rows, uint64_t cols, uint64_t ld, uint32_t tr, uint32_t tc,
+                      uint32_t s, uint32_t lmax, uint32_t pair_fit, uint32_t family, uint8_t* blob, uint64_t cap,
+                      uint64_t* used);
 int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* w, uint64_t ld);
 int orc_validate(const uint8_t* blob, uint64_t bytes);
 }
@@ -81,7 +82,7 @@ int main(int argc, char** argv) {
     const uint32_t lms[] = {6, 7, 8, 9, 11, 12};
     const uint32_t pfs[] = {0, 1, 1024};
     const auto& tc = tcs[r.below(6)];
-    nwc_params p{trs[r.below(7)], tc[0], tc[1], lms[r.below(6)], pfs[r.below(3)]};
+    nwc_params p{trs[r.below(7)], tc[0], tc[1], lms[r.below(6)], pfs[r.below(3)], r.below(2)};
     size_t bound = 0;
     const nwc_status bs = nwc::encode_bound(rows, cols, &p, &bound);
     uint64_t obound = 0;
@@ -92,8 +93,9 @@ int main(int argc, char** argv) {
     size_t used = 0;
     uint64_t oused = 0;
     const nwc_status es = nwc::encode(w.data(), rows, cols, cols, &p, a.data(), a.size(), &used);
-    const int oes = orc_encode(w.data(), rows, cols, cols, p.tile_rows, p.tile_cols, p.chunks_per_tile,
-                               p.max_code_len, p.pair_fit ? p.pair_fit : 1024, b.data(), b.size(), &oused);
+    const int oes = orc_encode_family(w.data(), rows, cols, cols, p.tile_rows, p.tile_cols, p.chunks_per_tile,
+                                      p.max_code_len, p.pair_fit ? p.pair_fit : 1024, p.code_family, b.data(),
+                                      b.size(), &oused);
     if ((es == NWC_OK) != (oes == 0)) return fail("encode success disagrees", it);
     if (es != NWC_OK) continue;  // e.g. more distinct exponents than a short limit codes
     if (used != oused || std::memcmp(a.data(), b.data(), used) != 0) return fail("blobs differ", it);

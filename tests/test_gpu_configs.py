@@ -390,3 +390,39 @@ def test_one_hot_columns_other_geometries(params):
         Yh = Y.cpu().numpy()
         for beta, k in enumerate(ks):
             _exact_column(Yh[beta], w[:, k], "%s skinny column %d" % (params, k))
+
+
+# ------------------------------- the ranked unary code family (escape index) --
+
+@pytest.mark.parametrize("lmax", [9, 12])
+def test_unary_family_parity(lmax):
+    # blobs of the second code family decode and multiply through the same
+    # kernels: decode bit-exact, every GEMV row within the bound, one-hot
+    # columns exact (batch 1 and the skinny GEMM)
+    w = _w(3, "gate")
+    host = nwc.nwc_encode(w, dict(code_family=1, max_code_len=lmax))
+    info = nwc.nwc_inspect(host)
+    b = dev(host)
+    _say("unary family L=%d: decode, GEMV, one-hot" % lmax)
+    out = torch.empty((info.rows, info.cols), dtype=torch.int16, device="cuda")
+    nwc.nwc_decode(info, b, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dev(w.view(np.int16)))
+    ws = torch.zeros(nwc.nwc_workspace_size(info, 1), dtype=torch.uint8, device="cuda")
+    y = torch.empty(info.rows, dtype=torch.float32, device="cuda")
+    nwc.nwc_gemv(info, b, dev(workloads.activations(3, "gate")[0]), y, ws)
+    torch.cuda.synchronize()
+    Y, A = _llama_ref(0, "gate")
+    _check_y(_to_f64(y), Y, A, True, "unary L=%d" % lmax)
+    for k in _probe_columns(w, info)[:12]:
+        nwc.nwc_gemv(info, b, dev(_one_hot(info.cols, k)), y, ws)
+        torch.cuda.synchronize()
+        _exact_column(y.cpu().numpy(), w[:, k], "unary L=%d column %d" % (lmax, k))
+    X = np.stack([_one_hot(info.cols, k) for k in range(0, 16 * 211, 211)])
+    Ys = torch.empty((16, info.rows), dtype=torch.float32, device="cuda")
+    nwc.nwc_gemm_skinny(info, b, dev(X), Ys, torch.zeros(max(1, nwc.nwc_workspace_size(info, 16)),
+                                                         dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    Yh = Ys.cpu().numpy()
+    for beta, k in enumerate(range(0, 16 * 211, 211)):
+        _exact_column(Yh[beta], w[:, k], "unary L=%d skinny column %d" % (lmax, k))

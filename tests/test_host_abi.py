@@ -384,3 +384,27 @@ def test_pair_fit_infeasible_caps_fall_back_like_the_oracle():
     # pair_fit 1 caps nothing: the plain limit
     w2 = workloads.weights(1, "w")
     assert np.array_equal(nwc.nwc_encode(w2, dict(pair_fit=1)), oracle.encode(w2, 8, 512, 64, 8, 0))
+
+
+@pytest.mark.parametrize("lmax", [8, 12])
+@pytest.mark.parametrize("cid,name", [(1, "w"), (2, "gate"), (3, "gate"), (5, "lm_head"), (0, "all_patterns"),
+                                      (0, "one_symbol")])
+def test_encoder_bytes_equal_oracle_unary_family(cid, name, lmax):
+    # the ranked unary code with an escape (code_family 1): the library's
+    # lengths, canonical codes and blob bytes are the oracle's
+    if cid == 0:
+        w = workloads.all_patterns() if name == "all_patterns" else np.full((40, 72), 0x3C55, np.uint16)
+    else:
+        w = workloads.weights(cid, name, rows=slice(0, 2048))
+    blob = nwc.nwc_encode(w, dict(max_code_len=lmax, code_family=1))
+    assert np.array_equal(blob, oracle.encode(w, 8, 512, 64, lmax, 0, family=1))
+    info = nwc.nwc_inspect(blob)
+    e, _ = oracle.split(w)
+    assert np.array_equal(np.asarray(info.code_len), oracle.code_lengths_unary(oracle.histogram(e), lmax))
+    assert np.array_equal(oracle.decode(blob), w)
+
+
+def test_unknown_code_family_is_rejected():
+    w = workloads.gaussian_bits((16, 512), 0.02, 1)
+    with pytest.raises(nwc.NwcError):
+        nwc.nwc_encode(w, dict(code_family=2))
