@@ -305,29 +305,32 @@ def traffic_from_profile(path):
 
 def read_probe(torch, nwc, stream, reps=20):
     """HBM read rate of a plain streaming kernel (nwc_read_probe) over a 4 GiB
-    buffer, 16x the Infinity Cache: the fastest of three launch sizes, each
-    averaged over `reps` back-to-back launches timed with HIP events on the
-    probe's stream."""
+    buffer, 16x the Infinity Cache: the fastest of two layouts (grid-stride;
+    one contiguous range per workgroup) at four launch sizes, each averaged
+    over `reps` back-to-back launches timed with HIP events on the probe's
+    stream."""
     buf = torch.ones(PROBE_BYTES, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     best = None
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for per_cu in (4, 8, 16):
-        groups = cus * per_cu
-        with torch.cuda.stream(stream):
-            for i in range(3):
-                nwc.nwc_read_probe(buf, sink, groups, stream=stream)
-            e0.record(stream)
-            for i in range(reps):
-                nwc.nwc_read_probe(buf, sink, groups, stream=stream)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        gbps = PROBE_BYTES / (us * 1e-6) / 1e9
-        if best is None or gbps > best["GBps"]:
-            best = {"GBps": round(gbps, 1), "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
-                    "bytes": PROBE_BYTES, "workgroups": groups, "avg_launch_us": round(us, 2)}
+    for layout in (0, 1):
+        for per_cu in (2, 4, 8, 16):
+            groups = cus * per_cu
+            with torch.cuda.stream(stream):
+                for i in range(3):
+                    nwc.nwc_read_probe(buf, sink, groups, layout, stream=stream)
+                e0.record(stream)
+                for i in range(reps):
+                    nwc.nwc_read_probe(buf, sink, groups, layout, stream=stream)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            gbps = PROBE_BYTES / (us * 1e-6) / 1e9
+            if best is None or gbps > best["GBps"]:
+                best = {"GBps": round(gbps, 1), "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+                        "bytes": PROBE_BYTES, "layout": ("grid-stride", "contiguous per workgroup")[layout],
+                        "workgroups": groups, "avg_launch_us": round(us, 2)}
     del buf
     return best
 

@@ -101,7 +101,7 @@ _lib.nwc_blas_create.argtypes = [ctypes.POINTER(_vp)]
 _lib.nwc_blas_destroy.argtypes = [_vp]
 _lib.nwc_prefill_workspace_size.argtypes = [ctypes.POINTER(nwc_info), ctypes.POINTER(_sz)]
 _lib.nwc_gemm_prefill.argtypes = [_vp, ctypes.POINTER(nwc_info), _vp, _vp, _u64, _i, _vp, _u64, _i, _vp, _sz, _vp]
-_lib.nwc_read_probe.argtypes = [_vp, _sz, _vp, _u32, _vp]
+_lib.nwc_read_probe.argtypes = [_vp, _sz, _vp, _u32, _i, _vp]
 _lib.nwc_noalloc_scratch_bytes.argtypes = [ctypes.POINTER(_sz)]
 _lib.nwc_gemv_noalloc.argtypes = [ctypes.POINTER(nwc_info), _vp, _vp, _vp, _i, _vp]
 for _f in ("nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode", "nwc_workspace_size", "nwc_gemv",
@@ -373,11 +373,11 @@ def nwc_gemv_bf16(w_dev, x_dev, y_dev, ws, stream=None):
                               _ytype(y_dev), wp, wn, _stream(stream)), "nwc_gemv_bf16")
 
 
-def nwc_read_probe(buf_dev, sink_dev, groups: int = 0, stream=None):
+def nwc_read_probe(buf_dev, sink_dev, groups: int = 0, layout: int = 1, stream=None):
     """Stream-read every byte of the device tensor buf_dev (HBM read probe); sink_dev a device tensor
-    of at least 4 bytes."""
+    of at least 4 bytes; layout 0 grid-stride, 1 one contiguous range per workgroup."""
     _check(_lib.nwc_read_probe(_dptr(buf_dev), int(buf_dev.numel() * buf_dev.element_size()), _dptr(sink_dev),
-                               int(groups), _stream(stream)), "nwc_read_probe")
+                               int(groups), int(layout), _stream(stream)), "nwc_read_probe")
 
 
 def info_dict(info: nwc_info) -> dict:

@@ -1387,24 +1387,38 @@ __global__ void k_reduce(const float* __restrict__ partial, uint64_t rows, uint3
 // ---------------------------------------------------------- HBM read probe
 
 // A plain streaming read of `n16` 16-byte words: each lane keeps 8 loads in
-// flight (grid-stride, so every wavefront reads 1 KB contiguous per load
-// instruction), folds them into one value and stores it only if it equals a
-// value no realistic input produces, so the loads cannot be dropped.  Its
-// rate is the read bandwidth a kernel can reach on this GPU, the ceiling the
-// decode kernels are compared with beside the 8 TB/s peak.
+// flight and every wavefront reads 1 KB contiguous per load instruction.
+// Layout 0 is grid-stride (the 8 loads of a lane are a grid apart); layout 1
+// gives each workgroup one contiguous range, walked 32 KB at a time (the 8
+// loads of a workgroup cover consecutive 4 KB), which keeps each workgroup on
+// few DRAM pages.  The loads are folded into one value that is stored only if
+// it equals a value no realistic input produces, so they cannot be dropped.
+// The faster layout's rate is the read bandwidth a kernel can reach on this
+// GPU, the ceiling the decode kernels are compared with beside the 8 TB/s peak.
+template <int LAYOUT>
 __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, uint64_t n16,
                                                     uint32_t* __restrict__ sink) {
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
-  uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint64_t i, end, stride;
+  if constexpr (LAYOUT == 0) {
+    stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    end = n16;
+  } else {
+    const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const uint64_t b0 = static_cast<uint64_t>(blockIdx.x) * per;
+    stride = blockDim.x;
+    i = b0 + threadIdx.x;
+    end = b0 + per < n16 ? b0 + per : n16;
+  }
   uint32_t acc = 0;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
+  for (; i + 7 * stride < end; i += 8 * stride) {
     uint4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; u++) v[u] = p[i + u * stride];
 #pragma unroll
     for (int u = 0; u < 8; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < end; i += stride) {
     const uint4 v = p[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
@@ -2106,16 +2120,20 @@ nwc_status nwc_gemv_bf16(const uint16_t* w_dev, uint64_t rows, uint64_t cols, ui
                                               static_cast<hipStream_t>(stream));
 }
 
-nwc_status nwc_read_probe(const void* buf_dev, size_t bytes, uint32_t* sink_dev, uint32_t groups, void* stream) {
-  if (!buf_dev || !sink_dev || bytes < 16) return NWC_ERR_INVALID_ARG;
+nwc_status nwc_read_probe(const void* buf_dev, size_t bytes, uint32_t* sink_dev, uint32_t groups,
+                          int layout, void* stream) {
+  if (!buf_dev || !sink_dev || bytes < 16 || (layout != 0 && layout != 1)) return NWC_ERR_INVALID_ARG;
   if (!aligned(buf_dev, 16) || !aligned(sink_dev, 4)) return NWC_ERR_ALIGNMENT;
   if (groups == 0) {
     const int cus = cu_count();
     if (cus < 1) return NWC_ERR_HIP;
     groups = static_cast<uint32_t>(cus) * 8;
   }
-  return launch(k_read_probe, dim3(groups), dim3(256), 0, static_cast<hipStream_t>(stream),
-                static_cast<const uint4*>(buf_dev), static_cast<uint64_t>(bytes / 16), sink_dev);
+  const auto* p = static_cast<const uint4*>(buf_dev);
+  const uint64_t n16 = static_cast<uint64_t>(bytes / 16);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return layout == 0 ? launch(k_read_probe<0>, dim3(groups), dim3(256), 0, st, p, n16, sink_dev)
+                     : launch(k_read_probe<1>, dim3(groups), dim3(256), 0, st, p, n16, sink_dev);
 }
 
 }  // extern "C"

@@ -328,13 +328,15 @@ nwc_status nwc_gemv_bf16(const uint16_t *w_dev, uint64_t rows, uint64_t cols, ui
  * token reads the weights from HBM, so the achievable read rate bounds
  * decoding): a plain streaming read of `bytes` (rounded down to 16) from
  * buf_dev (device, 16-byte aligned), 8 loads of 16 bytes in flight per lane,
- * in `groups` workgroups of 256 lanes (0 = 8 per compute unit).  sink_dev
- * (device, 4 bytes, 4-byte aligned) is written only for a value no realistic
- * input produces, so the loads cannot be optimised away.  The caller times
- * it (bytes / duration) to know what a kernel can reach on this GPU.  Async.
- * Errors: INVALID_ARG, ALIGNMENT, HIP. */
+ * in `groups` workgroups of 256 lanes (0 = 8 per compute unit).  layout 0:
+ * grid-stride over the whole buffer; layout 1: one contiguous range per
+ * workgroup.  sink_dev (device, 4 bytes, 4-byte aligned) is written only for
+ * a value no realistic input produces, so the loads cannot be optimised away.
+ * The caller times it (bytes / duration) to know what a kernel can reach on
+ * this GPU.  Async.
+ * Errors: INVALID_ARG (also for a layout other than 0 or 1), ALIGNMENT, HIP. */
 nwc_status nwc_read_probe(const void *buf_dev, size_t bytes, uint32_t *sink_dev, uint32_t groups,
-                          void *stream);
+                          int layout, void *stream);
 
 #ifdef __cplusplus
 }

@@ -531,6 +531,28 @@ def test_gemv_bf16_comparator(cid, name):
     assert int(ws.count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("n16,groups,at", [(1000, 3, 999), (1000, 3, 0), (4099, 7, 2050), (64, 8, 63),
+                                           (1 << 20, 0, (1 << 20) - 1)])
+def test_read_probe_reads_every_word(layout, n16, groups, at):
+    # one 16-byte word whose four dwords XOR to the probe's marker, zeros
+    # elsewhere: the lane that loads it (and only that lane) stores the
+    # marker, so the sink shows the word was read, at the edges of the
+    # workgroups' ranges and the ragged tail too
+    _say("read probe layout %d n16 %d groups %d at %d" % (layout, n16, groups, at))
+    buf = torch.zeros(n16 * 4, dtype=torch.int32, device="cuda")
+    buf[at * 4] = int(np.int32(np.uint32(0x9E3779B9).view(np.int32)))
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nwc.nwc_read_probe(buf, sink, groups, layout)
+    torch.cuda.synchronize()
+    assert int(sink.view(torch.int32).item()) == int(np.uint32(0x9E3779B9).view(np.int32))
+    sink.zero_()
+    buf.zero_()
+    nwc.nwc_read_probe(buf, sink, groups, layout)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+
+
 def test_native_library_is_in_tree():
     assert os.path.dirname(os.path.abspath(nwc.LIB_PATH)).startswith(ROOT)
     maps = open("/proc/self/maps").read()

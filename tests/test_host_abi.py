@@ -257,10 +257,12 @@ def test_device_calls_validate_before_launch():
     assert L.nwc_gemv_bf16(A, 64, 512, 512, A, A, 0, A + 16, BW, None) == nwc.NWC_ERR_ALIGNMENT
     assert L.nwc_gemv_bf16(A, 64, 512, 512, A, A, 0, A, BW - 8, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
     # the read probe
-    assert L.nwc_read_probe(None, 1 << 20, A, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_read_probe(A, 8, A, 0, None) == nwc.NWC_ERR_INVALID_ARG
-    assert L.nwc_read_probe(A + 8, 1 << 20, A, 0, None) == nwc.NWC_ERR_ALIGNMENT
-    assert L.nwc_read_probe(A, 1 << 20, A + 2, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_read_probe(None, 1 << 20, A, 0, 1, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_read_probe(A, 8, A, 0, 1, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_read_probe(A, 1 << 20, A, 0, 2, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_read_probe(A, 1 << 20, A, 0, -1, None) == nwc.NWC_ERR_INVALID_ARG
+    assert L.nwc_read_probe(A + 8, 1 << 20, A, 0, 0, None) == nwc.NWC_ERR_ALIGNMENT
+    assert L.nwc_read_probe(A, 1 << 20, A + 2, 0, 1, None) == nwc.NWC_ERR_ALIGNMENT
     # grouped launch: count, NULL arrays, per-entry checks, geometry mix
     infos = (nwc.nwc_info * 2)(info, info)
     V2 = ctypes.c_void_p * 2
