@@ -255,6 +255,12 @@ struct LaneBits {
     return __builtin_amdgcn_alignbit(lds_word(a + 256), lds_word(a), q);
   }
   __device__ __forceinline__ void advance(uint32_t n) { q += n; }
+  // the window n bits further on, without moving
+  __device__ __forceinline__ uint32_t window_after(uint32_t n) const {
+    const uint32_t p = q + n;
+    const uint32_t a = ((p << 3) & ~0xFFu) | lane4;
+    return __builtin_amdgcn_alignbit(lds_word(a + 256), lds_word(a), p);
+  }
 };
 
 // Decode the next two exponents with either reader: returns a dword with
@@ -292,22 +298,37 @@ __device__ __forceinline__ uint32_t Bits::pair(const uint32_t* tab) { return dec
 // uses only the low 5 bits of its amount, which hold that length).  The
 // window holds 30 stream bits, so this needs every pair to fit 18 bits:
 // codes of at most 9 bits.  When some lane's first or second entry holds a
-// single code (its pair did not fit the 12-bit window), the wavefront redoes
-// both pairs one lookup chain at a time; with codes of at most 6 bits (FIT2)
+// single code (its pair did not fit the 12-bit window), the wavefront
+// completes both pairs with second lookups, the second pair from a window
+// read past the first (rare: the branch is laid out off the common path,
+// which then has no register copies); with codes of at most 6 bits (FIT2)
 // every pair fits and that test is dropped.
+// A pair entry whose window held only one code (sign bit set) completed by
+// a lookup at the window shifted past that code; other entries unchanged.
+__device__ __forceinline__ uint32_t complete_pair(uint32_t ent, uint32_t win, const uint32_t* tab) {
+  const uint32_t l0 = ent & 0xFu;
+  const uint32_t ent2 = tab[((win >> l0) & 0x3FFCu) >> 2];
+  const uint32_t merged = (ent & 0x7F80u) | ((ent2 & 0x7F80u) << 16) | (l0 + ((ent2 >> 16) & 0xFu));
+  return static_cast<int32_t>(ent) < 0 ? merged : ent;
+}
+
 template <bool FIT2, class R>
 __device__ __forceinline__ void decode_quad(R& rd, const uint32_t* tab, uint32_t& e1, uint32_t& e2) {
   const uint32_t win = rd.window();
   e1 = tab[(win & 0x3FFCu) >> 2];
   e2 = tab[((win >> e1) & 0x3FFCu) >> 2];
+  uint32_t adv = (e1 & 0x1Fu) + (e2 & 0x1Fu);
   if constexpr (!FIT2) {
-    if (__builtin_amdgcn_ballot_w64(static_cast<int32_t>(e1 | e2) < 0)) {
-      e1 = decode_pair<false>(rd, tab);
-      e2 = decode_pair<false>(rd, tab);
-      return;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(e1 | e2) < 0) != 0, 0)) {
+      // some lane's entry holds one code: complete each pair with a second
+      // lookup, the second pair from a window read past the first
+      e1 = complete_pair(e1, win, tab);
+      const uint32_t w2 = rd.window_after(e1 & 0x1Fu);
+      e2 = complete_pair(tab[(w2 & 0x3FFCu) >> 2], w2, tab);
+      adv = (e1 & 0x1Fu) + (e2 & 0x1Fu);
     }
   }
-  rd.advance((e1 & 0x1Fu) + (e2 & 0x1Fu));
+  rd.advance(adv);
 }
 
 // Two BF16 weights from a pair entry and 4 raw bytes; `hi` selects raw bytes
@@ -769,9 +790,11 @@ __device__ __forceinline__ uint32_t interleave(const uint32_t* buf, uint32_t w0,
 template <int TR, int NX, int R0, int R1, bool FIT2 = false, bool QUAD = false>
 __device__ __forceinline__ void gemv_rows(const TileRegs<TR, NX>& in, LaneBits& br, const uint32_t* tab,
                                           float (&acc)[TR * NX]) {
+  // wave-uniform: the row test is a scalar compare
+  const uint32_t nrows = __builtin_amdgcn_readfirstlane(in.nrows);
 #pragma unroll
   for (int r = R0; r < R1; r++) {
-    if (static_cast<uint32_t>(r) < in.nrows) {
+    if (static_cast<uint32_t>(r) < nrows) {
       float a[NX];
 #pragma unroll
       for (int k = 0; k < NX; k++) a[k] = 0.0f;
