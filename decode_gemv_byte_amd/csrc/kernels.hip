@@ -37,11 +37,15 @@
 //      finished along a chain of 64-bit atomic exchanges in the workspace, so
 //      the summation order is fixed and no workgroup waits for another.
 //    - Skinny mode: whole row blocks per range; up to 4 X rows are
-//      multiplied as each pair is decoded, 5..9 rows from the decoded tile in
-//      registers, 10..16 rows on the matrix cores (v_mfma_f32_16x16x32_bf16,
-//      the decoded tile passed through LDS into operand layout).
+//      multiplied as each pair is decoded, more (16-row tiles) from the
+//      decoded tile in registers.
 //    - Decode mode: each decoded tile is stored once the next tile's loads
 //      are in flight.
+//  * k_skinny_mc: the skinny decode-GEMM for 8-row tiles and 5..16 X rows on
+//    the matrix cores (v_mfma_f32_16x16x32_bf16), with two kinds of
+//    wavefront per workgroup: decoding wavefronts (the batch-1 pipeline) hand
+//    decoded tiles through a ring of LDS slots to matrix-core wavefronts that
+//    keep one column tile's X in registers.
 //  * k_decode_generic, k_gemv_generic (+ k_reduce), k_gather: any geometry,
 //    two codes per table lookup, one tile per wavefront; the generic GEMV
 //    writes FP32 partial sums per column tile that k_reduce adds in order.
@@ -602,6 +606,9 @@ struct GemvGroup {
   // skinny mode (one matrix): X rows of ldx elements, Y rows of ldy entries
   uint64_t ldx, ldy;
   uint32_t batch;
+  // k_skinny_mc: decoding and matrix-core wavefronts per workgroup, log2 of
+  // the ring slots
+  uint32_t producers, consumers, ring_log2;
 };
 
 // Registers of one tile for the batch-1 kernel: raw bytes of this lane's
@@ -899,20 +906,16 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 // decoded into registers first and then multiplied by the X rows 32 / TR at
 // a time (NB 0, 2, 4: the skinny mode, one matrix, ranges of whole row
 // blocks); -1 for the standalone decode, which writes each decoded tile to
-// W' (job.y, rows of g.ldy elements) once the next tile's data is in; 16
-// for Y = X W^T with up to 16 X rows on the matrix cores (8-row tiles: the
-// decoded tile goes through LDS into MFMA operand layout).
+// W' (job.y, rows of g.ldy elements) once the next tile's data is in.
 template <int TR, int MAXW, int NB, bool FIT2 = false, bool QUAD = false>
 __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   constexpr bool RAW16 = NB == kRawBf16;
   static_assert(!QUAD || NB == 1, "two pairs per window: batch 1");
   constexpr bool DECODE = NB < 0;
-  constexpr bool MF = NB == 16;
   constexpr bool SKINNY = !RAW16 && (NB == 0 || NB > 1);
-  constexpr int NX = NB > 0 && !MF && !RAW16 ? NB : 0;  // X rows that come with each tile
-  constexpr int NA = NB > 0 && !MF && !RAW16 ? NB : 1;  // sums per row of a tile formed while decoding
+  constexpr int NX = NB > 0 && !RAW16 ? NB : 0;  // X rows that come with each tile
+  constexpr int NA = NB > 0 && !RAW16 ? NB : 1;  // sums per row of a tile formed while decoding
   using Regs = std::conditional_t<RAW16, TileRegs16<TR>, TileRegs<TR, NX>>;
-  static_assert(!MF || TR == 8, "the matrix-core mode takes 8-row tiles");
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const uint32_t nw = blockDim.x / kWave;
@@ -1037,86 +1040,6 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     }
   };
   while (t < r1) {
-    if constexpr (MF) {
-      // Matrix-core mode.  The whole tile is in (the next tile's loads go out
-      // at the end of this one, so that the X loads below never wait behind
-      // them: vector memory operations retire in order).
-      wait_vmem();
-      wave_sync_lds();
-      const uint32_t q0 = interleave(buf, in.w0, in.a0, in.cb(), J, slot);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      wave_sync_lds();
-      uint32_t wv[TR][4];
-#pragma unroll
-      for (int k = 0; k < TR; k++) wv[k][0] = wv[k][1] = wv[k][2] = wv[k][3] = 0u;
-      LaneBits br;
-      br.init(slot, q0);
-      if (in.active) decode_rows<TR, NX, 0, TR, FIT2>(in, br, tab, wv);
-      // Y block (16 weight rows x 16 X rows) += W block (16 x 32) x X^T block
-      // (32 x 16), 16 times over the tile's 512 columns.  MFMA operands: lane
-      // l holds row l % 16 of W (rows 8..15 zero) and row l % 16 of X (zero
-      // past the batch), columns 8 (l / 16) .. + 7 of the 32; the result holds
-      // W rows 4 (l / 16) .. + 3 for X row l % 16.  The tile goes through the
-      // slot, whose stream is no longer needed, 128 columns (16 lanes) at a
-      // time: T[r][c] at byte r * 272 + 2 c (rows padded against bank
-      // conflicts).
-      const uint32_t m = lane & 15u, gq = lane >> 4;
-      const uint32_t T = lds_addr(slot);
-      const uint32_t zero = lds_addr(buf);  // the staging buffer's 4 zero guard words
-      const uint32_t a_at = m < TR ? T + m * 272u + gq * 16u : zero;
-      const uint32_t a_step = m < TR ? 64u : 0u;
-      const uint64_t col0 = static_cast<uint64_t>(in.col) * 512;
-      const bool x_row = m < g.batch;
-      const uint16_t* xr = job.x + (x_row ? static_cast<uint64_t>(m) * g.ldx : 0) + col0;
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int h = 0; h < 4; h++) {
-        // this phase's X (issued here, not hoisted: four phases at once would
-        // not fit the registers)
-        asm volatile("" ::: "memory");
-        uint4 xb[4];
-#pragma unroll
-        for (int qq = 0; qq < 4; qq++) {
-          const uint32_t kc = static_cast<uint32_t>(128 * h + 32 * qq) + gq * 8u;
-          const bool ok = x_row && col0 + kc < b.cols;
-          xb[qq] = *reinterpret_cast<const uint4*>(xr + (ok ? kc : 0u));
-          if (!ok) xb[qq] = make_uint4(0, 0, 0, 0);
-        }
-        if (gq == static_cast<uint32_t>(h)) {
-#pragma unroll
-          for (int r = 0; r < TR; r++)
-            lds_put4(T + static_cast<uint32_t>(r) * 272u + m * 16u,
-                     make_uint4(wv[r][0], wv[r][1], wv[r][2], wv[r][3]));
-        }
-        wave_sync_lds();
-#pragma unroll
-        for (int qq = 0; qq < 4; qq++) {
-          const uint4 av = lds_get4(a_at + static_cast<uint32_t>(qq) * a_step);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                        __builtin_bit_cast(bf16x8_t, xb[qq]), acc, 0, 0, 0);
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // this phase's reads are done before T is written again
-        wave_sync_lds();
-      }
-      if (gq < TR / 4 && x_row) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) gsum[((t - r0) * TR + gq * 4 + e) * g.batch + m] = acc[e];
-      }
-      Regs nx;
-      const uint64_t tn = claims ? claim() : r1;
-      if (tn < r1) {
-        const uint64_t ni = tn / n_tc;
-        const uint32_t nj = static_cast<uint32_t>(tn - ni * n_tc);
-        uint32_t w0, w1;
-        words(tn, w0, w1);
-        nx.load(b, job.x, g.ldx, g.batch, ni, nj, w0, w1, buf);
-        asm volatile("" ::: "memory");
-        nx.load_rest(b, ni, nj);
-      }
-      in = nx;
-      t = tn;
-      continue;
-    }
     if constexpr (RAW16) {
       // Uncompressed comparator: the same pipeline (rows [0, PRE) before the
       // next tile's loads go out), products of plain BF16 rows with x.
@@ -1175,7 +1098,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     br.init(slot, q0);
     if constexpr (NB <= 0) {
       if (in.active) decode_rows<TR, NX, 0, PRE, FIT2>(in, br, tab, wv);
-    } else if constexpr (!MF) {
+    } else {
       if (in.active) gemv_rows<TR, NX, 0, PRE, FIT2, QUAD>(in, br, tab, acc);
     }
     // the rest of the raw bytes, then the next tile's loads: they go out
@@ -1229,7 +1152,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
         const uint32_t beta = gi2 * GB + v % GB;
         if ((lane & 1u) == 0 && beta < g.batch) gsum[((t - r0) * TR + vr) * g.batch + beta] = sv;
       }
-    } else if constexpr (!MF) {
+    } else {
       if (in.active) gemv_rows<TR, NX, PRE, TR, FIT2, QUAD>(in, br, tab, acc);
       // lanes (64 / (TR NB)) v .. hold sum v: row v / NB, X row v % NB
       const float s = reduce_rows<TR * NA>(acc);
@@ -1251,7 +1174,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     // whole row blocks only: every output adds its tile sums in column order
     if (n_r == 0) return;
     const uint64_t rb_a = r0 / n_tc;
-    const uint32_t nbs = NB > 0 && !MF ? NB : g.batch;  // sums per row of a tile in LDS
+    const uint32_t nbs = NB > 0 ? NB : g.batch;  // sums per row of a tile in LDS
     const uint32_t per_rb = TR * g.batch;
     for (uint32_t k = threadIdx.x; k < n_r / n_tc * per_rb; k += blockDim.x) {
       const uint64_t rb = rb_a + k / per_rb;
@@ -1310,6 +1233,284 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       }
       link++;
     }
+  }
+}
+
+// ------------------------------------ skinny GEMM, specialised wavefronts
+
+// Y = X W^T on the matrix cores for one matrix of 8-row tiles and up to 16
+// X rows, with two kinds of wavefront in a workgroup.  Each workgroup owns
+// whole row blocks.  Wavefronts 0 .. P-1 decode tiles with the batch-1
+// pipeline (first tiles at once, further ones claimed from an LDS counter
+// 7/8 of the way through the current one, the next tile's loads issued
+// there) and hand every decoded tile to the matrix-core wavefronts through
+// a ring of LDS slots.  Wavefronts P .. P+C-1 (consumer c) keep one column
+// tile's X in registers, in the operand layout of v_mfma_f32_16x16x32_bf16,
+// and multiply each row block's tile of that column by it.  Tiles are
+// handed out in column groups of C columns: within a group row block by row
+// block, consumer c taking column (group C + c), so each column tile's X is
+// loaded once per workgroup, and the decoding never waits for X.
+// A slot's flag counts its uses: 2k means free for its k-th tile, 2k + 1
+// full.  Tile s uses slot s mod S for the (s / S)-th time; a decoding
+// wavefront writes it once the tile s - S has been read, and consumers read
+// their tiles in increasing order, so the lowest unfinished tile can always
+// move on.  Every wait is bounded: past the limit the workgroup marks itself
+// failed and writes NaN for its outputs instead of hanging.
+// Consumer c adds its columns' products to its own partial sums of each row
+// block (in LDS, columns in increasing order); y adds the consumers' partial
+// sums in consumer order, so repeated calls give the same bits.
+constexpr uint32_t kRingRow = 1088;  // bytes per decoded row in a slot: 1 KB + 64 (2-way banked MFMA reads)
+constexpr uint32_t kRingSlot = 8 * kRingRow;
+constexpr int kMcMaxWaves = 16;
+constexpr int kMcMinBatch = 5;  // batch sizes from which the skinny GEMM takes k_skinny_mc (8-row tiles)
+constexpr uint32_t kSpinLimit = 1u << 22;  // polls of a flag (with a short sleep each) before giving up
+
+__device__ __forceinline__ uint32_t flag_load(uint32_t* f) {
+  return uniform(__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+__device__ __forceinline__ void flag_store(uint32_t* f, uint32_t v) {
+  if (lane_id() == 0) __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Wait until *f == want; false (and the workgroup marked failed) past the
+// poll limit or once another wavefront has failed.
+__device__ __forceinline__ bool flag_wait(uint32_t* f, uint32_t want, uint32_t* failed) {
+  for (uint32_t i = 0;; i++) {
+    if (flag_load(f) == want) return true;
+    if (i >= kSpinLimit || flag_load(failed) != 0) {
+      flag_store(failed, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+template <bool FIT2>
+__global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGroup g) {
+  constexpr int TR = 8;
+  using Regs = TileRegs<TR, 0>;
+  __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  const uint32_t P = g.producers, C = g.consumers, SL = g.ring_log2, S = 1u << SL;
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t lane = lane_id();
+  const GemvJob job = g.job[0];
+  const BlobDev& b = job.b;
+  const uint32_t J = g.lane_words;
+  const uint32_t per_wave = g.buf_words + kWave * J;
+  uint32_t* buf = lds + wave * per_wave;  // decoding wavefronts only
+  uint32_t* slot = buf + g.buf_words;
+  const uint32_t ring = lds_addr(lds + P * per_wave);
+  uint32_t* zero4 = lds + P * per_wave + S * (kRingSlot / 4);
+  uint32_t* ctl = zero4 + 4;  // [0] next tile to claim, [1] failed, [2..] slot flags
+  uint32_t* flags = ctl + 2;
+  uint32_t* tw = ctl + ((2 + S + 3) & ~3u);
+  uint32_t* ord = tw + g.tw_words;  // hand-out order: tile s is (row block << 16) | column
+  float* part = reinterpret_cast<float*>(ord + g.tw_words);
+  const uint32_t n_tc = b.n_tc;
+  const uint32_t B = g.batch;
+  // this workgroup's row blocks [rb_a, rb_b) and tiles [r0, r1)
+  const uint64_t G = job.groups, gi = blockIdx.x;
+  const uint64_t rb_a = gi * b.n_tr / G, rb_b = (gi + 1) * b.n_tr / G;
+  const uint32_t n_rb = static_cast<uint32_t>(rb_b - rb_a);
+  const uint64_t r0 = rb_a * n_tc;
+  const uint32_t n_r = n_rb * n_tc;
+  const uint32_t Ce = C < n_tc ? C : n_tc;  // consumers with a column
+  // tile s of the hand-out order -> (row block, column) in the range
+  auto tile_of = [&](uint32_t s, uint32_t& rb, uint32_t& j) __attribute__((always_inline)) {
+    const uint32_t grp = s / (C * n_rb);
+    const uint32_t rest = s - grp * C * n_rb;
+    const uint32_t mc = n_tc - grp * C < C ? n_tc - grp * C : C;
+    rb = rest / mc;
+    j = grp * C + rest % mc;
+  };
+  auto claim = [&]() __attribute__((always_inline)) {
+    uint32_t v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  const bool claims = n_r > P - 1;
+  auto issue = [&](Regs& r, uint32_t ss, bool scalar_words) __attribute__((always_inline)) {
+    uint32_t rb, j;
+    if (scalar_words) {
+      tile_of(ss, rb, j);
+    } else {
+      const uint32_t o = __builtin_amdgcn_readfirstlane(ord[ss]);
+      rb = o >> 16;
+      j = o & 0xFFFFu;
+    }
+    const uint64_t ti = rb_a + rb;
+    const uint64_t t = ti * n_tc + j;
+    uint32_t w0, w1;
+    if (scalar_words) {
+      w0 = sload(b.tile_words, t);
+      w1 = sload(b.tile_words, t + 1);
+    } else {
+      w0 = __builtin_amdgcn_readfirstlane(tw[t - r0]);
+      w1 = __builtin_amdgcn_readfirstlane(tw[t - r0 + 1]);
+    }
+    r.load(b, nullptr, 0, 0, ti, j, w0, w1, buf);
+    asm volatile("" ::: "memory");
+    r.load_rest(b, ti, j);
+  };
+  if (wave == 0) {
+    if (lane == 0) {
+      ctl[0] = P - 1;
+      ctl[1] = 0u;
+    }
+    for (uint32_t i = lane; i < S; i += kWave) flags[i] = 0u;
+    if (lane < 4) zero4[lane] = 0u;
+    for (uint32_t base = 0; base < kTable; base += kWave * 4)
+      __builtin_amdgcn_global_load_lds(b.table + base + lane * 4, tab + base, 16, 0, 0);
+    if (claims) {
+      for (uint32_t i = lane; i <= n_r; i += kWave) tw[i] = b.tile_words[r0 + i];
+      for (uint32_t i = lane; i < n_r; i += kWave) {
+        uint32_t rb, j;
+        tile_of(i, rb, j);
+        ord[i] = (rb << 16) | j;
+      }
+    }
+    wait_vmem();
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's LDS writes are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  uint32_t* failed = ctl + 1;
+
+  if (wave < P) {
+    // ---- decoding wavefront: wavefronts 1 .. P-1 take the first tiles,
+    // wavefront 0 claims (its tile's loads are issued here, after the
+    // barrier, so that no tile's registers live across the split into the
+    // two kinds of wavefront)
+    Regs in;
+    uint32_t s = n_r;
+    if (wave == 0) {
+      if (claims) s = claim();
+    } else if (wave - 1 < n_r) {
+      s = wave - 1;
+    }
+    if (s < n_r) issue(in, s, !claims);
+    constexpr int PRE = TR * 7 / 8;
+    while (s < n_r) {
+      wait_vmem_but<(TR - PRE < TR / 2 ? TR - PRE : TR / 2)>();
+      wave_sync_lds();
+      const uint32_t q0 = interleave(buf, in.w0, in.a0, in.cb(), J, slot);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      wave_sync_lds();
+      uint32_t wv[TR][4];
+#pragma unroll
+      for (int k = 0; k < TR; k++) wv[k][0] = wv[k][1] = wv[k][2] = wv[k][3] = 0u;
+      LaneBits br;
+      br.init(slot, q0);
+      if (in.active) decode_rows<TR, 0, 0, PRE, FIT2>(in, br, tab, wv);
+      wait_vmem();
+      asm volatile("" ::: "memory");
+      Regs nx;
+      const uint32_t sn = claims ? claim() : n_r;
+      if (sn < n_r) issue(nx, sn, false);
+      if (in.active) decode_rows<TR, 0, PRE, TR, FIT2>(in, br, tab, wv);
+      // hand the tile over: slot s mod S, free once tile s - S has been read
+      const uint32_t k = s >> SL, i = s & (S - 1);
+      if (!flag_wait(flags + i, 2 * k, failed)) break;
+      const uint32_t at = ring + i * kRingSlot + lane * 16u;
+#pragma unroll
+      for (int r = 0; r < TR; r++)
+        lds_put4(at + static_cast<uint32_t>(r) * kRingRow, make_uint4(wv[r][0], wv[r][1], wv[r][2], wv[r][3]));
+      flag_store(flags + i, 2 * k + 1);
+      in = nx;
+      s = sn;
+    }
+    // a wavefront that gave up may leave loads in flight: wait for them
+    wait_vmem();
+  } else if (wave - P < Ce) {
+    // ---- matrix-core wavefront c: column tiles c, c + C, ...
+    const uint32_t c = wave - P;
+    const uint32_t m = lane & 15u, gq = lane >> 4;
+    // A operand: row m of the tile (rows 8..15 read the zero words), columns
+    // 8 gq .. + 7 of each 32-column block
+    const uint32_t a_off = m < TR ? m * kRingRow + gq * 16u : 0u;
+    const uint32_t a_step = m < TR ? 64u : 0u;
+    const bool x_row = m < B;
+    bool ok = true;
+    // a column tile's X: lane l holds X row l % 16, columns 512 j + 32 q +
+    // 8 (l / 16) .. + 7 for q = 0 .. 15 (zero past the batch or the matrix)
+    const uint16_t* xrow = job.x + (x_row ? static_cast<uint64_t>(m) * g.ldx : 0);
+    auto x_part = [&](uint32_t j, int q) __attribute__((always_inline)) {
+      const uint64_t kc = static_cast<uint64_t>(j) * 512 + static_cast<uint32_t>(32 * q) + gq * 8u;
+      const bool in_x = x_row && kc < b.cols;
+      uint4 v = *reinterpret_cast<const uint4*>(xrow + (in_x ? kc : 0u));
+      return in_x ? v : make_uint4(0, 0, 0, 0);
+    };
+    uint4 xb[16];
+    if (c < n_tc) {
+#pragma unroll
+      for (int q = 0; q < 16; q++) xb[q] = x_part(c, q);
+    }
+    for (uint32_t grp = 0; ok && grp * C + c < n_tc; grp++) {
+      const uint32_t j = grp * C + c;
+      const uint32_t mc = n_tc - grp * C < C ? n_tc - grp * C : C;
+      // the next column tile's X replaces this one's part by part during the
+      // group's last tile, so its loads overlap that tile's products and the
+      // wait for the next group's first tile (no extra registers)
+      const uint32_t jn = j + C;
+      const bool x_next = jn < n_tc;
+      for (uint32_t rb = 0; rb < n_rb; rb++) {
+        const uint32_t st = grp * C * n_rb + rb * mc + c;
+        const uint32_t k = st >> SL, i = st & (S - 1);
+        if (!flag_wait(flags + i, 2 * k + 1, failed)) {
+          ok = false;
+          break;
+        }
+        // this consumer's partial sums of the row block so far (rows 4 gq ..
+        // + 3 for X row m; lanes of rows 8..15 hold zeros)
+        const uint32_t pp = lds_addr(part) + (((rb * C + c) * TR + gq * 4u) * B + m) * 4u;
+        const bool mine = gq < TR / 4 && x_row;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (grp > 0 && mine) {
+#pragma unroll
+          for (int e = 0; e < 4; e++) acc[e] = __builtin_bit_cast(float, lds_word(pp + e * B * 4u));
+        }
+        const uint32_t a_at = m < TR ? ring + i * kRingSlot + a_off : lds_addr(zero4);
+        // two A operands read at a time (all sixteen at once would not fit
+        // the registers beside X)
+        const bool swap_x = x_next && rb + 1 == n_rb;
+#pragma unroll
+        for (int q2 = 0; q2 < 16; q2 += 2) {
+          uint4 av[2];
+#pragma unroll
+          for (int q = 0; q < 2; q++) av[q] = lds_get4(a_at + static_cast<uint32_t>(q2 + q) * a_step);
+#pragma unroll
+          for (int q = 0; q < 2; q++)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[q]),
+                                                          __builtin_bit_cast(bf16x8_t, xb[q2 + q]), acc, 0, 0, 0);
+          if (swap_x) {
+#pragma unroll
+            for (int q = 0; q < 2; q++) xb[q2 + q] = x_part(jn, q2 + q);
+          }
+          asm volatile("" ::: "memory");
+        }
+        // the slot's reads are done before it is released (release order)
+        flag_store(flags + i, 2 * k + 2);
+        if (mine) {
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            // a copy first: __builtin_bit_cast of a vector element reads element 0
+            const float v = acc[e];
+            lds_put(pp + e * B * 4u, __builtin_bit_cast(uint32_t, v));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // y: the consumers' partial sums of each row, in consumer order
+  const bool bad = flag_load(failed) != 0;
+  for (uint32_t kk = threadIdx.x; kk < n_rb * TR * B; kk += blockDim.x) {
+    const uint32_t rb = kk / (TR * B), rr = (kk / B) % TR, beta = kk % B;
+    const uint64_t row = (rb_a + rb) * TR + rr;
+    if (row >= b.rows) continue;
+    float sum = 0.0f;
+    for (uint32_t c = 0; c < Ce; c++) sum += part[((static_cast<uint64_t>(rb) * C + c) * TR + rr) * B + beta];
+    store_y(job.y, beta * g.ldy + row, bad ? __builtin_nanf("") : sum, g.y_f32);
   }
 }
 
@@ -1677,16 +1878,13 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     lane_words = std::max(lane_words, (((30 + L[j].max_chunk_bits) >> 5) + 2 + 1) & ~1u);
     buf_words = std::max(buf_words, L[j].b.buf_words);
   }
-  // the matrix-core mode passes each decoded tile through the slot (8 rows
-  // of 272 bytes)
-  if (NB == 16) lane_words = std::max(lane_words, 10u);
   // the interleaving copy reads up to lane_words past the last chunk start;
   // whole 256-byte units keep every slot 256-byte aligned
   buf_words = (buf_words + lane_words + 63) & ~63u;
   if (NB == kRawBf16) lane_words = buf_words = 0;  // plain BF16: no stream to stage
   const size_t per_wave = (static_cast<size_t>(kWave) * lane_words + buf_words) * 4;
   constexpr bool SKINNY = NB != kRawBf16 && (NB == 0 || NB > 1);
-  const uint32_t sums = NB < 0 ? 0 : NB == kRawBf16 ? TR : NB == 0 || NB == 16 ? TR * batch : TR * NB;
+  const uint32_t sums = NB < 0 ? 0 : NB == kRawBf16 ? TR : NB == 0 ? TR * batch : TR * NB;
   const uint32_t cus = static_cast<uint32_t>(cu_count());
   if (cus == 0) return NWC_ERR_HIP;
   auto occupancy = [&](uint32_t n, size_t lds, int* k) {
@@ -1809,6 +2007,74 @@ nwc_status launch_fused(const Launch* L, int count, A... a) {
       default: return fit2 ? launch_gemv<32, 4, NB, true>(L, a...) : launch_gemv<32, 4, NB>(L, a...);
     }
   }
+}
+
+// The specialised-wavefront skinny GEMM (k_skinny_mc): one workgroup per CU
+// (16 wavefronts).  Candidates trade decoding wavefronts and ring slots for
+// LDS; each is sized to the most row blocks per range that fit, and the one
+// with the fewest rounds of workgroups over the CUs wins (ties: the first,
+// i.e. the most decoding wavefronts and slots).
+template <bool FIT2>
+nwc_status launch_skinny_mc(const Launch& L, const uint16_t* X, void* Y, int y_f32, hipStream_t s, int batch,
+                            uint64_t ldx, uint64_t ldy) {
+  const uint32_t J = (((30 + L.max_chunk_bits) >> 5) + 2 + 1) & ~1u;
+  const uint32_t bw = (L.b.buf_words + J + 63) & ~63u;
+  const size_t per_wave = (static_cast<size_t>(kWave) * J + bw) * 4;
+  const uint32_t cus = static_cast<uint32_t>(cu_count());
+  if (cus == 0) return NWC_ERR_HIP;
+  const uint64_t n_tr = L.b.n_tr, n_tc = L.b.n_tc;
+  struct Cfg {
+    uint32_t P, C, S;
+  };
+  const Cfg cfgs[] = {{12, 4, 3}, {12, 4, 2}, {10, 4, 2}, {8, 4, 2}};  // S: log2 of the ring slots
+  auto need = [&](const Cfg& c, uint64_t rb) {
+    const uint64_t tw = (rb * n_tc + 1 + 3) & ~3ull;  // tile offsets; the hand-out order takes as many
+    const uint32_t slots = 1u << c.S;
+    return c.P * per_wave + static_cast<size_t>(slots) * kRingSlot + 16 + ((2 + slots + 3) & ~3u) * 4 +
+           2 * tw * 4 + static_cast<size_t>(rb) * c.C * 8 * batch * 4;
+  };
+  int best = -1;
+  uint64_t best_rounds = 0, best_g = 0, best_rb = 0;
+  for (int i = 0; i < static_cast<int>(sizeof(cfgs) / sizeof(cfgs[0])); i++) {
+    uint64_t rb = (n_tr + cus - 1) / cus;
+    while (rb > 1 && need(cfgs[i], rb) > kMaxLds) rb--;
+    if (need(cfgs[i], rb) > kMaxLds) continue;
+    const uint64_t G = (n_tr + rb - 1) / rb;
+    const uint64_t rounds = (G + cus - 1) / cus;
+    if (best < 0 || rounds < best_rounds) {
+      best = i;
+      best_rounds = rounds;
+      best_g = G;
+      best_rb = (n_tr + G - 1) / G;  // the largest range
+    }
+  }
+  if (best < 0) return NWC_ERR_UNSUPPORTED;
+  const Cfg& c = cfgs[best];
+  const size_t lds = need(c, best_rb);
+  if (set_lds(k_skinny_mc<FIT2>, lds) != hipSuccess) return NWC_ERR_HIP;
+  int k = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&k, k_skinny_mc<FIT2>, (c.P + c.C) * kWave, lds) != hipSuccess)
+    return NWC_ERR_HIP;
+  if (k < 1) return NWC_ERR_UNSUPPORTED;
+  GemvGroup g;
+  std::memset(&g, 0, sizeof(g));
+  g.job[0].b = L.b;
+  g.job[0].x = X;
+  g.job[0].y = Y;
+  g.job[0].groups = static_cast<uint32_t>(best_g);
+  g.job[0].whole_rows = 1;
+  g.count = 1;
+  g.y_f32 = y_f32;
+  g.lane_words = J;
+  g.buf_words = bw;
+  g.tw_words = static_cast<uint32_t>((best_rb * n_tc + 1 + 3) & ~3ull);
+  g.ldx = ldx;
+  g.ldy = ldy;
+  g.batch = static_cast<uint32_t>(batch);
+  g.producers = c.P;
+  g.consumers = c.C;
+  g.ring_log2 = c.S;
+  return launch(k_skinny_mc<FIT2>, dim3(static_cast<uint32_t>(best_g)), dim3((c.P + c.C) * kWave), lds, s, g);
 }
 
 // Whether a blob and batch take the skinny mode of the fused kernel (no
@@ -1945,11 +2211,14 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
     // skinny mode of the fused kernel (nwc_workspace_size said so)
     const uint16_t* XX = X;
     void* yy = Y;
-    // up to 32 / TR X rows are multiplied as each pair is decoded; more go
-    // through the tile decoded into registers, and from 10 X rows on (8-row
-    // tiles) through the matrix cores, which then cost less than the
-    // vector products they replace
-    // (with codes of at most 6 bits, the second-lookup-free decode)
+    // up to 32 / TR X rows are multiplied as each pair is decoded; with
+    // 8-row tiles, from 5 X rows on the matrix cores take the products
+    // (k_skinny_mc: on 4096 x 14336, 34.7 / 35.3 / 35.4 us at 5 / 8 / 16
+    // rows, against 41.5 / 41.4 us from the decoded tile in registers at 5 / 8
+    // and 50.6 us at 16 with the products on the matrix cores inside each
+    // decoding wavefront); 16-row tiles multiply more rows from the decoded
+    // tile in registers (with codes of at most 6 bits, the
+    // second-lookup-free decode)
     const bool fit2 = L.max_code_len <= 6;
 #define NWC_SKINNY(TR_, MAXW_, NB_)                                                                      \
   return fit2 ? launch_gemv<TR_, MAXW_, NB_, true>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy) \
@@ -1960,8 +2229,9 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
         case 3:  // a power-of-two count of sums per lane: X row 3 is zero
         case 4: NWC_SKINNY(8, 16, 4);
         default:
-          if (batch < 10) NWC_SKINNY(8, 16, 0);
-          NWC_SKINNY(8, 16, 16);
+          if (batch < kMcMinBatch) NWC_SKINNY(8, 16, 0);
+          return fit2 ? launch_skinny_mc<true>(L, XX, yy, y_f32, s, batch, ldx, ldy)
+                      : launch_skinny_mc<false>(L, XX, yy, y_f32, s, batch, ldx, ldy);
       }
     }
     if (batch == 2) NWC_SKINNY(16, 8, 2);

@@ -270,8 +270,10 @@ nwc_status nwc_gather_rows(const nwc_info *info, const void *blob_dev, const uin
  * matrix-core accumulation path is the planned next step):
  * Y[b, n] = sum_k X[b, k] W[n, k] with X (device, batch x cols, row stride
  * ldx) and Y (device, batch x rows, row stride ldy, y_type).  Same decode as
- * nwc_gemv; FP32 accumulation.  From 10 batch rows on (8-row tiles) the
- * products run on the matrix cores.  Async.
+ * nwc_gemv; FP32 accumulation.  From 5 batch rows on (8-row tiles) the
+ * products run on the matrix cores, fed by wavefronts that only decode
+ * (decoded tiles pass through LDS, never through HBM).  Repeated calls give
+ * the same bits.  Async.
  * Errors: INVALID_ARG (batch outside 2..16), BUFFER_TOO_SMALL, ALIGNMENT, HIP. */
 nwc_status nwc_gemm_skinny(const nwc_info *info, const void *blob_dev, const uint16_t *X_dev,
                            uint64_t ldx, int batch, void *Y_dev, uint64_t ldy,

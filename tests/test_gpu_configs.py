@@ -241,7 +241,7 @@ def _skinny_ref(name):
     return X, _oracle_gemm(_w(4, name), X)
 
 
-@pytest.mark.parametrize("batch", [2, 3, 4, 8, 9, 16])
+@pytest.mark.parametrize("batch", [2, 3, 4, 8, 9, 12, 16])
 @pytest.mark.parametrize("name", ["w_4096x14336", "w_14336x4096"])
 def test_skinny_gemm_all_rows(name, batch):
     info, b = _dev_blob(4, name)

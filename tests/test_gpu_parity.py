@@ -322,6 +322,27 @@ def test_gemm_small(name, params, batch):
             _check_y(Y[beta], Y_ref[beta], A_ref[beta], out_f32, "%s b%d" % (name, beta))
 
 
+@pytest.mark.parametrize("rows,cols", [(1003, 4104), (37, 2056), (3000, 512), (4096, 1536)])
+@pytest.mark.parametrize("batch", [10, 12, 16])
+def test_gemm_matrix_core_shapes(rows, cols, batch):
+    # the matrix-core skinny GEMM (8-row tiles, batch >= 10) on shapes whose
+    # ranges cut the column groups unevenly: a last column tile of 8 columns
+    # (4104), fewer column tiles than matrix-core wavefronts (512, 1536), a
+    # last row block of 3 or 5 rows; every output within the bound, repeats
+    # bitwise equal
+    w = workloads.gaussian_bits((rows, cols), 0.02, 71)
+    X = workloads.gaussian_bits((batch, cols), 1.0, 72)
+    _say("matrix-core gemm %dx%d batch %d" % (rows, cols, batch))
+    b = Blob(w)
+    Y_ref, A_ref = oracle.gemm(w, X)
+    Y = _gemm(b, X, True)
+    Y2 = _gemm(b, X, True)
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+    Yd = _to_f64(Y)
+    for beta in range(batch):
+        _check_y(Yd[beta], Y_ref[beta], A_ref[beta], True, "%dx%d b%d" % (rows, cols, beta))
+
+
 def test_gemm_deterministic():
     w = _w(4, "w_4096x14336")
     X = workloads.activations(4, "w_4096x14336", batch=16)
