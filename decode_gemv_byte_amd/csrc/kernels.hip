@@ -607,8 +607,10 @@ struct GemvGroup {
   uint64_t ldx, ldy;
   uint32_t batch;
   // k_skinny_mc: decoding and matrix-core wavefronts per workgroup, log2 of
-  // the ring slots
-  uint32_t producers, consumers, ring_log2;
+  // the ring slots, LDS words for the per-row-block counters, and whether
+  // the columns of a row block are added along one chain (else each
+  // consumer keeps its own sums)
+  uint32_t producers, consumers, ring_log2, rb_words, chain;
 };
 
 // Registers of one tile for the batch-1 kernel: raw bytes of this lane's
@@ -847,16 +849,28 @@ __device__ __forceinline__ void gemv_rows(const TileRegs<TR, NX>& in, LaneBits& 
 
 // Skinny mode: rows [R0, R1) of the tile decoded into registers, four BF16
 // pairs per row (rows past the matrix edge stay zero).
-template <int TR, int NX, int R0, int R1, bool FIT2 = false>
+// QUAD: two pairs per window read (codes of at most 9 bits).
+template <int TR, int NX, int R0, int R1, bool FIT2 = false, bool QUAD = false>
 __device__ __forceinline__ void decode_rows(const TileRegs<TR, NX>& in, LaneBits& br, const uint32_t* tab,
                                             uint32_t (&wv)[TR][4]) {
+  const uint32_t nrows = __builtin_amdgcn_readfirstlane(in.nrows);
 #pragma unroll
   for (int r = R0; r < R1; r++) {
-    if (static_cast<uint32_t>(r) < in.nrows) {
-      wv[r][0] = assemble(decode_pair<FIT2>(br, tab), in.raw[r].x, false);
-      wv[r][1] = assemble(decode_pair<FIT2>(br, tab), in.raw[r].x, true);
-      wv[r][2] = assemble(decode_pair<FIT2>(br, tab), in.raw[r].y, false);
-      wv[r][3] = assemble(decode_pair<FIT2>(br, tab), in.raw[r].y, true);
+    if (static_cast<uint32_t>(r) < nrows) {
+      uint32_t e0, e1, e2, e3;
+      if constexpr (QUAD) {
+        decode_quad<FIT2>(br, tab, e0, e1);
+        decode_quad<FIT2>(br, tab, e2, e3);
+      } else {
+        e0 = decode_pair<FIT2>(br, tab);
+        e1 = decode_pair<FIT2>(br, tab);
+        e2 = decode_pair<FIT2>(br, tab);
+        e3 = decode_pair<FIT2>(br, tab);
+      }
+      wv[r][0] = assemble(e0, in.raw[r].x, false);
+      wv[r][1] = assemble(e1, in.raw[r].x, true);
+      wv[r][2] = assemble(e2, in.raw[r].y, false);
+      wv[r][3] = assemble(e3, in.raw[r].y, true);
     }
   }
 }
@@ -910,7 +924,7 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 template <int TR, int MAXW, int NB, bool FIT2 = false, bool QUAD = false>
 __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   constexpr bool RAW16 = NB == kRawBf16;
-  static_assert(!QUAD || NB == 1, "two pairs per window: batch 1");
+  static_assert(!QUAD || NB != kRawBf16, "two pairs per window: decoding modes");
   constexpr bool DECODE = NB < 0;
   constexpr bool SKINNY = !RAW16 && (NB == 0 || NB > 1);
   constexpr int NX = NB > 0 && !RAW16 ? NB : 0;  // X rows that come with each tile
@@ -1097,7 +1111,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     LaneBits br;
     br.init(slot, q0);
     if constexpr (NB <= 0) {
-      if (in.active) decode_rows<TR, NX, 0, PRE, FIT2>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, 0, PRE, FIT2, QUAD>(in, br, tab, wv);
     } else {
       if (in.active) gemv_rows<TR, NX, 0, PRE, FIT2, QUAD>(in, br, tab, acc);
     }
@@ -1121,7 +1135,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       nx.load_rest(b, ni, nj);
     }
     if constexpr (DECODE) {
-      if (in.active) decode_rows<TR, NX, PRE, TR, FIT2>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, PRE, TR, FIT2, QUAD>(in, br, tab, wv);
 #pragma unroll
       for (int rr = 0; rr < TR; rr++)
 #pragma unroll
@@ -1131,7 +1145,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       p_nrows = in.nrows;
       p_active = in.active;
     } else if constexpr (NB == 0) {
-      if (in.active) decode_rows<TR, NX, PRE, TR, FIT2>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, NX, PRE, TR, FIT2, QUAD>(in, br, tab, wv);
       // X rows in groups of GB: TR GB sums per lane, reduced over the
       // wavefront at once; lanes 2v and 2v + 1 end with sum v (row v / GB,
       // batch row g GB + v % GB)
@@ -1256,9 +1270,18 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
 // their tiles in increasing order, so the lowest unfinished tile can always
 // move on.  Every wait is bounded: past the limit the workgroup marks itself
 // failed and writes NaN for its outputs instead of hanging.
-// Consumer c adds its columns' products to its own partial sums of each row
-// block (in LDS, columns in increasing order); y adds the consumers' partial
-// sums in consumer order, so repeated calls give the same bits.
+// Sums in LDS, in a fixed order either way, so repeated calls give the same
+// bits.  Per consumer (when they fit): consumer c adds its columns to its own
+// sums of each row block, and y adds the consumers' sums in consumer order.
+// Chained (for ranges of many row blocks, where per-consumer sums would cost
+// LDS that decoding wavefronts need): a row block's sums take each column in
+// column order -- the consumer of column j waits until column j - 1 is in (a
+// counter per row block), starts its MFMA chain from the sums and writes them
+// back.  Waiting for the previous column never blocks the lowest unfinished
+// tile: its previous column is an earlier tile.  With few row blocks per
+// range the chain serialises the consumers (4096 x 14336: 45 against 35 us),
+// with many it lets the launch keep 12 decoding wavefronts in one round of
+// workgroups (LM head at batch 8: 217 against 314 us).
 constexpr uint32_t kRingRow = 1088;  // bytes per decoded row in a slot: 1 KB + 64 (2-way banked MFMA reads)
 constexpr uint32_t kRingSlot = 8 * kRingRow;
 constexpr int kMcMaxWaves = 16;
@@ -1284,7 +1307,7 @@ __device__ __forceinline__ bool flag_wait(uint32_t* f, uint32_t want, uint32_t* 
   }
 }
 
-template <bool FIT2>
+template <bool FIT2, bool QUAD>
 __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGroup g) {
   constexpr int TR = 8;
   using Regs = TileRegs<TR, 0>;
@@ -1305,7 +1328,8 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
   uint32_t* flags = ctl + 2;
   uint32_t* tw = ctl + ((2 + S + 3) & ~3u);
   uint32_t* ord = tw + g.tw_words;  // hand-out order: tile s is (row block << 16) | column
-  float* part = reinterpret_cast<float*>(ord + g.tw_words);
+  uint32_t* done = ord + g.tw_words;  // per row block: columns added to its sums so far
+  float* part = reinterpret_cast<float*>(done + g.rb_words);
   const uint32_t n_tc = b.n_tc;
   const uint32_t B = g.batch;
   // this workgroup's row blocks [rb_a, rb_b) and tiles [r0, r1)
@@ -1315,6 +1339,7 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
   const uint64_t r0 = rb_a * n_tc;
   const uint32_t n_r = n_rb * n_tc;
   const uint32_t Ce = C < n_tc ? C : n_tc;  // consumers with a column
+  const bool chain = g.chain != 0;
   // tile s of the hand-out order -> (row block, column) in the range
   auto tile_of = [&](uint32_t s, uint32_t& rb, uint32_t& j) __attribute__((always_inline)) {
     const uint32_t grp = s / (C * n_rb);
@@ -1358,6 +1383,7 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
       ctl[1] = 0u;
     }
     for (uint32_t i = lane; i < S; i += kWave) flags[i] = 0u;
+    for (uint32_t i = lane; i < n_rb; i += kWave) done[i] = 0u;
     if (lane < 4) zero4[lane] = 0u;
     for (uint32_t base = 0; base < kTable; base += kWave * 4)
       __builtin_amdgcn_global_load_lds(b.table + base + lane * 4, tab + base, 16, 0, 0);
@@ -1401,13 +1427,13 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
       for (int k = 0; k < TR; k++) wv[k][0] = wv[k][1] = wv[k][2] = wv[k][3] = 0u;
       LaneBits br;
       br.init(slot, q0);
-      if (in.active) decode_rows<TR, 0, 0, PRE, FIT2>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, 0, 0, PRE, FIT2, QUAD>(in, br, tab, wv);
       wait_vmem();
       asm volatile("" ::: "memory");
       Regs nx;
       const uint32_t sn = claims ? claim() : n_r;
       if (sn < n_r) issue(nx, sn, false);
-      if (in.active) decode_rows<TR, 0, PRE, TR, FIT2>(in, br, tab, wv);
+      if (in.active) decode_rows<TR, 0, PRE, TR, FIT2, QUAD>(in, br, tab, wv);
       // hand the tile over: slot s mod S, free once tile s - S has been read
       const uint32_t k = s >> SL, i = s & (S - 1);
       if (!flag_wait(flags + i, 2 * k, failed)) break;
@@ -1460,12 +1486,19 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
           ok = false;
           break;
         }
-        // this consumer's partial sums of the row block so far (rows 4 gq ..
-        // + 3 for X row m; lanes of rows 8..15 hold zeros)
-        const uint32_t pp = lds_addr(part) + (((rb * C + c) * TR + gq * 4u) * B + m) * 4u;
+        // chain: the row block's sums over columns 0 .. j-1 (the previous
+        // column's consumer has added its tile: columns are added in
+        // order); else this consumer's own sums over its earlier columns.
+        // Rows 4 gq .. + 3 for X row m; lanes of rows 8..15 hold zeros.
+        if (chain && !flag_wait(done + rb, j, failed)) {
+          ok = false;
+          break;
+        }
+        const uint32_t pp =
+            lds_addr(part) + (((chain ? rb : rb * C + c) * TR + gq * 4u) * B + m) * 4u;
         const bool mine = gq < TR / 4 && x_row;
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (grp > 0 && mine) {
+        if ((chain ? j : grp) > 0 && mine) {
 #pragma unroll
           for (int e = 0; e < 4; e++) acc[e] = __builtin_bit_cast(float, lds_word(pp + e * B * 4u));
         }
@@ -1498,18 +1531,24 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
             lds_put(pp + e * B * 4u, __builtin_bit_cast(uint32_t, v));
           }
         }
+        // the sums now cover column j (release: after the stores above)
+        if (chain) flag_store(done + rb, j + 1);
       }
     }
   }
   __syncthreads();
-  // y: the consumers' partial sums of each row, in consumer order
+  // y: each row block's sums over all its columns
   const bool bad = flag_load(failed) != 0;
   for (uint32_t kk = threadIdx.x; kk < n_rb * TR * B; kk += blockDim.x) {
     const uint32_t rb = kk / (TR * B), rr = (kk / B) % TR, beta = kk % B;
     const uint64_t row = (rb_a + rb) * TR + rr;
     if (row >= b.rows) continue;
-    float sum = 0.0f;
-    for (uint32_t c = 0; c < Ce; c++) sum += part[((static_cast<uint64_t>(rb) * C + c) * TR + rr) * B + beta];
+    float sum = part[kk];
+    if (!chain) {
+      // the consumers' sums, in consumer order
+      sum = 0.0f;
+      for (uint32_t c = 0; c < Ce; c++) sum += part[((rb * C + c) * TR + rr) * B + beta];
+    }
     store_y(job.y, beta * g.ldy + row, bad ? __builtin_nanf("") : sum, g.y_f32);
   }
 }
@@ -1998,14 +2037,22 @@ nwc_status launch_fused(const Launch* L, int count, A... a) {
       default: return launch_batch1<32, 4>(L, count, a...);
     }
   } else {
-    bool fit2 = true;
-    for (int j = 0; j < count; j++) fit2 = fit2 && L[j].max_code_len <= 6;
-    switch (L[0].b.tr) {
-      case 4: return fit2 ? launch_gemv<4, 16, NB, true>(L, a...) : launch_gemv<4, 16, NB>(L, a...);
-      case 8: return fit2 ? launch_gemv<8, 16, NB, true>(L, a...) : launch_gemv<8, 16, NB>(L, a...);
-      case 16: return fit2 ? launch_gemv<16, 8, NB, true>(L, a...) : launch_gemv<16, 8, NB>(L, a...);
-      default: return fit2 ? launch_gemv<32, 4, NB, true>(L, a...) : launch_gemv<32, 4, NB>(L, a...);
+    bool fit2 = true, quad = true;
+    for (int j = 0; j < count; j++) {
+      fit2 = fit2 && L[j].max_code_len <= 6;
+      quad = quad && L[j].max_code_len <= 9;
     }
+#define NWC_DECODE(TR_, MAXW_)                                             \
+  return fit2   ? launch_gemv<TR_, MAXW_, NB, true, true>(L, a...)  \
+         : quad ? launch_gemv<TR_, MAXW_, NB, false, true>(L, a...) \
+                : launch_gemv<TR_, MAXW_, NB, false, false>(L, a...)
+    switch (L[0].b.tr) {
+      case 4: NWC_DECODE(4, 16);
+      case 8: NWC_DECODE(8, 16);
+      case 16: NWC_DECODE(16, 8);
+      default: NWC_DECODE(32, 4);
+    }
+#undef NWC_DECODE
   }
 }
 
@@ -2014,7 +2061,7 @@ nwc_status launch_fused(const Launch* L, int count, A... a) {
 // LDS; each is sized to the most row blocks per range that fit, and the one
 // with the fewest rounds of workgroups over the CUs wins (ties: the first,
 // i.e. the most decoding wavefronts and slots).
-template <bool FIT2>
+template <bool FIT2, bool QUAD>
 nwc_status launch_skinny_mc(const Launch& L, const uint16_t* X, void* Y, int y_f32, hipStream_t s, int batch,
                             uint64_t ldx, uint64_t ldy) {
   const uint32_t J = (((30 + L.max_chunk_bits) >> 5) + 2 + 1) & ~1u;
@@ -2027,33 +2074,41 @@ nwc_status launch_skinny_mc(const Launch& L, const uint16_t* X, void* Y, int y_f
     uint32_t P, C, S;
   };
   const Cfg cfgs[] = {{12, 4, 3}, {12, 4, 2}, {10, 4, 2}, {8, 4, 2}};  // S: log2 of the ring slots
-  auto need = [&](const Cfg& c, uint64_t rb) {
+  auto need = [&](const Cfg& c, uint64_t rb, bool chain) {
     const uint64_t tw = (rb * n_tc + 1 + 3) & ~3ull;  // tile offsets; the hand-out order takes as many
     const uint32_t slots = 1u << c.S;
     return c.P * per_wave + static_cast<size_t>(slots) * kRingSlot + 16 + ((2 + slots + 3) & ~3u) * 4 +
-           2 * tw * 4 + static_cast<size_t>(rb) * c.C * 8 * batch * 4;
+           2 * tw * 4 + ((rb + 3) & ~3ull) * 4 + static_cast<size_t>(rb) * (chain ? 1 : c.C) * 8 * batch * 4;
   };
-  int best = -1;
-  uint64_t best_rounds = 0, best_g = 0, best_rb = 0;
-  for (int i = 0; i < static_cast<int>(sizeof(cfgs) / sizeof(cfgs[0])); i++) {
-    uint64_t rb = (n_tr + cus - 1) / cus;
-    while (rb > 1 && need(cfgs[i], rb) > kMaxLds) rb--;
-    if (need(cfgs[i], rb) > kMaxLds) continue;
-    const uint64_t G = (n_tr + rb - 1) / rb;
-    const uint64_t rounds = (G + cus - 1) / cus;
-    if (best < 0 || rounds < best_rounds) {
-      best = i;
-      best_rounds = rounds;
-      best_g = G;
-      best_rb = (n_tr + G - 1) / G;  // the largest range
+  // per chaining choice: the candidate with the fewest rounds (first on ties)
+  int best[2] = {-1, -1};
+  uint64_t best_rounds[2] = {0, 0}, best_g[2] = {0, 0}, best_rb[2] = {0, 0};
+  for (int ch = 0; ch < 2; ch++)
+    for (int i = 0; i < static_cast<int>(sizeof(cfgs) / sizeof(cfgs[0])); i++) {
+      uint64_t rb = (n_tr + cus - 1) / cus;
+      while (rb > 1 && need(cfgs[i], rb, ch) > kMaxLds) rb--;
+      if (need(cfgs[i], rb, ch) > kMaxLds) continue;
+      const uint64_t G = (n_tr + rb - 1) / rb;
+      const uint64_t rounds = (G + cus - 1) / cus;
+      if (best[ch] < 0 || rounds < best_rounds[ch]) {
+        best[ch] = i;
+        best_rounds[ch] = rounds;
+        best_g[ch] = G;
+        best_rb[ch] = (n_tr + G - 1) / G;  // the largest range
+      }
     }
-  }
-  if (best < 0) return NWC_ERR_UNSUPPORTED;
-  const Cfg& c = cfgs[best];
-  const size_t lds = need(c, best_rb);
-  if (set_lds(k_skinny_mc<FIT2>, lds) != hipSuccess) return NWC_ERR_HIP;
+  // per-consumer sums unless chaining gets fewer rounds or more decoding
+  // wavefronts / ring slots (an earlier candidate)
+  int ch = 0;
+  if (best[0] < 0 || (best[1] >= 0 && (best_rounds[1] < best_rounds[0] ||
+                                       (best_rounds[1] == best_rounds[0] && best[1] < best[0]))))
+    ch = 1;
+  if (best[ch] < 0) return NWC_ERR_UNSUPPORTED;
+  const Cfg& c = cfgs[best[ch]];
+  const size_t lds = need(c, best_rb[ch], ch);
+  if (set_lds(k_skinny_mc<FIT2, QUAD>, lds) != hipSuccess) return NWC_ERR_HIP;
   int k = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&k, k_skinny_mc<FIT2>, (c.P + c.C) * kWave, lds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&k, k_skinny_mc<FIT2, QUAD>, (c.P + c.C) * kWave, lds) != hipSuccess)
     return NWC_ERR_HIP;
   if (k < 1) return NWC_ERR_UNSUPPORTED;
   GemvGroup g;
@@ -2061,20 +2116,23 @@ nwc_status launch_skinny_mc(const Launch& L, const uint16_t* X, void* Y, int y_f
   g.job[0].b = L.b;
   g.job[0].x = X;
   g.job[0].y = Y;
-  g.job[0].groups = static_cast<uint32_t>(best_g);
+  g.job[0].groups = static_cast<uint32_t>(best_g[ch]);
   g.job[0].whole_rows = 1;
   g.count = 1;
   g.y_f32 = y_f32;
   g.lane_words = J;
   g.buf_words = bw;
-  g.tw_words = static_cast<uint32_t>((best_rb * n_tc + 1 + 3) & ~3ull);
+  g.tw_words = static_cast<uint32_t>((best_rb[ch] * n_tc + 1 + 3) & ~3ull);
   g.ldx = ldx;
   g.ldy = ldy;
   g.batch = static_cast<uint32_t>(batch);
   g.producers = c.P;
   g.consumers = c.C;
   g.ring_log2 = c.S;
-  return launch(k_skinny_mc<FIT2>, dim3(static_cast<uint32_t>(best_g)), dim3((c.P + c.C) * kWave), lds, s, g);
+  g.rb_words = static_cast<uint32_t>((best_rb[ch] + 3) & ~3ull);
+  g.chain = static_cast<uint32_t>(ch);
+  return launch(k_skinny_mc<FIT2, QUAD>, dim3(static_cast<uint32_t>(best_g[ch])), dim3((c.P + c.C) * kWave), lds, s,
+                g);
 }
 
 // Whether a blob and batch take the skinny mode of the fused kernel (no
@@ -2219,10 +2277,11 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
     // decoding wavefront); 16-row tiles multiply more rows from the decoded
     // tile in registers (with codes of at most 6 bits, the
     // second-lookup-free decode)
-    const bool fit2 = L.max_code_len <= 6;
-#define NWC_SKINNY(TR_, MAXW_, NB_)                                                                      \
-  return fit2 ? launch_gemv<TR_, MAXW_, NB_, true>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy) \
-              : launch_gemv<TR_, MAXW_, NB_>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy)
+    const bool fit2 = L.max_code_len <= 6, quad = L.max_code_len <= 9;
+#define NWC_SKINNY(TR_, MAXW_, NB_)                                                                             \
+  return fit2   ? launch_gemv<TR_, MAXW_, NB_, true, true>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy)  \
+         : quad ? launch_gemv<TR_, MAXW_, NB_, false, true>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy) \
+                : launch_gemv<TR_, MAXW_, NB_, false, false>(&L, &XX, &yy, nullptr, 1, y_f32, s, batch, ldx, ldy)
     if (L.b.tr == 8) {
       switch (batch) {
         case 2: NWC_SKINNY(8, 16, 2);
@@ -2230,8 +2289,9 @@ static nwc_status gemm_common(const nwc_info* info, const void* blob_dev, const 
         case 4: NWC_SKINNY(8, 16, 4);
         default:
           if (batch < kMcMinBatch) NWC_SKINNY(8, 16, 0);
-          return fit2 ? launch_skinny_mc<true>(L, XX, yy, y_f32, s, batch, ldx, ldy)
-                      : launch_skinny_mc<false>(L, XX, yy, y_f32, s, batch, ldx, ldy);
+          if (fit2) return launch_skinny_mc<true, true>(L, XX, yy, y_f32, s, batch, ldx, ldy);
+          if (L.max_code_len <= 9) return launch_skinny_mc<false, true>(L, XX, yy, y_f32, s, batch, ldx, ldy);
+          return launch_skinny_mc<false, false>(L, XX, yy, y_f32, s, batch, ldx, ldy);
       }
     }
     if (batch == 2) NWC_SKINNY(16, 8, 2);

@@ -322,14 +322,15 @@ def test_gemm_small(name, params, batch):
             _check_y(Y[beta], Y_ref[beta], A_ref[beta], out_f32, "%s b%d" % (name, beta))
 
 
-@pytest.mark.parametrize("rows,cols", [(1003, 4104), (37, 2056), (3000, 512), (4096, 1536)])
-@pytest.mark.parametrize("batch", [10, 12, 16])
+@pytest.mark.parametrize("rows,cols", [(1003, 4104), (37, 2056), (3000, 512), (4096, 1536), (30000, 1024)])
+@pytest.mark.parametrize("batch", [5, 10, 16])
 def test_gemm_matrix_core_shapes(rows, cols, batch):
-    # the matrix-core skinny GEMM (8-row tiles, batch >= 10) on shapes whose
+    # the matrix-core skinny GEMM (8-row tiles, batch >= 5) on shapes whose
     # ranges cut the column groups unevenly: a last column tile of 8 columns
     # (4104), fewer column tiles than matrix-core wavefronts (512, 1536), a
-    # last row block of 3 or 5 rows; every output within the bound, repeats
-    # bitwise equal
+    # last row block of 3 or 5 rows, and ranges of 15 row blocks whose sums
+    # are chained column by column (30000 rows); every output within the
+    # bound, repeats bitwise equal
     w = workloads.gaussian_bits((rows, cols), 0.02, 71)
     X = workloads.gaussian_bits((batch, cols), 1.0, 72)
     _say("matrix-core gemm %dx%d batch %d" % (rows, cols, batch))
