@@ -507,8 +507,12 @@ def main():
         return e0.elapsed_time(e1) * 1e3 / reps
 
     dom_name = "+".join("%s%s" % (n, "@%d" % l if wl.layers > 1 else "") for (l, n) in groups[gi])
-    kernel = ("k_gemv via nwc_gemv_batched" if batch == 1 else "k_gemv skinny mode via nwc_gemm_skinny"
-              if batch <= 16 else "k_gemv decode mode + hipBLASLt GEMM via nwc_gemm_prefill")
+    # the skinny GEMM runs on the matrix cores (k_skinny_mc) from 5 X rows with 8-row tiles
+    mc = 5 <= batch <= 16 and all(info[k].tile_rows == 8 for k in groups[gi])
+    kernel = ("k_gemv via nwc_gemv_batched" if batch == 1 else
+              "k_skinny_mc via nwc_gemm_skinny" if mc else
+              "k_gemv skinny mode via nwc_gemm_skinny" if batch <= 16 else
+              "k_gemv decode mode + hipBLASLt GEMM via nwc_gemm_prefill")
 
     def roofline(us):
         if batch <= 16:
