@@ -8,7 +8,7 @@ launched in the order a decode step needs them, GEMVs that read the same
 activations sharing a launch (128 launches, one graph).  Other workloads:
   1  one 1024x1024 matrix, batch 1
   2  one Qwen3-4B-shaped decoder layer, batch 1
-  4  skinny decode-GEMM, 4096x14336 and 14336x4096, --batch 2..16
+  4  skinny decode-GEMM, 4096x14336 and 14336x4096, --batch 2..32 (more: decode + hipBLASLt)
   5  LM head 128256x4096, --batch 1 or 8
 
 Inputs are resident in HBM before timing starts.  To measure HBM rather than
@@ -97,6 +97,8 @@ def parse():
     ap.add_argument("--roofline-reps", type=int, default=200)
     ap.add_argument("--roofline-only", action="store_true", help="time only the dominant launch")
     ap.add_argument("--skip-bf16", action="store_true", help="skip the plain-BF16 comparators")
+    ap.add_argument("--force-prefill", action="store_true",
+                    help="batches above 1 through decode + hipBLASLt even where the skinny GEMM takes them")
     ap.add_argument("--tile-rows", type=int, default=0, help="encoder tile rows (0 = library default)")
     ap.add_argument("--max-code-len", type=int, default=0, help="encoder code length limit (0 = library default)")
     ap.add_argument("--pair-fit", type=int, default=0, metavar="K",
@@ -420,6 +422,10 @@ def main():
             del w
     enc_s = time.time() - t0
     note("encoded %d matrices in %.1f s" % (len(keys), enc_s))
+    # the fused skinny GEMM takes up to 16 X rows, up to 32 with 8-row tiles
+    # (matrix cores); more go through the decode + hipBLASLt path
+    skinny = batch > 1 and not args.force_prefill and (
+        batch <= 16 or (batch <= 32 and all(info[k].tile_rows == 8 for k in keys)))
 
     def cbytes(k):  # compressed bytes of one GEMV / GEMM: blob + x + y
         return host_blob[k].size + 2 * batch * (info[k].cols + info[k].rows)
@@ -453,7 +459,7 @@ def main():
 
         def launch(c, i):
             nwc.nwc_gemv_batched(launches[c][i], stream=stream)
-    elif batch <= 16:
+    elif skinny:
         kws = {k: zeroed(nwc.nwc_workspace_size(info[k], batch)) for k in keys}
 
         def launch(c, i):
@@ -487,7 +493,7 @@ def main():
     def launch_dominant(c):
         if batch == 1:
             nwc.nwc_gemv_batched(dbatch[c], stream=stream)
-        elif batch <= 16:
+        elif skinny:
             for k in groups[gi]:
                 nwc.nwc_gemm_skinny(info[k], dblobs[c][k], xs[k], ys[k], kws[k], stream=stream)
         else:
@@ -508,14 +514,14 @@ def main():
 
     dom_name = "+".join("%s%s" % (n, "@%d" % l if wl.layers > 1 else "") for (l, n) in groups[gi])
     # the skinny GEMM runs on the matrix cores (k_skinny_mc) from 5 X rows with 8-row tiles
-    mc = 5 <= batch <= 16 and all(info[k].tile_rows == 8 for k in groups[gi])
+    mc = skinny and batch >= 5 and all(info[k].tile_rows == 8 for k in groups[gi])
     kernel = ("k_gemv via nwc_gemv_batched" if batch == 1 else
               "k_skinny_mc via nwc_gemm_skinny" if mc else
-              "k_gemv skinny mode via nwc_gemm_skinny" if batch <= 16 else
+              "k_gemv skinny mode via nwc_gemm_skinny" if skinny else
               "k_gemv decode mode + hipBLASLt GEMM via nwc_gemm_prefill")
 
     def roofline(us):
-        if batch <= 16:
+        if batch == 1 or skinny:
             a = gbytes[gi] / (us * 1e-6) / 1e9
             return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(a / HBM_PEAK_GBPS, 4),
@@ -734,7 +740,7 @@ def main():
                    "launch_order": groups_named, "launches_per_step": len(groups),
                    "device_copies": copies, "hip_graph": graphs is not None, "output": "bf16",
                    "encoder": ({"tuned": tuned} if tuned else params or "default"),
-                   "path": ("fused decode-GEMV" if batch == 1 else "fused skinny decode-GEMM" if batch <= 16
+                   "path": ("fused decode-GEMV" if batch == 1 else "fused skinny decode-GEMM" if skinny
                             else "decode to BF16 + hipBLASLt GEMM")},
         "compressed_GBps": round(value, 1),
         "uncompressed_equiv_GBps": round(value_u, 1),

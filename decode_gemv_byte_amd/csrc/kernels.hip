@@ -610,7 +610,7 @@ struct GemvGroup {
   // the ring slots, LDS words for the per-row-block counters, and whether
   // the columns of a row block are added along one chain (else each
   // consumer keeps its own sums)
-  uint32_t producers, consumers, ring_log2, rb_words, chain;
+  uint32_t producers, consumers, ring_log2, rb_words, chain, batch_groups;
 };
 
 // Registers of one tile for the batch-1 kernel: raw bytes of this lane's
@@ -1252,24 +1252,30 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
 
 // ------------------------------------ skinny GEMM, specialised wavefronts
 
-// Y = X W^T on the matrix cores for one matrix of 8-row tiles and up to 16
-// X rows, with two kinds of wavefront in a workgroup.  Each workgroup owns
-// whole row blocks.  Wavefronts 0 .. P-1 decode tiles with the batch-1
-// pipeline (first tiles at once, further ones claimed from an LDS counter
-// 7/8 of the way through the current one, the next tile's loads issued
-// there) and hand every decoded tile to the matrix-core wavefronts through
-// a ring of LDS slots.  Wavefronts P .. P+C-1 (consumer c) keep one column
-// tile's X in registers, in the operand layout of v_mfma_f32_16x16x32_bf16,
-// and multiply each row block's tile of that column by it.  Tiles are
-// handed out in column groups of C columns: within a group row block by row
-// block, consumer c taking column (group C + c), so each column tile's X is
-// loaded once per workgroup, and the decoding never waits for X.
-// A slot's flag counts its uses: 2k means free for its k-th tile, 2k + 1
-// full.  Tile s uses slot s mod S for the (s / S)-th time; a decoding
-// wavefront writes it once the tile s - S has been read, and consumers read
-// their tiles in increasing order, so the lowest unfinished tile can always
-// move on.  Every wait is bounded: past the limit the workgroup marks itself
-// failed and writes NaN for its outputs instead of hanging.
+// Y = X W^T on the matrix cores for one matrix of 8-row tiles and up to 32
+// X rows (one or two groups of 16, the MFMA's N), with two kinds of
+// wavefront in a workgroup.  Each workgroup owns whole row blocks.
+// Wavefronts 0 .. P-1 decode tiles with the batch-1 pipeline (first tiles at
+// once, further ones claimed from an LDS counter 7/8 of the way through the
+// current one, the next tile's loads issued there) and hand every decoded
+// tile to the matrix-core wavefronts through a ring of LDS slots.
+// Wavefronts P .. P+C-1 (consumers) keep one column tile's X for one batch
+// group in registers, in the operand layout of v_mfma_f32_16x16x32_bf16, and
+// multiply each row block's tile of that column by it.  With CG = C / (batch
+// groups) consumers per batch group, tiles are handed out in column groups of
+// CG columns: within a group row block by row block, consumer c' of each
+// batch group taking column (group CG + c').  So each column tile's X is
+// loaded once per workgroup and batch group, every tile is read once per
+// batch group, and the decoding never waits for X.
+// A slot's flag counts its uses and reads: k (G + 2) means free for its k-th
+// tile, k (G + 2) + 1 full, then one more per batch group's read, and the
+// last read adds one more, which makes it free for the next use (G batch
+// groups).  Tile s uses slot s mod S for the (s / S)-th time; a decoding
+// wavefront writes it once tile s - S has been read by every batch group,
+// and consumers read their tiles in increasing order, so the lowest
+// unfinished tile can always move on.  Every wait is bounded: past the limit
+// the workgroup marks itself failed and writes NaN for its outputs instead
+// of hanging.
 // Sums in LDS, in a fixed order either way, so repeated calls give the same
 // bits.  Per consumer (when they fit): consumer c adds its columns to its own
 // sums of each row block, and y adds the consumers' sums in consumer order.
@@ -1286,6 +1292,11 @@ constexpr uint32_t kRingRow = 1088;  // bytes per decoded row in a slot: 1 KB + 
 constexpr uint32_t kRingSlot = 8 * kRingRow;
 constexpr int kMcMaxWaves = 16;
 constexpr int kMcMinBatch = 5;  // batch sizes from which the skinny GEMM takes k_skinny_mc (8-row tiles)
+// the skinny GEMM's largest batch (k_skinny_mc: two groups of 16 X rows).  On
+// 4096 x 14336 + 14336 x 4096 at 32 rows it takes 101 us against 128 us for
+// decode + hipBLASLt; at 64 rows (four groups, each matrix-core wavefront then
+// walking every column and reloading X for each) 167 against 146 us.
+constexpr int kMaxSkinnyBatch = 32;
 constexpr uint32_t kSpinLimit = 1u << 22;  // polls of a flag (with a short sleep each) before giving up
 
 __device__ __forceinline__ uint32_t flag_load(uint32_t* f) {
@@ -1305,6 +1316,25 @@ __device__ __forceinline__ bool flag_wait(uint32_t* f, uint32_t want, uint32_t* 
     }
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// Wait until *f >= want (same bound as flag_wait).
+__device__ __forceinline__ bool flag_wait_ge(uint32_t* f, uint32_t want, uint32_t* failed) {
+  for (uint32_t i = 0;; i++) {
+    if (flag_load(f) >= want) return true;
+    if (i >= kSpinLimit || flag_load(failed) != 0) {
+      flag_store(failed, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+// Add v to *f (one lane, release after this wavefront's earlier LDS
+// accesses); returns the value before, the same in every lane.
+__device__ __forceinline__ uint32_t flag_add(uint32_t* f, uint32_t v) {
+  uint32_t old = 0;
+  if (lane_id() == 0) old = __hip_atomic_fetch_add(f, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return uniform(old);
 }
 
 template <bool FIT2, bool QUAD>
@@ -1338,15 +1368,20 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
   const uint32_t n_rb = static_cast<uint32_t>(rb_b - rb_a);
   const uint64_t r0 = rb_a * n_tc;
   const uint32_t n_r = n_rb * n_tc;
-  const uint32_t Ce = C < n_tc ? C : n_tc;  // consumers with a column
+  // X rows come in groups of 16 (the MFMA's N); consumer c serves batch
+  // group c / CG and the columns c % CG, c % CG + CG, ...; every tile is read
+  // by one consumer of each batch group
+  const uint32_t NG = g.batch_groups, CG = C / NG;
+  const uint32_t CGe = CG < n_tc ? CG : n_tc;  // consumers of a batch group with a column
   const bool chain = g.chain != 0;
+  const uint32_t use = NG + 2;  // flag values per use of a slot: free, full, one per read
   // tile s of the hand-out order -> (row block, column) in the range
   auto tile_of = [&](uint32_t s, uint32_t& rb, uint32_t& j) __attribute__((always_inline)) {
-    const uint32_t grp = s / (C * n_rb);
-    const uint32_t rest = s - grp * C * n_rb;
-    const uint32_t mc = n_tc - grp * C < C ? n_tc - grp * C : C;
+    const uint32_t grp = s / (CG * n_rb);
+    const uint32_t rest = s - grp * CG * n_rb;
+    const uint32_t mc = n_tc - grp * CG < CG ? n_tc - grp * CG : CG;
     rb = rest / mc;
-    j = grp * C + rest % mc;
+    j = grp * CG + rest % mc;
   };
   auto claim = [&]() __attribute__((always_inline)) {
     uint32_t v = 0;
@@ -1383,7 +1418,7 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
       ctl[1] = 0u;
     }
     for (uint32_t i = lane; i < S; i += kWave) flags[i] = 0u;
-    for (uint32_t i = lane; i < n_rb; i += kWave) done[i] = 0u;
+    for (uint32_t i = lane; i < NG * n_rb; i += kWave) done[i] = 0u;
     if (lane < 4) zero4[lane] = 0u;
     for (uint32_t base = 0; base < kTable; base += kWave * 4)
       __builtin_amdgcn_global_load_lds(b.table + base + lane * 4, tab + base, 16, 0, 0);
@@ -1435,31 +1470,34 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
       if (sn < n_r) issue(nx, sn, false);
       if (in.active) decode_rows<TR, 0, PRE, TR, FIT2, QUAD>(in, br, tab, wv);
       // hand the tile over: slot s mod S, free once tile s - S has been read
+      // by every batch group
       const uint32_t k = s >> SL, i = s & (S - 1);
-      if (!flag_wait(flags + i, 2 * k, failed)) break;
+      if (!flag_wait(flags + i, k * use, failed)) break;
       const uint32_t at = ring + i * kRingSlot + lane * 16u;
 #pragma unroll
       for (int r = 0; r < TR; r++)
         lds_put4(at + static_cast<uint32_t>(r) * kRingRow, make_uint4(wv[r][0], wv[r][1], wv[r][2], wv[r][3]));
-      flag_store(flags + i, 2 * k + 1);
+      flag_store(flags + i, k * use + 1);
       in = nx;
       s = sn;
     }
     // a wavefront that gave up may leave loads in flight: wait for them
     wait_vmem();
-  } else if (wave - P < Ce) {
-    // ---- matrix-core wavefront c: column tiles c, c + C, ...
-    const uint32_t c = wave - P;
+  } else if ((wave - P) % CG < CGe) {
+    // ---- matrix-core wavefront c: batch group bg, columns cc, cc + CG, ...
+    const uint32_t c = wave - P, bg = c / CG, cc = c % CG;
     const uint32_t m = lane & 15u, gq = lane >> 4;
     // A operand: row m of the tile (rows 8..15 read the zero words), columns
     // 8 gq .. + 7 of each 32-column block
     const uint32_t a_off = m < TR ? m * kRingRow + gq * 16u : 0u;
     const uint32_t a_step = m < TR ? 64u : 0u;
-    const bool x_row = m < B;
+    const uint32_t xr = bg * 16u + m;  // this lane's X row
+    const bool x_row = xr < B;
     bool ok = true;
-    // a column tile's X: lane l holds X row l % 16, columns 512 j + 32 q +
-    // 8 (l / 16) .. + 7 for q = 0 .. 15 (zero past the batch or the matrix)
-    const uint16_t* xrow = job.x + (x_row ? static_cast<uint64_t>(m) * g.ldx : 0);
+    // a column tile's X: lane l holds X row 16 bg + l % 16, columns
+    // 512 j + 32 q + 8 (l / 16) .. + 7 for q = 0 .. 15 (zero past the batch
+    // or the matrix)
+    const uint16_t* xrow = job.x + (x_row ? static_cast<uint64_t>(xr) * g.ldx : 0);
     auto x_part = [&](uint32_t j, int q) __attribute__((always_inline)) {
       const uint64_t kc = static_cast<uint64_t>(j) * 512 + static_cast<uint32_t>(32 * q) + gq * 8u;
       const bool in_x = x_row && kc < b.cols;
@@ -1467,40 +1505,41 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
       return in_x ? v : make_uint4(0, 0, 0, 0);
     };
     uint4 xb[16];
-    if (c < n_tc) {
 #pragma unroll
-      for (int q = 0; q < 16; q++) xb[q] = x_part(c, q);
-    }
-    for (uint32_t grp = 0; ok && grp * C + c < n_tc; grp++) {
-      const uint32_t j = grp * C + c;
-      const uint32_t mc = n_tc - grp * C < C ? n_tc - grp * C : C;
+    for (int q = 0; q < 16; q++) xb[q] = x_part(cc, q);
+    for (uint32_t grp = 0; ok && grp * CG + cc < n_tc; grp++) {
+      const uint32_t j = grp * CG + cc;
+      const uint32_t mc = n_tc - grp * CG < CG ? n_tc - grp * CG : CG;
       // the next column tile's X replaces this one's part by part during the
       // group's last tile, so its loads overlap that tile's products and the
       // wait for the next group's first tile (no extra registers)
-      const uint32_t jn = j + C;
+      const uint32_t jn = j + CG;
       const bool x_next = jn < n_tc;
       for (uint32_t rb = 0; rb < n_rb; rb++) {
-        const uint32_t st = grp * C * n_rb + rb * mc + c;
+        const uint32_t st = grp * CG * n_rb + rb * mc + cc;
         const uint32_t k = st >> SL, i = st & (S - 1);
-        if (!flag_wait(flags + i, 2 * k + 1, failed)) {
+        // full for its k-th use: k use + 1 plus the reads so far (this
+        // consumer's own read comes before the slot can be refilled)
+        if (!flag_wait_ge(flags + i, k * use + 1, failed)) {
           ok = false;
           break;
         }
-        // chain: the row block's sums over columns 0 .. j-1 (the previous
-        // column's consumer has added its tile: columns are added in
-        // order); else this consumer's own sums over its earlier columns.
-        // Rows 4 gq .. + 3 for X row m; lanes of rows 8..15 hold zeros.
-        if (chain && !flag_wait(done + rb, j, failed)) {
+        // chain: the row block's sums (this batch group) over columns
+        // 0 .. j-1 (the previous column's consumer has added its tile:
+        // columns are added in order); else this consumer's own sums over
+        // its earlier columns.  Rows 4 gq .. + 3 for X row m; lanes of rows
+        // 8..15 hold zeros.
+        const uint32_t cnt = bg * n_rb + rb;
+        if (chain && !flag_wait(done + cnt, j, failed)) {
           ok = false;
           break;
         }
-        const uint32_t pp =
-            lds_addr(part) + (((chain ? rb : rb * C + c) * TR + gq * 4u) * B + m) * 4u;
+        const uint32_t pp = lds_addr(part) + (((chain ? cnt : rb * C + c) * TR + gq * 4u) * 16u + m) * 4u;
         const bool mine = gq < TR / 4 && x_row;
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
         if ((chain ? j : grp) > 0 && mine) {
 #pragma unroll
-          for (int e = 0; e < 4; e++) acc[e] = __builtin_bit_cast(float, lds_word(pp + e * B * 4u));
+          for (int e = 0; e < 4; e++) acc[e] = __builtin_bit_cast(float, lds_word(pp + e * 64u));
         }
         const uint32_t a_at = m < TR ? ring + i * kRingSlot + a_off : lds_addr(zero4);
         // two A operands read at a time (all sixteen at once would not fit
@@ -1521,18 +1560,19 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
           }
           asm volatile("" ::: "memory");
         }
-        // the slot's reads are done before it is released (release order)
-        flag_store(flags + i, 2 * k + 2);
+        // count this read (release: the slot's reads are done first); the
+        // last batch group's read frees the slot for its next use
+        if (flag_add(flags + i, 1u) == k * use + NG) flag_add(flags + i, 1u);
         if (mine) {
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             // a copy first: __builtin_bit_cast of a vector element reads element 0
             const float v = acc[e];
-            lds_put(pp + e * B * 4u, __builtin_bit_cast(uint32_t, v));
+            lds_put(pp + e * 64u, __builtin_bit_cast(uint32_t, v));
           }
         }
         // the sums now cover column j (release: after the stores above)
-        if (chain) flag_store(done + rb, j + 1);
+        if (chain) flag_store(done + cnt, j + 1);
       }
     }
   }
@@ -1541,13 +1581,16 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
   const bool bad = flag_load(failed) != 0;
   for (uint32_t kk = threadIdx.x; kk < n_rb * TR * B; kk += blockDim.x) {
     const uint32_t rb = kk / (TR * B), rr = (kk / B) % TR, beta = kk % B;
+    const uint32_t bg = beta / 16u, m = beta % 16u;
     const uint64_t row = (rb_a + rb) * TR + rr;
     if (row >= b.rows) continue;
-    float sum = part[kk];
-    if (!chain) {
-      // the consumers' sums, in consumer order
+    float sum;
+    if (chain) {
+      sum = part[((bg * n_rb + rb) * TR + rr) * 16u + m];
+    } else {
+      // the batch group's consumers' sums, in consumer order
       sum = 0.0f;
-      for (uint32_t c = 0; c < Ce; c++) sum += part[((rb * C + c) * TR + rr) * B + beta];
+      for (uint32_t cc = 0; cc < CGe; cc++) sum += part[((rb * C + bg * CG + cc) * TR + rr) * 16u + m];
     }
     store_y(job.y, beta * g.ldy + row, bad ? __builtin_nanf("") : sum, g.y_f32);
   }
@@ -2073,12 +2116,16 @@ nwc_status launch_skinny_mc(const Launch& L, const uint16_t* X, void* Y, int y_f
   struct Cfg {
     uint32_t P, C, S;
   };
-  const Cfg cfgs[] = {{12, 4, 3}, {12, 4, 2}, {10, 4, 2}, {8, 4, 2}};  // S: log2 of the ring slots
+  // batch groups of 16 X rows; four matrix-core wavefronts (two per group
+  // for two groups), the rest of 16 decode
+  const uint32_t NG = static_cast<uint32_t>(batch + 15) / 16;
+  const uint32_t C = NG == 3 ? 3 : 4;
+  const Cfg cfgs[] = {{16 - C, C, 3}, {16 - C, C, 2}, {14 - C, C, 2}, {12 - C, C, 2}};  // S: log2 of the ring slots
   auto need = [&](const Cfg& c, uint64_t rb, bool chain) {
     const uint64_t tw = (rb * n_tc + 1 + 3) & ~3ull;  // tile offsets; the hand-out order takes as many
     const uint32_t slots = 1u << c.S;
     return c.P * per_wave + static_cast<size_t>(slots) * kRingSlot + 16 + ((2 + slots + 3) & ~3u) * 4 +
-           2 * tw * 4 + ((rb + 3) & ~3ull) * 4 + static_cast<size_t>(rb) * (chain ? 1 : c.C) * 8 * batch * 4;
+           2 * tw * 4 + ((NG * rb + 3) & ~3ull) * 4 + static_cast<size_t>(rb) * (chain ? NG : c.C) * 8 * 16 * 4;
   };
   // per chaining choice: the candidate with the fewest rounds (first on ties)
   int best[2] = {-1, -1};
@@ -2129,17 +2176,21 @@ nwc_status launch_skinny_mc(const Launch& L, const uint16_t* X, void* Y, int y_f
   g.producers = c.P;
   g.consumers = c.C;
   g.ring_log2 = c.S;
-  g.rb_words = static_cast<uint32_t>((best_rb[ch] + 3) & ~3ull);
+  g.rb_words = static_cast<uint32_t>((NG * best_rb[ch] + 3) & ~3ull);
   g.chain = static_cast<uint32_t>(ch);
+  g.batch_groups = NG;
   return launch(k_skinny_mc<FIT2, QUAD>, dim3(static_cast<uint32_t>(best_g[ch])), dim3((c.P + c.C) * kWave), lds, s,
                 g);
 }
 
-// Whether a blob and batch take the skinny mode of the fused kernel (no
-// workspace): default chunk geometry, 8- or 16-row tiles, and one row
-// block's tile sums within kSkinnyLds.
+// Whether a blob and batch take a no-workspace skinny kernel: default chunk
+// geometry and 8- or 16-row tiles; the fused kernel's skinny mode (batch
+// 2..16) needs one row block's tile sums within kSkinnyLds, the matrix-core
+// kernel (8-row tiles, batch kMcMinBatch..kMaxSkinnyBatch) keeps its sums
+// per row block.
 bool skinny_fits(const nwc::Geometry& g, int batch) {
   const bool fast = g.s == 64 && g.v == 8 && (g.tr == 8 || g.tr == 16) && g.cols % 8 == 0;
+  if (fast && g.tr == 8 && batch >= kMcMinBatch && batch <= kMaxSkinnyBatch) return true;
   return fast && batch >= 2 && batch <= 16 &&
          static_cast<uint64_t>(g.n_tc) * g.tr * skinny_sums_per_row(static_cast<int>(g.tr), batch) * 4 <= kSkinnyLds;
 }
@@ -2181,7 +2232,8 @@ nwc_status nwc_inspect(const void* blob, size_t bytes, nwc_info* info) { return 
 
 nwc_status nwc_workspace_size(const nwc_info* info, int batch, size_t* bytes) {
   nwc::Geometry g;
-  if (!info || !bytes || batch < 1 || batch > 16 || !nwc::info_geometry(info, &g)) return NWC_ERR_INVALID_ARG;
+  if (!info || !bytes || batch < 1 || batch > kMaxSkinnyBatch || !nwc::info_geometry(info, &g))
+    return NWC_ERR_INVALID_ARG;
   const bool fast = g.s == 64 && g.v == 8 && (g.tr == 4 || g.tr == 8 || g.tr == 16 || g.tr == 32) && g.cols % 8 == 0;
   if (fast && batch == 1)
     *bytes = fused_ws_bytes(g);
@@ -2426,7 +2478,7 @@ nwc_status nwc_decode_batched(int count, const nwc_info* infos, const void* cons
 
 nwc_status nwc_gemm_skinny(const nwc_info* info, const void* blob_dev, const uint16_t* X_dev, uint64_t ldx, int batch,
                            void* Y_dev, uint64_t ldy, nwc_out_type y_type, void* ws, size_t ws_bytes, void* stream) {
-  if (batch < 2 || batch > 16) return NWC_ERR_INVALID_ARG;
+  if (batch < 2 || batch > kMaxSkinnyBatch) return NWC_ERR_INVALID_ARG;
   return gemm_common(info, blob_dev, X_dev, ldx, batch, Y_dev, ldy, y_type, ws, ws_bytes, stream);
 }
 

@@ -8,7 +8,8 @@ idea over this library's entry points.  ``forward`` picks the path by the
 number of input rows:
 
 * 1 row: ``nwc_gemv`` (fused decode-GEMV),
-* 2..16 rows: ``nwc_gemm_skinny`` (fused skinny decode-GEMM),
+* 2..16 rows (up to 32 with 8-row tiles): ``nwc_gemm_skinny`` (fused skinny
+  decode-GEMM, from 5 rows on the matrix cores),
 * more: ``nwc_gemm_prefill`` (decode into a scratch buffer + hipBLASLt GEMM).
 
 All arithmetic runs in the library's kernels (and hipBLASLt for prefill);
@@ -27,7 +28,8 @@ import torch
 from . import (Blas, nwc_decode, nwc_encode, nwc_gemm_prefill, nwc_gemm_skinny, nwc_gemv, nwc_inspect,
                nwc_prefill_workspace_size, nwc_workspace_size)
 
-SKINNY_MAX = 16
+SKINNY_MAX = 16      # any tile height
+SKINNY_MAX_MC = 32   # 8-row tiles (the matrix-core skinny GEMM)
 
 
 class NWCLinear(torch.nn.Module):
@@ -83,7 +85,7 @@ class NWCLinear(torch.nn.Module):
             y = torch.empty(self.out_features, dtype=torch.bfloat16, device=x.device)
             nwc_gemv(self.info, self.blob, Xb[0], y, self._ws1)
             Y = y.view(1, -1)
-        elif B <= SKINNY_MAX:
+        elif B <= (SKINNY_MAX_MC if self.info.tile_rows == 8 else SKINNY_MAX):
             Y = torch.empty((B, self.out_features), dtype=torch.bfloat16, device=x.device)
             nwc_gemm_skinny(self.info, self.blob, Xb, Y, self._workspace(B))
         else:

@@ -161,14 +161,15 @@ nwc_status nwc_decode(const nwc_info *info, const void *blob_dev, uint16_t *w_de
                       uint64_t ld, void *stream);
 
 /* Workspace bytes needed by nwc_gemv (batch = 1) or nwc_gemm_skinny
- * (batch 2..16) for this blob.
+ * (batch 2..32) for this blob.
  *  - Fused batch-1 path (default geometry, cols % 8 == 0): one 64-bit slot
  *    per (tile, row), rounded up to 256 bytes.  The kernel splits the tiles
  *    evenly over the GPU, so a row block can be shared by several
  *    workgroups; their partial sums meet in these slots.  The workspace
  *    must be zero-filled before its first use; every call leaves it
  *    zero-filled.
- *  - Fused skinny path (tile_rows 8 or 16, batch 2..16): 0 (ws may be NULL).
+ *  - Fused skinny path (tile_rows 8 or 16 and batch 2..16, or tile_rows 8
+ *    and batch 5..32): 0 (ws may be NULL).
  *  - Otherwise FP32 partial sums, one per (column tile, batch row, output
  *    row), for the generic path (any geometry), which runs a second reduction
  *    kernel; contents need not be initialised. */
@@ -263,7 +264,7 @@ nwc_status nwc_decode_batched(int count, const nwc_info *infos, const void *cons
 nwc_status nwc_gather_rows(const nwc_info *info, const void *blob_dev, const uint32_t *ids_dev,
                            uint32_t n_ids, uint16_t *out_dev, uint64_t ld, void *stream);
 
-/* Skinny decode-GEMM for batch 2..16 ("Unweight ...", Direct GPU
+/* Skinny decode-GEMM for batch 2..32 ("Unweight ...", Direct GPU
  * Decompression: weights decompressed in on-chip memory feed the matrix
  * units directly, with a strategy per batch size; "NWC -- Neural Weight
  * Compression", Status and limitations: batch 1 is the fast path there and a
@@ -272,9 +273,10 @@ nwc_status nwc_gather_rows(const nwc_info *info, const void *blob_dev, const uin
  * ldx) and Y (device, batch x rows, row stride ldy, y_type).  Same decode as
  * nwc_gemv; FP32 accumulation.  From 5 batch rows on (8-row tiles) the
  * products run on the matrix cores, fed by wavefronts that only decode
- * (decoded tiles pass through LDS, never through HBM).  Repeated calls give
- * the same bits.  Async.
- * Errors: INVALID_ARG (batch outside 2..16), BUFFER_TOO_SMALL, ALIGNMENT, HIP. */
+ * (decoded tiles pass through LDS, never through HBM), 16 X rows per matrix
+ * core pass, up to two passes; other tile heights take more than 16 rows on
+ * the generic path (workspace).  Repeated calls give the same bits.  Async.
+ * Errors: INVALID_ARG (batch outside 2..32), BUFFER_TOO_SMALL, ALIGNMENT, HIP. */
 nwc_status nwc_gemm_skinny(const nwc_info *info, const void *blob_dev, const uint16_t *X_dev,
                            uint64_t ldx, int batch, void *Y_dev, uint64_t ldy,
                            nwc_out_type y_type, void *ws, size_t ws_bytes, void *stream);

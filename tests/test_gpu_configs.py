@@ -235,18 +235,19 @@ def test_skinny_decode_bit_exact(name):
 
 
 @functools.lru_cache(maxsize=None)
+@functools.lru_cache(maxsize=None)
 def _skinny_ref(name):
     # the batch rows of every batch size are the first rows of the same draw
-    X = workloads.activations(4, name, batch=16)
+    X = workloads.activations(4, name, batch=32)
     return X, _oracle_gemm(_w(4, name), X)
 
 
-@pytest.mark.parametrize("batch", [2, 3, 4, 8, 9, 12, 16])
+@pytest.mark.parametrize("batch", [2, 3, 4, 8, 9, 12, 16, 32])
 @pytest.mark.parametrize("name", ["w_4096x14336", "w_14336x4096"])
 def test_skinny_gemm_all_rows(name, batch):
     info, b = _dev_blob(4, name)
-    X16, (Y16, A16) = _skinny_ref(name)
-    X = X16[:batch]
+    X32, (Y16, A16) = _skinny_ref(name)
+    X = X32[:batch]
     assert np.array_equal(X, workloads.activations(4, name, batch=batch))
     ws = torch.zeros(max(1, nwc.nwc_workspace_size(info, batch)), dtype=torch.uint8, device="cuda")
     for out_f32 in (False, True):

@@ -323,9 +323,10 @@ def test_gemm_small(name, params, batch):
 
 
 @pytest.mark.parametrize("rows,cols", [(1003, 4104), (37, 2056), (3000, 512), (4096, 1536), (30000, 1024)])
-@pytest.mark.parametrize("batch", [5, 10, 16])
+@pytest.mark.parametrize("batch", [5, 10, 16, 17, 24, 32])
 def test_gemm_matrix_core_shapes(rows, cols, batch):
-    # the matrix-core skinny GEMM (8-row tiles, batch >= 5) on shapes whose
+    # the matrix-core skinny GEMM (8-row tiles, batch 5..32: one or two
+    # groups of 16 X rows, the second partial at 17 and 24) on shapes whose
     # ranges cut the column groups unevenly: a last column tile of 8 columns
     # (4104), fewer column tiles than matrix-core wavefronts (512, 1536), a
     # last row block of 3 or 5 rows, and ranges of 15 row blocks whose sums

@@ -183,7 +183,8 @@ def test_workspace_sizes():
     info = nwc.nwc_inspect(blob)
     assert nwc.nwc_workspace_size(info, 1) == 3 * 100 * 4
     assert nwc.nwc_workspace_size(info, 16) == 3 * 16 * 100 * 4
-    for bad in (0, 17):
+    assert nwc.nwc_workspace_size(info, 32) == 3 * 32 * 100 * 4
+    for bad in (0, 33):
         with pytest.raises(nwc.NwcError):
             nwc.nwc_workspace_size(info, bad)
     # fused batch 1: one 64-bit chain slot per (tile, row), rounded up to 256
@@ -195,6 +196,10 @@ def test_workspace_sizes():
     assert nwc.nwc_workspace_size(tr16, 1) == up(7 * 3 * 16 * 8)
     assert nwc.nwc_workspace_size(tr16, 8) == 0
     assert nwc.nwc_workspace_size(fast, 8) == 0
+    # up to 32 X rows: 8-row tiles on the matrix cores (no workspace), other
+    # tile heights past 16 rows on the generic path
+    assert nwc.nwc_workspace_size(fast, 32) == 0
+    assert nwc.nwc_workspace_size(tr16, 17) == 3 * 17 * 100 * 4
     assert nwc.gemv_batched_workspace_size([fast, tr16]) == (nwc.nwc_workspace_size(fast, 1) +
                                                              nwc.nwc_workspace_size(tr16, 1))
     # batch > 1 with tile_rows 32 takes the generic path
@@ -229,7 +234,7 @@ def test_device_calls_validate_before_launch():
     assert L.nwc_gemv(ref, A, A, A, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
     assert L.nwc_gemv(ref, A, A, A, 0, A, W - 4, None) == nwc.NWC_ERR_BUFFER_TOO_SMALL
     assert L.nwc_gemv(ref, A, A, A, 0, A + 16, W, None) == nwc.NWC_ERR_ALIGNMENT
-    for batch in (0, 1, 17):
+    for batch in (0, 1, 33):
         assert L.nwc_gemm_skinny(ref, A, A, 512, batch, A, 64, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
     assert L.nwc_gemm_skinny(ref, A, A, 100, 4, A, 64, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
     assert L.nwc_gemm_skinny(ref, A, A, 512, 4, A, 63, 0, None, 0, None) == nwc.NWC_ERR_INVALID_ARG
