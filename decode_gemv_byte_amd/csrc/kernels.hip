@@ -321,7 +321,9 @@ __device__ __forceinline__ void decode_quad(R& rd, const uint32_t* tab, uint32_t
   const uint32_t win = rd.window();
   e1 = tab[(win & 0x3FFCu) >> 2];
   e2 = tab[((win >> e1) & 0x3FFCu) >> 2];
-  uint32_t adv = (e1 & 0x1Fu) + (e2 & 0x1Fu);
+  // both total lengths at once: they sit in bits 0..4 of each entry over two
+  // zero bits, so the low bits of the sum are their sum (at most 48)
+  uint32_t adv = (e1 + e2) & 0x3Fu;
   if constexpr (!FIT2) {
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(e1 | e2) < 0) != 0, 0)) {
       // some lane's entry holds one code: complete each pair with a second
@@ -329,7 +331,7 @@ __device__ __forceinline__ void decode_quad(R& rd, const uint32_t* tab, uint32_t
       e1 = complete_pair(e1, win, tab);
       const uint32_t w2 = rd.window_after(e1 & 0x1Fu);
       e2 = complete_pair(tab[(w2 & 0x3FFCu) >> 2], w2, tab);
-      adv = (e1 & 0x1Fu) + (e2 & 0x1Fu);
+      adv = (e1 + e2) & 0x3Fu;
     }
   }
   rd.advance(adv);
