@@ -1269,9 +1269,9 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
 // batch group taking column (group CG + c').  So each column tile's X is
 // loaded once per workgroup and batch group, every tile is read once per
 // batch group, and the decoding never waits for X.
-// A slot's flag counts its uses and reads: k (G + 2) means free for its k-th
-// tile, k (G + 2) + 1 full, then one more per batch group's read, and the
-// last read adds one more, which makes it free for the next use (G batch
+// A slot's flag counts its uses and reads: k (G + 1) means free for its k-th
+// tile, k (G + 1) + 1 full, then one more per batch group's read, so after
+// the last read it is (k + 1) (G + 1), free for the next use (G batch
 // groups).  Tile s uses slot s mod S for the (s / S)-th time; a decoding
 // wavefront writes it once tile s - S has been read by every batch group,
 // and consumers read their tiles in increasing order, so the lowest
@@ -1332,11 +1332,9 @@ __device__ __forceinline__ bool flag_wait_ge(uint32_t* f, uint32_t want, uint32_
   }
 }
 // Add v to *f (one lane, release after this wavefront's earlier LDS
-// accesses); returns the value before, the same in every lane.
-__device__ __forceinline__ uint32_t flag_add(uint32_t* f, uint32_t v) {
-  uint32_t old = 0;
-  if (lane_id() == 0) old = __hip_atomic_fetch_add(f, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-  return uniform(old);
+// accesses; the old value is not needed, so nothing waits for it).
+__device__ __forceinline__ void flag_add(uint32_t* f, uint32_t v) {
+  if (lane_id() == 0) (void)__hip_atomic_fetch_add(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 template <bool FIT2, bool QUAD>
@@ -1374,9 +1372,10 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
   // group c / CG and the columns c % CG, c % CG + CG, ...; every tile is read
   // by one consumer of each batch group
   const uint32_t NG = g.batch_groups, CG = C / NG;
+  const uint32_t BW = NG == 1 ? B : 16u;  // X rows per batch group as the sums store them
   const uint32_t CGe = CG < n_tc ? CG : n_tc;  // consumers of a batch group with a column
   const bool chain = g.chain != 0;
-  const uint32_t use = NG + 2;  // flag values per use of a slot: free, full, one per read
+  const uint32_t use = NG + 1;  // flag values per use of a slot: full, then one per read
   // tile s of the hand-out order -> (row block, column) in the range
   auto tile_of = [&](uint32_t s, uint32_t& rb, uint32_t& j) __attribute__((always_inline)) {
     const uint32_t grp = s / (CG * n_rb);
@@ -1536,12 +1535,12 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
           ok = false;
           break;
         }
-        const uint32_t pp = lds_addr(part) + (((chain ? cnt : rb * C + c) * TR + gq * 4u) * 16u + m) * 4u;
+        const uint32_t pp = lds_addr(part) + (((chain ? cnt : rb * C + c) * TR + gq * 4u) * BW + m) * 4u;
         const bool mine = gq < TR / 4 && x_row;
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
         if ((chain ? j : grp) > 0 && mine) {
 #pragma unroll
-          for (int e = 0; e < 4; e++) acc[e] = __builtin_bit_cast(float, lds_word(pp + e * 64u));
+          for (int e = 0; e < 4; e++) acc[e] = __builtin_bit_cast(float, lds_word(pp + e * BW * 4u));
         }
         const uint32_t a_at = m < TR ? ring + i * kRingSlot + a_off : lds_addr(zero4);
         // two A operands read at a time (all sixteen at once would not fit
@@ -1562,15 +1561,16 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
           }
           asm volatile("" ::: "memory");
         }
-        // count this read (release: the slot's reads are done first); the
-        // last batch group's read frees the slot for its next use
-        if (flag_add(flags + i, 1u) == k * use + NG) flag_add(flags + i, 1u);
+        // count this read (release: the slot's reads are done first); after
+        // the last batch group's read the count is (k + 1) use: free for the
+        // slot's next use
+        flag_add(flags + i, 1u);
         if (mine) {
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             // a copy first: __builtin_bit_cast of a vector element reads element 0
             const float v = acc[e];
-            lds_put(pp + e * 64u, __builtin_bit_cast(uint32_t, v));
+            lds_put(pp + e * BW * 4u, __builtin_bit_cast(uint32_t, v));
           }
         }
         // the sums now cover column j (release: after the stores above)
@@ -1588,11 +1588,11 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
     if (row >= b.rows) continue;
     float sum;
     if (chain) {
-      sum = part[((bg * n_rb + rb) * TR + rr) * 16u + m];
+      sum = part[((bg * n_rb + rb) * TR + rr) * BW + m];
     } else {
       // the batch group's consumers' sums, in consumer order
       sum = 0.0f;
-      for (uint32_t cc = 0; cc < CGe; cc++) sum += part[((rb * C + bg * CG + cc) * TR + rr) * 16u + m];
+      for (uint32_t cc = 0; cc < CGe; cc++) sum += part[((rb * C + bg * CG + cc) * TR + rr) * BW + m];
     }
     store_y(job.y, beta * g.ldy + row, bad ? __builtin_nanf("") : sum, g.y_f32);
   }
@@ -2127,7 +2127,8 @@ nwc_status launch_skinny_mc(const Launch& L, const uint16_t* X, void* Y, int y_f
     const uint64_t tw = (rb * n_tc + 1 + 3) & ~3ull;  // tile offsets; the hand-out order takes as many
     const uint32_t slots = 1u << c.S;
     return c.P * per_wave + static_cast<size_t>(slots) * kRingSlot + 16 + ((2 + slots + 3) & ~3u) * 4 +
-           2 * tw * 4 + ((NG * rb + 3) & ~3ull) * 4 + static_cast<size_t>(rb) * (chain ? NG : c.C) * 8 * 16 * 4;
+           2 * tw * 4 + ((NG * rb + 3) & ~3ull) * 4 +
+           static_cast<size_t>(rb) * (chain ? NG : c.C) * 8 * (NG == 1 ? batch : 16) * 4;
   };
   // per chaining choice: the candidate with the fewest rounds (first on ties)
   int best[2] = {-1, -1};
