@@ -104,10 +104,12 @@ _lib.nwc_gemm_prefill.argtypes = [_vp, ctypes.POINTER(nwc_info), _vp, _vp, _u64,
 _lib.nwc_read_probe.argtypes = [_vp, _sz, _vp, _u32, _i, _vp]
 _lib.nwc_noalloc_scratch_bytes.argtypes = [ctypes.POINTER(_sz)]
 _lib.nwc_gemv_noalloc.argtypes = [ctypes.POINTER(nwc_info), _vp, _vp, _vp, _i, _vp]
+_lib.nwc_set_wait_limit.argtypes = [_u32]
 for _f in ("nwc_encode_bound", "nwc_encode", "nwc_inspect", "nwc_decode", "nwc_workspace_size", "nwc_gemv",
            "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16", "nwc_gemv_batched", "nwc_decode_batched",
            "nwc_blas_create", "nwc_blas_destroy", "nwc_prefill_workspace_size", "nwc_gemm_prefill",
-           "nwc_gather_rows", "nwc_read_probe", "nwc_noalloc_scratch_bytes", "nwc_gemv_noalloc"):
+           "nwc_gather_rows", "nwc_read_probe", "nwc_noalloc_scratch_bytes", "nwc_gemv_noalloc",
+           "nwc_set_wait_limit"):
     getattr(_lib, _f).restype = _st
 
 # the exported C symbols, for checks against include/nwc.h
@@ -115,7 +117,7 @@ EXPORTS = ("nwc_status_str", "nwc_encode_bound", "nwc_encode", "nwc_inspect", "n
            "nwc_workspace_size", "nwc_gemv", "nwc_gemm_skinny", "nwc_bf16_workspace_size", "nwc_gemv_bf16",
            "nwc_gemv_batched", "nwc_decode_batched", "nwc_blas_create", "nwc_blas_destroy",
            "nwc_prefill_workspace_size", "nwc_gemm_prefill", "nwc_gather_rows", "nwc_read_probe",
-           "nwc_noalloc_scratch_bytes", "nwc_gemv_noalloc")
+           "nwc_noalloc_scratch_bytes", "nwc_gemv_noalloc", "nwc_set_wait_limit")
 
 
 def _check(st: int, where: str):
@@ -267,6 +269,11 @@ def nwc_noalloc_scratch_bytes() -> int:
     out = _sz(0)
     _check(_lib.nwc_noalloc_scratch_bytes(ctypes.byref(out)), "nwc_noalloc_scratch_bytes")
     return out.value
+
+
+def nwc_set_wait_limit(polls: int = 0):
+    """Polls after which the matrix-core skinny GEMM's waits give up (its outputs then NaN); 0 = default."""
+    _check(_lib.nwc_set_wait_limit(int(polls)), "nwc_set_wait_limit")
 
 
 def nwc_gemv_noalloc(info: nwc_info, blob_dev, x_dev, y_dev, stream=None):

@@ -56,6 +56,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -613,6 +614,7 @@ struct GemvGroup {
   // the columns of a row block are added along one chain (else each
   // consumer keeps its own sums)
   uint32_t producers, consumers, ring_log2, rb_words, chain, batch_groups;
+  uint32_t wait_limit;  // polls of a flag before a wait gives up
 };
 
 // Registers of one tile for the batch-1 kernel: raw bytes of this lane's
@@ -1300,6 +1302,8 @@ constexpr int kMcMinBatch = 5;  // batch sizes from which the skinny GEMM takes 
 // walking every column and reloading X for each) 167 against 146 us.
 constexpr int kMaxSkinnyBatch = 32;
 constexpr uint32_t kSpinLimit = 1u << 22;  // polls of a flag (with a short sleep each) before giving up
+// the bound used by launches (nwc_set_wait_limit; kSpinLimit unless a test lowers it)
+std::atomic<uint32_t> g_wait_limit{kSpinLimit};
 
 __device__ __forceinline__ uint32_t flag_load(uint32_t* f) {
   return uniform(__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
@@ -1307,12 +1311,12 @@ __device__ __forceinline__ uint32_t flag_load(uint32_t* f) {
 __device__ __forceinline__ void flag_store(uint32_t* f, uint32_t v) {
   if (lane_id() == 0) __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-// Wait until *f == want; false (and the workgroup marked failed) past the
-// poll limit or once another wavefront has failed.
-__device__ __forceinline__ bool flag_wait(uint32_t* f, uint32_t want, uint32_t* failed) {
+// Wait until *f == want; false (and the workgroup marked failed) past
+// `limit` polls or once another wavefront has failed.
+__device__ __forceinline__ bool flag_wait(uint32_t* f, uint32_t want, uint32_t* failed, uint32_t limit) {
   for (uint32_t i = 0;; i++) {
     if (flag_load(f) == want) return true;
-    if (i >= kSpinLimit || flag_load(failed) != 0) {
+    if (i >= limit || flag_load(failed) != 0) {
       flag_store(failed, 1u);
       return false;
     }
@@ -1321,10 +1325,10 @@ __device__ __forceinline__ bool flag_wait(uint32_t* f, uint32_t want, uint32_t* 
 }
 
 // Wait until *f >= want (same bound as flag_wait).
-__device__ __forceinline__ bool flag_wait_ge(uint32_t* f, uint32_t want, uint32_t* failed) {
+__device__ __forceinline__ bool flag_wait_ge(uint32_t* f, uint32_t want, uint32_t* failed, uint32_t limit) {
   for (uint32_t i = 0;; i++) {
     if (flag_load(f) >= want) return true;
-    if (i >= kSpinLimit || flag_load(failed) != 0) {
+    if (i >= limit || flag_load(failed) != 0) {
       flag_store(failed, 1u);
       return false;
     }
@@ -1473,7 +1477,7 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
       // hand the tile over: slot s mod S, free once tile s - S has been read
       // by every batch group
       const uint32_t k = s >> SL, i = s & (S - 1);
-      if (!flag_wait(flags + i, k * use, failed)) break;
+      if (!flag_wait(flags + i, k * use, failed, g.wait_limit)) break;
       const uint32_t at = ring + i * kRingSlot + lane * 16u;
 #pragma unroll
       for (int r = 0; r < TR; r++)
@@ -1521,7 +1525,7 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
         const uint32_t k = st >> SL, i = st & (S - 1);
         // full for its k-th use: k use + 1 plus the reads so far (this
         // consumer's own read comes before the slot can be refilled)
-        if (!flag_wait_ge(flags + i, k * use + 1, failed)) {
+        if (!flag_wait_ge(flags + i, k * use + 1, failed, g.wait_limit)) {
           ok = false;
           break;
         }
@@ -1531,7 +1535,7 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
         // its earlier columns.  Rows 4 gq .. + 3 for X row m; lanes of rows
         // 8..15 hold zeros.
         const uint32_t cnt = bg * n_rb + rb;
-        if (chain && !flag_wait(done + cnt, j, failed)) {
+        if (chain && !flag_wait(done + cnt, j, failed, g.wait_limit)) {
           ok = false;
           break;
         }
@@ -1577,6 +1581,8 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
         if (chain) flag_store(done + cnt, j + 1);
       }
     }
+    // a wavefront that gave up may still have X loads in flight
+    wait_vmem();
   }
   __syncthreads();
   // y: each row block's sums over all its columns
@@ -2182,6 +2188,7 @@ nwc_status launch_skinny_mc(const Launch& L, const uint16_t* X, void* Y, int y_f
   g.rb_words = static_cast<uint32_t>((NG * best_rb[ch] + 3) & ~3ull);
   g.chain = static_cast<uint32_t>(ch);
   g.batch_groups = NG;
+  g.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
   return launch(k_skinny_mc<FIT2, QUAD>, dim3(static_cast<uint32_t>(best_g[ch])), dim3((c.P + c.C) * kWave), lds, s,
                 g);
 }
@@ -2397,6 +2404,11 @@ nwc_status scratch_ptr(void** out) {
   return NWC_OK;
 }
 }  // namespace
+
+nwc_status nwc_set_wait_limit(uint32_t polls) {
+  g_wait_limit.store(polls ? polls : kSpinLimit, std::memory_order_relaxed);
+  return NWC_OK;
+}
 
 nwc_status nwc_noalloc_scratch_bytes(size_t* bytes) {
   if (!bytes) return NWC_ERR_INVALID_ARG;

@@ -342,6 +342,18 @@ nwc_status nwc_gemv_bf16(const uint16_t *w_dev, uint64_t rows, uint64_t cols, ui
 nwc_status nwc_read_probe(const void *buf_dev, size_t bytes, uint32_t *sink_dev, uint32_t groups,
                           int layout, void *stream);
 
+/* Test hook for the bounded waits of nwc_gemm_skinny's matrix-core kernel
+ * (batch >= 5, 8-row tiles), whose decoding and matrix-core wavefronts wait
+ * for each other through flags in LDS.  Every such wait gives up after
+ * `polls` polls (each with a short sleep); the workgroup then marks itself
+ * failed, stops, and writes NaN for its outputs, so a broken hand-over shows
+ * as NaN rather than as a hung GPU.  polls = 0 restores the default bound,
+ * 2^22 polls, far beyond any legitimate wait; a tiny bound lets a test drive
+ * the give-up path from the host.  Process-wide, read at each launch; not
+ * meant to be changed while calls are being made from other threads.
+ * Errors: none. */
+nwc_status nwc_set_wait_limit(uint32_t polls);
+
 #ifdef __cplusplus
 }
 #endif

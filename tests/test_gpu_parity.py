@@ -345,6 +345,27 @@ def test_gemm_matrix_core_shapes(rows, cols, batch):
         _check_y(Yd[beta], Y_ref[beta], A_ref[beta], True, "%dx%d b%d" % (rows, cols, beta))
 
 
+def test_gemm_matrix_core_wait_limit_gives_nan_not_a_hang():
+    # a one-poll bound makes the matrix-core wavefronts' first waits give up
+    # (the decoders take microseconds per tile): the kernel still ends, its
+    # outputs are NaN, and with the default bound restored the same call is
+    # correct again
+    w = workloads.gaussian_bits((4096, 1536), 0.02, 81)
+    X = workloads.gaussian_bits((16, 1536), 1.0, 82)
+    b = Blob(w)
+    _say("wait limit 1")
+    try:
+        nwc.nwc_set_wait_limit(1)
+        Y = _gemm(b, X, True)
+    finally:
+        nwc.nwc_set_wait_limit(0)
+    assert torch.isnan(Y).any()
+    Y_ref, A_ref = oracle.gemm(w, X)
+    Yd = _to_f64(_gemm(b, X, True))
+    for beta in range(16):
+        _check_y(Yd[beta], Y_ref[beta], A_ref[beta], True, "restored b%d" % beta)
+
+
 def test_gemm_deterministic():
     w = _w(4, "w_4096x14336")
     X = workloads.activations(4, "w_4096x14336", batch=16)
