@@ -25,9 +25,12 @@
 //      bits, one lookup in the 4096-entry table (static LDS) gives two
 //      exponents already at BF16 bit positions and their lengths; a byte
 //      permute and a bit-field insert build two BF16 weights in a dword,
-//      which v_dot2c_f32_bf16 multiplies into FP32 (subnormals kept).  A
-//      wave-uniform branch takes a second lookup when some lane's second code
-//      did not fit the window (never with codes of at most 6 bits).
+//      which v_dot2c_f32_bf16 multiplies into FP32 (subnormals kept).  With
+//      codes of at most 9 bits one window read serves two such lookups (the
+//      second at the window shifted by the first pair's length), four
+//      weights per step.  A wave-uniform branch takes extra lookups when
+//      some lane's pair did not fit 12 bits (never with codes of at most 6
+//      bits).
 //    - Work split: as many workgroups as the GPU holds at once (occupancy
 //      queried at launch), each owning an equal contiguous range of a
 //      matrix's tiles; within it, wavefronts claim tiles from an LDS counter
@@ -41,11 +44,12 @@
 //      decoded tile in registers.
 //    - Decode mode: each decoded tile is stored once the next tile's loads
 //      are in flight.
-//  * k_skinny_mc: the skinny decode-GEMM for 8-row tiles and 5..16 X rows on
-//    the matrix cores (v_mfma_f32_16x16x32_bf16), with two kinds of
-//    wavefront per workgroup: decoding wavefronts (the batch-1 pipeline) hand
-//    decoded tiles through a ring of LDS slots to matrix-core wavefronts that
-//    keep one column tile's X in registers.
+//  * k_skinny_mc: the skinny decode-GEMM for 8-row tiles and 5..32 X rows
+//    (one or two groups of 16) on the matrix cores
+//    (v_mfma_f32_16x16x32_bf16), with two kinds of wavefront per workgroup:
+//    decoding wavefronts (the batch-1 pipeline) hand decoded tiles through a
+//    ring of LDS slots to matrix-core wavefronts that keep one column tile's
+//    X for one group in registers.
 //  * k_decode_generic, k_gemv_generic (+ k_reduce), k_gather: any geometry,
 //    two codes per table lookup, one tile per wavefront; the generic GEMV
 //    writes FP32 partial sums per column tile that k_reduce adds in order.

@@ -166,8 +166,8 @@ def tune_geometry(w: Union[np.ndarray, Sequence[np.ndarray]], batch: int = 1, ca
     for m in mats:
         if m.dtype != np.uint16 or m.ndim != 2:
             raise ValueError("expected 2-D uint16 BF16 bit patterns")
-    if not 1 <= batch <= 16:
-        raise ValueError("batch must be 1..16 (the fused kernels' range)")
+    if not 1 <= batch <= 32:
+        raise ValueError("batch must be 1..32 (nwc_gemv_batched at 1, nwc_gemm_skinny above)")
     if batch == 1 and len(mats) > 8:
         raise ValueError("at most 8 matrices share one launch")
     device = torch.device(device or "cuda")

@@ -39,7 +39,7 @@ def test_tune_rejects_bad_inputs_before_touching_a_gpu():
     with pytest.raises(ValueError):
         tune.tune_geometry(w.astype(np.int32))
     with pytest.raises(ValueError):
-        tune.tune_geometry(w, batch=17)
+        tune.tune_geometry(w, batch=33)
     with pytest.raises(ValueError):
         tune.tune_geometry([w] * 9)
     with pytest.raises(ValueError):
