@@ -49,11 +49,34 @@ CHECK_ROWS = 256              # rows per matrix checked against an FP64 product
 PROBE_BYTES = 4 << 30         # read-probe buffer, 16x the Infinity Cache
 DEFAULT_PAIR_FIT = 1024       # the library's default 6-bit cap of common exponents (nwc_params.pair_fit)
 KERNEL_SRC = os.path.join(ROOT, "decode_gemv_byte_amd", "csrc", "kernels.hip")
+SETTLE_MS = 50.0              # GPU time of work run before each timed loop (clocks settle)
 
 
 def note(msg):
     """A progress line on stderr (the JSON result is the one stdout line)."""
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def settle(torch, stream, launch, ms=SETTLE_MS):
+    """Keep the GPU busy with launch(i) (one launch or one graph replay on
+    `stream`) for at least `ms` of GPU time, so that a timed loop starts at
+    settled clocks: on an MI355X that was idle, the first few milliseconds
+    of load run up to ~15% slower (gate+up of the Llama step: 42.9 us per
+    launch over its first ~9 ms of launches, 36.7-36.9 us afterwards, eager
+    or graph-replayed alike).  Returns the launches run."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n, done, batch = 0, 0.0, 4
+    while done < ms:
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(batch):
+                launch(n + i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        n += batch
+        done += e0.elapsed_time(e1)
+        batch = min(2 * batch, 1 << 14)
+    return n
 
 
 def traffic_file(workload_name, group):
@@ -233,6 +256,7 @@ def model_step(args):
             graph.replay()
         torch.cuda.synchronize()
         outs[dense] = x.float().cpu().clone()
+        settle(torch, stream, lambda i: graph.replay())
         for i in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
@@ -310,12 +334,13 @@ def read_probe(torch, nwc, stream, reps=20):
     buffer, 16x the Infinity Cache: the fastest of two layouts (grid-stride;
     one contiguous range per workgroup) at four launch sizes, each averaged
     over `reps` back-to-back launches timed with HIP events on the probe's
-    stream."""
+    stream, after the clocks have settled."""
     buf = torch.ones(PROBE_BYTES, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     best = None
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settle(torch, stream, lambda i: nwc.nwc_read_probe(buf, sink, cus * 8, 1, stream=stream))
     for layout in (0, 1):
         for per_cu in (2, 4, 8, 16):
             groups = cus * per_cu
@@ -502,9 +527,8 @@ def main():
 
     def time_dominant():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        settle(torch, stream, lambda i: launch_dominant(i % dcopies))
         with torch.cuda.stream(stream):
-            for i in range(10):
-                launch_dominant(i % dcopies)
             e0.record(stream)
             for i in range(reps):
                 launch_dominant(i % dcopies)
@@ -595,6 +619,7 @@ def main():
                     step(c)
 
     # --------------------------------------------------------------- timed
+    settle(torch, stream, lambda i: run(1, i))
     run(args.warmup, 0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -621,9 +646,8 @@ def main():
         iws = zeroed(nwc.gemv_batched_workspace_size([info[k] for k in keys]))
         allb = [nwc.GemvBatch([info[k] for k in keys], [blobs[c][k] for k in keys], [xs[k][0] for k in keys],
                               [ys[k] for k in keys], iws) for c in range(copies)]
+        settle(torch, stream, lambda i: nwc.nwc_gemv_batched(allb[i % copies], stream=stream))
         with torch.cuda.stream(stream):
-            for i in range(10):
-                nwc.nwc_gemv_batched(allb[i % copies], stream=stream)
             e0.record(stream)
             for i in range(reps):
                 nwc.nwc_gemv_batched(allb[i % copies], stream=stream)
@@ -657,9 +681,13 @@ def main():
                 step_decode(c)
             dgraphs.append(g)
         torch.cuda.synchronize()
-        for i in range(args.warmup):
+
+        def decode_once(i):
             with torch.cuda.stream(stream):
                 dgraphs[i % copies].replay() if dgraphs else step_decode(i % copies)
+        settle(torch, stream, decode_once)
+        for i in range(args.warmup):
+            decode_once(i)
         torch.cuda.synchronize()
         e0.record(stream)
         for i in range(args.steps):
@@ -686,9 +714,8 @@ def main():
             ids = torch.from_numpy(g_rng.integers(0, info[k].rows, n_ids).astype(np.int32)).to(dev)
             gout = torch.empty((n_ids, info[k].cols), dtype=torch.int16, device=dev)
             ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            settle(torch, stream, lambda i: nwc.nwc_gather_rows(info[k], blobs[i % copies][k], ids, gout, stream=stream))
             with torch.cuda.stream(stream):
-                for i in range(5):
-                    nwc.nwc_gather_rows(info[k], blobs[i % copies][k], ids, gout, stream=stream)
                 ge0.record(stream)
                 for i in range(50):
                     nwc.nwc_gather_rows(info[k], blobs[i % copies][k], ids, gout, stream=stream)
@@ -697,9 +724,8 @@ def main():
             entry = {"us": round(ge0.elapsed_time(ge1) * 1e3 / 50, 3)}
             if want_bf16:
                 ids64 = ids.long()
+                settle(torch, stream, lambda i: torch.index_select(wbf[k], 0, ids64))
                 with torch.cuda.stream(stream):
-                    for i in range(5):
-                        torch.index_select(wbf[k], 0, ids64)
                     ge0.record(stream)
                     for i in range(50):
                         torch.index_select(wbf[k], 0, ids64)
@@ -729,6 +755,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": SETTLE_MS,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -788,6 +815,7 @@ def bf16_comparators(torch, nwc, args, keys, info, wbf, xs, ys, batch, bytes_u, 
         return out
 
     def rep_timed(gr):
+        settle(torch, stream, lambda i: gr[i % bcopies].replay())
         for i in range(args.warmup):
             with torch.cuda.stream(stream):
                 gr[i % bcopies].replay()
@@ -830,12 +858,15 @@ def bf16_comparators(torch, nwc, args, keys, info, wbf, xs, ys, batch, bytes_u, 
         dw = [{k: (wbf[k] if c == 0 else wbf[k].clone()) for k in dom_keys} for c in range(dcopies)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = args.roofline_reps
+
+        def bf16_dom(i):
+            for k in dom_keys:
+                nwc.nwc_gemv_bf16(dw[i % dcopies][k], xs[k][0], yb[k], wsb[k], stream=stream)
+        settle(torch, stream, bf16_dom)
         with torch.cuda.stream(stream):
-            for i in range(10 + reps):
-                if i == 10:
-                    e0.record(stream)
-                for k in dom_keys:
-                    nwc.nwc_gemv_bf16(dw[i % dcopies][k], xs[k][0], yb[k], wsb[k], stream=stream)
+            e0.record(stream)
+            for i in range(reps):
+                bf16_dom(i)
             e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
