@@ -36,6 +36,7 @@ from . import (GemvBatch, NwcError, nwc_decode, nwc_encode, nwc_gemm_skinny, nwc
 DEFAULT_CANDIDATES: Tuple[Tuple[int, int], ...] = ((4, 8), (8, 8), (16, 8), (32, 8), (8, 9), (4, 6), (8, 6))
 STREAM_BYTES = 768 << 20   # device copies cycled per timing: well above the last-level cache
 MAX_COPIES = 32
+SETTLE_MS = 50.0           # GPU time a candidate runs before it is timed
 
 
 @dataclass
@@ -136,9 +137,21 @@ def _time_candidate(ws_bits, blobs_host, batch, reps, device):
         for c in range(copies):
             launch(c)
     rounds = max(1, -(-reps // copies))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # replays until the GPU has run this candidate for SETTLE_MS: a GPU left
+    # idle (here, while the host encoded the candidate) runs its first
+    # milliseconds of load slower, which would favour later candidates
+    settled, n = 0.0, 1
+    while settled < SETTLE_MS:
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(n):
+                graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize(device)
+        settled += e0.elapsed_time(e1)
+        n = min(2 * n, 1024)
     with torch.cuda.stream(stream):
-        graph.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(rounds):
             graph.replay()
