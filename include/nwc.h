@@ -44,7 +44,9 @@
  *  - Results are deterministic: a fixed summation order, no floating-point
  *    atomics, so repeated calls give bitwise-identical outputs.
  *  - Functions are reentrant; the library holds no mutable global state,
- *    except nwc_gemv_noalloc's per-device static scratch (see there).
+ *    except nwc_gemv_noalloc's per-device static scratch and the wait bound
+ *    of the matrix-core skinny GEMM that the test hook nwc_set_wait_limit
+ *    sets (see there).
  */
 #ifndef NWC_H
 #define NWC_H
