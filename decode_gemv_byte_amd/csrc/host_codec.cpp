@@ -544,7 +544,7 @@ nwc_status inspect(const void* blob_v, size_t bytes, nwc_info* info) {
 // Re-derive the geometry of an nwc_info (for the device entry points).
 bool info_geometry(const nwc_info* info, Geometry* g) {
   if (!info) return false;
-  nwc_params p{info->tile_rows, info->tile_cols, info->chunks_per_tile, info->max_code_len, 0};
+  nwc_params p{info->tile_rows, info->tile_cols, info->chunks_per_tile, info->max_code_len, 0, 0};
   if (!p.tile_rows || !p.tile_cols || !p.chunks_per_tile || !p.max_code_len) return false;
   if (!params_resolve(&p, g)) return false;
   if (info->rows < 1 || info->cols < 1) return false;
