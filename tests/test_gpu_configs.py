@@ -5,7 +5,7 @@ For each of the five workloads (seeded synthetic weights from ``workloads``):
 * every output row of the fused products matches the CPU oracle's FP64
   product within 2^-10 * sum|w x| (FP32 output; plus 2^-8 |y| for BF16
   output): batch 1 through the grouped launches of a decode step (q+k+v and
-  gate+up in one launch each, o and down alone), batches 2..16 through the
+  gate+up in one launch each, o and down alone), batches 2..32 through the
   skinny GEMM, the LM head at batch 1 and 8;
 * one-hot inputs make the FP32 output a column of W exactly (each product is
   w * 1 and every other term is a zero), so a single wrongly decoded weight
