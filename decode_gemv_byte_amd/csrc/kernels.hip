@@ -684,15 +684,22 @@ struct TileRegs {
   // the last valid row
   template <int R0, int R1>
   __device__ __forceinline__ void load_raw(const BlobDev& b, uint64_t ti, uint32_t tj) {
+    load_raw_to<R0, R1>(b, ti, tj, raw);
+  }
+  // the same rows of this tile (its nrows) into another tile's registers
+  template <int R0, int R1>
+  __device__ __forceinline__ void load_raw_to(const BlobDev& b, uint64_t ti, uint32_t tj, uint2 (&dst)[TR]) const {
     const uint32_t lane = lane_id();
     const uint64_t row0 = ti * TR;
     const uint64_t col0 = static_cast<uint64_t>(tj) * 512;
     const __amdgpu_buffer_rsrc_t rr =
         buf_rsrc(b.raw + row0 * b.raw_ld + col0, (b.rows - row0) * b.raw_ld - col0);
+    const uint32_t nr = uniform(nrows);  // a scalar offset per row, not a loop over lanes
 #pragma unroll
     for (int r = R0; r < R1; r++) {
-      const uint32_t rr_off = static_cast<uint32_t>((static_cast<uint32_t>(r) < nrows ? r : nrows - 1) * b.raw_ld);
-      raw[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rr, lane * 8, rr_off, 0));
+      const uint32_t rr_off =
+          uniform(static_cast<uint32_t>((static_cast<uint32_t>(r) < nr ? r : nr - 1) * b.raw_ld));
+      dst[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rr, lane * 8, rr_off, 0));
     }
   }
   // the tile's stream words [w0 & ~3, w1 + 2) in 16-byte pieces, behind 4 zero
@@ -935,6 +942,9 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   static_assert(!QUAD || NB != kRawBf16, "two pairs per window: decoding modes");
   constexpr bool DECODE = NB < 0;
   constexpr bool SKINNY = !RAW16 && (NB == 0 || NB > 1);
+  // batch 1: a tile's last rows [7/8 TR, TR) are loaded once this tile's
+  // own last rows are decoded, into the same registers
+  constexpr bool DEFER = NB == 1;
   constexpr int NX = NB > 0 && !RAW16 ? NB : 0;  // X rows that come with each tile
   constexpr int NA = NB > 0 && !RAW16 ? NB : 1;  // sums per row of a tile formed while decoding
   using Regs = std::conditional_t<RAW16, TileRegs16<TR>, TileRegs<TR, NX>>;
@@ -1096,9 +1106,16 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     // against half the tile: batch 1 on 9728 x 2560 pairs 5% faster, the
     // skinny modes 1-5% and the standalone decode 2%, nothing slower)
     constexpr int PRE = TR * 7 / 8;
-    // every raw row below PRE is in: all but the last TR - PRE of the second
-    // half's TR / 2 row loads (issued last, in row order)
-    wait_vmem_but<(TR - PRE < TR / 2 ? TR - PRE : TR / 2)>();
+    if constexpr (DEFER) {
+      // the stream and the chunk lengths are in; x and the TR raw rows
+      // (issued after them, in that order) are waited for where they are
+      // first used, so row 0 decodes while the later rows still land
+      wait_vmem_but<TR + 1>();
+    } else {
+      // every raw row below PRE is in: all but the last TR - PRE of the
+      // second half's TR / 2 row loads (issued last, in row order)
+      wait_vmem_but<(TR - PRE < TR / 2 ? TR - PRE : TR / 2)>();
+    }
     if constexpr (DECODE) store_prev();
     wave_sync_lds();
     // this tile's stream into the slot; the linear buffer is then free for
@@ -1131,6 +1148,52 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     else
       wait_vmem();
     asm volatile("" ::: "memory");
+    if constexpr (DEFER) {
+      const uint64_t tn = claims ? claim() : r1;
+      // this tile's rows [PRE, TR), then its row sums into LDS
+      auto finish = [&]() __attribute__((always_inline)) {
+        if (in.active) gemv_rows<TR, NX, PRE, TR, FIT2, QUAD>(in, br, tab, acc);
+      };
+      auto sums = [&]() __attribute__((always_inline)) {
+        const float sv = reduce_rows<TR>(acc);
+        constexpr uint32_t lanes_per_sum = kWave / TR;
+        if ((lane & (lanes_per_sum - 1)) == 0) gsum[(t - r0) * TR + lane / lanes_per_sum] = sv;
+      };
+      // the range's last tile for this wavefront: no loads follow (on the
+      // path back to the loop head every tile issues the same loads in the
+      // same order, so the compiler's waits count them exactly)
+      if (tn >= r1) {
+        finish();
+        sums();
+        break;
+      }
+      const uint64_t ni = tn / n_tc;
+      const uint32_t nj = static_cast<uint32_t>(tn - ni * n_tc);
+      uint32_t w0, w1;
+      words(tn, w0, w1);
+      // the next tile's stream, chunk lengths, x and rows [0, PRE), the
+      // rows into the registers of this tile's rows already decoded
+      Regs nx;
+      nx.load_stream(b, w0, w1, buf);
+      nx.load_meta(b, job.x, g.ldx, g.batch, ni, nj);
+      nx.template load_raw_to<0, PRE>(b, ni, nj, in.raw);
+      finish();
+      // the next tile's rows [PRE, TR) into the registers just freed: loaded
+      // in place, so no register copy at the end of the tile waits for them
+      // (the next tile reads them last)
+      nx.template load_raw_to<PRE, TR>(b, ni, nj, in.raw);
+      sums();
+      in.x[0] = nx.x[0];
+      in.cbw = nx.cbw;
+      in.w0 = nx.w0;
+      in.a0 = nx.a0;
+      in.nrows = nx.nrows;
+      in.col = nx.col;
+      in.rowblk = nx.rowblk;
+      in.active = nx.active;
+      t = tn;
+      continue;
+    }
     Regs nx;
     const uint64_t tn = claims ? claim() : r1;
     if (tn < r1) {
