@@ -596,7 +596,21 @@ struct GemvJob {
   uint32_t groups;      // workgroups of this matrix
   uint32_t whole_rows;  // 1: each range is whole row blocks; 0: equal ranges
   uint64_t ld;          // decode mode: row stride of W' in elements
+  // k_gemv's ranges and tile coordinates without a run-time division: the
+  // range unit count N (tiles, or row blocks for whole_rows) = rq groups +
+  // rrem, and reciprocals ceil(2^48 / d) of groups and of n_tc, each split
+  // into its high and low 32 bits (div_magic)
+  uint32_t rq, rrem, gm_hi, gm_lo, cm_hi, cm_lo;
 };
+// floor(n / d) for n < 2^32 and 1 <= d < 2^16 from m = ceil(2^48 / d) =
+// hi 2^32 + lo: n m / 2^48 exceeds n / d by less than 2^-16 < 1 / d, too
+// little to reach the next integer, so the floor is exact.  Uniform values:
+// a few scalar instructions where a 64-bit division takes dozens.
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t hi, uint32_t lo) {
+  const uint64_t t = static_cast<uint64_t>(n) * hi + __umulhi(n, lo);
+  return static_cast<uint32_t>(t >> 16);
+}
+
 // a chain slot holds a partial sum's FP32 bits with this flag set
 constexpr uint64_t kSlotFull = 1ull << 32;
 constexpr int kMaxJobs = 8;
@@ -620,6 +634,20 @@ struct GemvGroup {
   uint32_t producers, consumers, ring_log2, rb_words, chain, batch_groups;
   uint32_t wait_limit;  // polls of a flag before a wait gives up
 };
+
+// Job j of a kernel's GemvGroup argument (its only argument, at the start of
+// the kernel-argument segment), read through the constant address space so
+// that a run-time j costs one batch of scalar loads.  (The host compilation
+// pass, which never runs kernels, reads the argument itself.)
+__device__ __forceinline__ GemvJob kernarg_job(const GemvGroup& g, int j) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef const __attribute__((address_space(4))) GemvGroup kgroup;
+  (void)g;
+  return ((kgroup*)__builtin_amdgcn_kernarg_segment_ptr())->job[j];
+#else
+  return g.job[j];
+#endif
+}
 
 // Registers of one tile for the batch-1 kernel: raw bytes of this lane's
 // 8 columns in every row, x for those columns, this lane's chunk length, and
@@ -953,14 +981,16 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   const uint32_t nw = blockDim.x / kWave;
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t lane = lane_id();
+  // the matrix of this workgroup: every job's first workgroup compared at
+  // once (independent scalar loads, not a chain of dependent ones)
   int j = 0;
-  while (j + 1 < static_cast<int>(g.count) && blockIdx.x >= g.job[j + 1].g0) j++;
-  // select the job with compile-time indices (no dynamic indexing of the
-  // kernel-argument struct, which would copy it to scratch)
-  GemvJob job = g.job[0];
 #pragma unroll
   for (int jj = 1; jj < kMaxJobs; jj++)
-    if (jj == j) job = g.job[jj];
+    if (jj < static_cast<int>(g.count) && blockIdx.x >= g.job[jj].g0) j = jj;
+  // the job's fields in one batch of scalar loads, straight from the
+  // kernel-argument segment (indexing the by-value argument with j would
+  // copy it to scratch; selecting among all jobs makes chains of loads)
+  const GemvJob job = kernarg_job(g, j);
   const BlobDev& b = job.b;
   const uint32_t J = g.lane_words;
   uint32_t* buf = lds + wave * (g.buf_words + kWave * J);
@@ -972,17 +1002,21 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   float* gsum = reinterpret_cast<float*>(tw + g.tw_words);
   const uint32_t n_tc = b.n_tc;
   const uint64_t T = b.n_tiles;
-  // this workgroup's tiles [r0, r1)
-  const uint64_t G = job.groups, gi = blockIdx.x - job.g0;
-  uint64_t r0, r1;
-  if (job.whole_rows) {
-    r0 = gi * b.n_tr / G * n_tc;
-    r1 = (gi + 1) * b.n_tr / G * n_tc;
-  } else {
-    r0 = gi * T / G;
-    r1 = (gi + 1) * T / G;
-  }
+  // this workgroup's tiles [r0, r1): range edge i is floor(i N / G) =
+  // i rq + floor(i rrem / G) (i rrem < G^2 < 2^32), in row blocks for
+  // whole_rows
+  const uint64_t G = job.groups;
+  const uint32_t gi = blockIdx.x - job.g0;
+  auto edge = [&](uint32_t i) __attribute__((always_inline)) {
+    const uint64_t e = static_cast<uint64_t>(i) * job.rq + div_magic(i * job.rrem, job.gm_hi, job.gm_lo);
+    return job.whole_rows ? e * n_tc : e;
+  };
+  const uint64_t r0 = edge(gi), r1 = edge(gi + 1);
   const uint32_t n_r = static_cast<uint32_t>(r1 - r0);
+  // tile t's row block (t < 2^32)
+  auto row_block = [&](uint64_t t) __attribute__((always_inline)) {
+    return static_cast<uint64_t>(div_magic(static_cast<uint32_t>(t), job.cm_hi, job.cm_lo));
+  };
 
   // the next tile of the range (claimed by lane 0, given to the wavefront)
   auto claim = [&]() __attribute__((always_inline)) {
@@ -1022,7 +1056,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     // the first tile's word offsets come by scalar loads (no LDS reads are
     // in flight yet)
     t = r0 + wave - 1;
-    const uint64_t ti = t / n_tc;
+    const uint64_t ti = row_block(t);
     const uint32_t tj = static_cast<uint32_t>(t - ti * n_tc);
     uint32_t w0 = 0, w1 = 0;
     if constexpr (!RAW16) {
@@ -1039,7 +1073,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   if (wave == 0 && claims) {
     t = claim();
     if (t < r1) {
-      const uint64_t ti = t / n_tc;
+      const uint64_t ti = row_block(t);
       const uint32_t tj = static_cast<uint32_t>(t - ti * n_tc);
       uint32_t w0, w1;
       words(t, w0, w1);
@@ -1086,7 +1120,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
       Regs nx;
       const uint64_t tn = claims ? claim() : r1;
       if (tn < r1) {
-        const uint64_t ni = tn / n_tc;
+        const uint64_t ni = row_block(tn);
         const uint32_t nj = static_cast<uint32_t>(tn - ni * n_tc);
         nx.load(b, job.x, g.ldx, g.batch, ni, nj, 0u, 0u, buf);
         asm volatile("" ::: "memory");
@@ -1167,7 +1201,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
         sums();
         break;
       }
-      const uint64_t ni = tn / n_tc;
+      const uint64_t ni = row_block(tn);
       const uint32_t nj = static_cast<uint32_t>(tn - ni * n_tc);
       uint32_t w0, w1;
       words(tn, w0, w1);
@@ -1197,7 +1231,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     Regs nx;
     const uint64_t tn = claims ? claim() : r1;
     if (tn < r1) {
-      const uint64_t ni = tn / n_tc;
+      const uint64_t ni = row_block(tn);
       const uint32_t nj = static_cast<uint32_t>(tn - ni * n_tc);
       uint32_t w0, w1;
       words(tn, w0, w1);
@@ -1258,7 +1292,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   if constexpr (SKINNY) {
     // whole row blocks only: every output adds its tile sums in column order
     if (n_r == 0) return;
-    const uint64_t rb_a = r0 / n_tc;
+    const uint64_t rb_a = row_block(r0);
     const uint32_t nbs = NB > 0 ? NB : g.batch;  // sums per row of a tile in LDS
     const uint32_t per_rb = TR * g.batch;
     for (uint32_t k = threadIdx.x; k < n_r / n_tc * per_rb; k += blockDim.x) {
@@ -1287,7 +1321,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   // waiting on another workgroup; the order of the additions is fixed by the
   // ranges, so repeated calls give the same bits.
   if (n_r == 0) return;
-  const uint64_t rb_a = r0 / n_tc, rb_b = (r1 - 1) / n_tc;
+  const uint64_t rb_a = row_block(r0), rb_b = row_block(r1 - 1);
   for (uint32_t k = threadIdx.x; k < (rb_b - rb_a + 1) * TR; k += blockDim.x) {
     const uint64_t rb = rb_a + k / TR;
     const uint32_t rr = k % TR;
@@ -2114,6 +2148,17 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
     job.ld = ld_out ? ld_out[j] : 0;
     job.g0 = groups;
     groups += job.groups;
+    // the kernel's divisions by groups and by n_tc (div_magic's ranges)
+    const uint64_t N = job.whole_rows ? L[j].b.n_tr : L[j].b.n_tiles;
+    if (job.groups >= (1u << 16) || L[j].b.n_tc >= (1u << 16) || L[j].b.n_tiles >= (1ull << 32))
+      return NWC_ERR_UNSUPPORTED;
+    job.rq = static_cast<uint32_t>(N / job.groups);
+    job.rrem = static_cast<uint32_t>(N % job.groups);
+    const uint64_t mg = ((1ull << 48) + job.groups - 1) / job.groups, mc = ((1ull << 48) + L[j].b.n_tc - 1) / L[j].b.n_tc;
+    job.gm_hi = static_cast<uint32_t>(mg >> 32);
+    job.gm_lo = static_cast<uint32_t>(mg);
+    job.cm_hi = static_cast<uint32_t>(mc >> 32);
+    job.cm_lo = static_cast<uint32_t>(mc);
   }
   g.count = static_cast<uint32_t>(count);
   g.y_f32 = y_f32;
