@@ -1538,24 +1538,28 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
     }
     wait_vmem();
   }
+  // decoding wavefronts 1 .. P-1 take the range's first tiles and ask for
+  // them at once (tile word offsets by scalar loads), before the barrier
+  // that waits for wavefront 0's decode table
+  Regs in;
+  const bool first = wave >= 1 && wave < P && wave - 1 < n_r;
+  if (first) issue(in, wave - 1, true);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's LDS writes are done
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   uint32_t* failed = ctl + 1;
 
   if (wave < P) {
-    // ---- decoding wavefront: wavefronts 1 .. P-1 take the first tiles,
+    // ---- decoding wavefront: wavefronts 1 .. P-1 decode the first tiles,
     // wavefront 0 claims (its tile's loads are issued here, after the
-    // barrier, so that no tile's registers live across the split into the
-    // two kinds of wavefront)
-    Regs in;
+    // barrier)
     uint32_t s = n_r;
     if (wave == 0) {
       if (claims) s = claim();
-    } else if (wave - 1 < n_r) {
+      if (s < n_r) issue(in, s, false);
+    } else if (first) {
       s = wave - 1;
     }
-    if (s < n_r) issue(in, s, !claims);
     constexpr int PRE = TR * 7 / 8;
     while (s < n_r) {
       wait_vmem_but<(TR - PRE < TR / 2 ? TR - PRE : TR / 2)>();
