@@ -633,6 +633,7 @@ struct GemvGroup {
   // consumer keeps its own sums)
   uint32_t producers, consumers, ring_log2, rb_words, chain, batch_groups;
   uint32_t wait_limit;  // polls of a flag before a wait gives up
+  uint32_t waves;       // k_gemv: wavefronts per workgroup (the launch's block size / 64)
 };
 
 // Job j of a kernel's GemvGroup argument (its only argument, at the start of
@@ -978,7 +979,9 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   using Regs = std::conditional_t<RAW16, TileRegs16<TR>, TileRegs<TR, NX>>;
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTable];  // static: LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  const uint32_t nw = blockDim.x / kWave;
+  // (the block size from the argument, not the launch's hidden arguments:
+  // one scalar load less on the way to the first tile load)
+  const uint32_t nw = g.waves;
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t lane = lane_id();
   // the matrix of this workgroup: every job's first workgroup compared at
@@ -992,6 +995,12 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   // copy it to scratch; selecting among all jobs makes chains of loads)
   const GemvJob job = kernarg_job(g, j);
   const BlobDev& b = job.b;
+  // the fields the first tile's loads need, all here at once: left to
+  // itself the compiler issues some of them only after waiting for the
+  // others, one more scalar-memory round trip before any tile load
+  asm volatile("" ::"s"(b.table), "s"(b.tile_words), "s"(b.chunk_bits), "s"(b.raw), "s"(b.stream), "s"(b.rows),
+               "s"(b.cols), "s"(b.raw_ld), "s"(job.x), "s"(job.rq), "s"(job.rrem), "s"(job.gm_hi), "s"(job.gm_lo),
+               "s"(nw));
   const uint32_t J = g.lane_words;
   uint32_t* buf = lds + wave * (g.buf_words + kWave * J);
   uint32_t* slot = buf + g.buf_words;
@@ -1295,7 +1304,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
     const uint64_t rb_a = row_block(r0);
     const uint32_t nbs = NB > 0 ? NB : g.batch;  // sums per row of a tile in LDS
     const uint32_t per_rb = TR * g.batch;
-    for (uint32_t k = threadIdx.x; k < n_r / n_tc * per_rb; k += blockDim.x) {
+    for (uint32_t k = threadIdx.x; k < n_r / n_tc * per_rb; k += nw * kWave) {
       const uint64_t rb = rb_a + k / per_rb;
       const uint32_t rr = (k % per_rb) / g.batch, beta = k % g.batch;
       const uint64_t row = rb * TR + rr;
@@ -1322,7 +1331,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   // ranges, so repeated calls give the same bits.
   if (n_r == 0) return;
   const uint64_t rb_a = row_block(r0), rb_b = row_block(r1 - 1);
-  for (uint32_t k = threadIdx.x; k < (rb_b - rb_a + 1) * TR; k += blockDim.x) {
+  for (uint32_t k = threadIdx.x; k < (rb_b - rb_a + 1) * TR; k += nw * kWave) {
     const uint64_t rb = rb_a + k / TR;
     const uint32_t rr = k % TR;
     const uint64_t row = rb * TR + rr;
@@ -2174,6 +2183,7 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   g.batch = static_cast<uint32_t>(batch);
   const size_t lds = nw * per_wave + best.group_lds(sums);
   if (set_lds(k_gemv<TR, MAXW, NB, FIT2, QUAD>, lds) != hipSuccess) return NWC_ERR_HIP;
+  g.waves = nw;
   return launch(k_gemv<TR, MAXW, NB, FIT2, QUAD>, dim3(groups), dim3(nw * kWave), lds, s, g);
 }
 
