@@ -188,7 +188,9 @@ nwc_status nwc_workspace_size(const nwc_info *info, int batch, size_t *bytes);
  * function describes (zero-filled before first use on the fused path).
  * Calls that share a workspace must not run concurrently (same stream, or
  * ordered by events).  x and y must not alias.  Async.
- * Errors: INVALID_ARG, BUFFER_TOO_SMALL (ws), ALIGNMENT, UNSUPPORTED, HIP. */
+ * Errors: INVALID_ARG, BUFFER_TOO_SMALL (ws), ALIGNMENT, HIP; UNSUPPORTED
+ * also for a fused-path blob of 2^32 tiles or more or of 65536 column tiles
+ * or more (cols >= 2^25), whose tile arithmetic the kernel does not cover. */
 nwc_status nwc_gemv(const nwc_info *info, const void *blob_dev, const uint16_t *x_dev,
                     void *y_dev, nwc_out_type y_type, void *ws, size_t ws_bytes,
                     void *stream);
