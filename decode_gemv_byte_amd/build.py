@@ -22,7 +22,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# kernarg preload: a kernel's first 7 arguments arrive in scalar registers at
+# launch (k_gemv's job boundaries), a memory round trip less before its first
+# tile load; the compiler keeps a loading prologue for firmware without it
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-kernarg-preload-count=7"]
 
 
 def _run(cmd):

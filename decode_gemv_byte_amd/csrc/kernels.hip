@@ -613,7 +613,7 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t hi, uint32_t 
 
 // a chain slot holds a partial sum's FP32 bits with this flag set
 constexpr uint64_t kSlotFull = 1ull << 32;
-constexpr int kMaxJobs = 8;
+constexpr int kMaxJobs = 8;  // k_gemv takes jobs 1 .. 7's first workgroups as arguments f1 .. f7
 constexpr int kRawBf16 = 100;  // NB of the uncompressed comparator: plain BF16 weights, no decode
 constexpr uint32_t kGroupLds = 8192;       // least per-workgroup LDS for control words, offsets, tile sums
 constexpr uint32_t kSkinnyLds = 24576;     // per-workgroup LDS for the skinny mode's tile sums
@@ -636,15 +636,23 @@ struct GemvGroup {
   uint32_t waves;       // k_gemv: wavefronts per workgroup (the launch's block size / 64)
 };
 
-// Job j of a kernel's GemvGroup argument (its only argument, at the start of
-// the kernel-argument segment), read through the constant address space so
-// that a run-time j costs one batch of scalar loads.  (The host compilation
-// pass, which never runs kernels, reads the argument itself.)
+// Where k_gemv's GemvGroup argument starts in the kernel-argument segment:
+// after its seven 32-bit arguments f1 .. f7, at the group's own alignment
+// (arguments are laid out in order, each at its natural alignment; the
+// kernel metadata of the build lists this offset for the argument).
+constexpr uint32_t kGemvGroupArgOffset =
+    (7 * sizeof(uint32_t) + alignof(GemvGroup) - 1) / alignof(GemvGroup) * alignof(GemvGroup);
+static_assert(kGemvGroupArgOffset == 32, "k_gemv's argument layout");
+
+// Job j of k_gemv's GemvGroup argument, read through the constant address
+// space so that a run-time j costs one batch of scalar loads.  (The host
+// compilation pass, which never runs kernels, reads the argument itself.)
 __device__ __forceinline__ GemvJob kernarg_job(const GemvGroup& g, int j) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef const __attribute__((address_space(4))) GemvGroup kgroup;
+  typedef const __attribute__((address_space(4))) uint8_t kbyte;
   (void)g;
-  return ((kgroup*)__builtin_amdgcn_kernarg_segment_ptr())->job[j];
+  return ((kgroup*)((kbyte*)__builtin_amdgcn_kernarg_segment_ptr() + kGemvGroupArgOffset))->job[j];
 #else
   return g.job[j];
 #endif
@@ -966,7 +974,12 @@ __device__ __forceinline__ uint64_t range_of(uint64_t t, uint64_t T, uint64_t W)
 // blocks); -1 for the standalone decode, which writes each decoded tile to
 // W' (job.y, rows of g.ldy elements) once the next tile's data is in.
 template <int TR, int MAXW, int NB, bool FIT2 = false, bool QUAD = false>
-__global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
+// f1 .. f7: the first workgroups of jobs 1 .. 7 (0xFFFFFFFF past the last
+// job), separate arguments so that they arrive preloaded in scalar registers
+// (the build preloads a kernel's first arguments) and the workgroup's job is
+// known without a memory round trip.
+__global__ __launch_bounds__(MAXW * kWave) void k_gemv(uint32_t f1, uint32_t f2, uint32_t f3, uint32_t f4, uint32_t f5,
+                                                       uint32_t f6, uint32_t f7, const GemvGroup g) {
   constexpr bool RAW16 = NB == kRawBf16;
   static_assert(!QUAD || NB != kRawBf16, "two pairs per window: decoding modes");
   constexpr bool DECODE = NB < 0;
@@ -984,12 +997,17 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   const uint32_t nw = g.waves;
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t lane = lane_id();
-  // the matrix of this workgroup: every job's first workgroup compared at
-  // once (independent scalar loads, not a chain of dependent ones)
+  // the matrix of this workgroup: the number of jobs that start at or
+  // before it, after the first
+  const uint32_t bx = blockIdx.x;
   int j = 0;
-#pragma unroll
-  for (int jj = 1; jj < kMaxJobs; jj++)
-    if (jj < static_cast<int>(g.count) && blockIdx.x >= g.job[jj].g0) j = jj;
+  j = bx >= f1 ? 1 : j;
+  j = bx >= f2 ? 2 : j;
+  j = bx >= f3 ? 3 : j;
+  j = bx >= f4 ? 4 : j;
+  j = bx >= f5 ? 5 : j;
+  j = bx >= f6 ? 6 : j;
+  j = bx >= f7 ? 7 : j;
   // the job's fields in one batch of scalar loads, straight from the
   // kernel-argument segment (indexing the by-value argument with j would
   // copy it to scratch; selecting among all jobs makes chains of loads)
@@ -1000,7 +1018,7 @@ __global__ __launch_bounds__(MAXW * kWave) void k_gemv(const GemvGroup g) {
   // others, one more scalar-memory round trip before any tile load
   asm volatile("" ::"s"(b.table), "s"(b.tile_words), "s"(b.chunk_bits), "s"(b.raw), "s"(b.stream), "s"(b.rows),
                "s"(b.cols), "s"(b.raw_ld), "s"(job.x), "s"(job.rq), "s"(job.rrem), "s"(job.gm_hi), "s"(job.gm_lo),
-               "s"(nw));
+               "s"(nw), "s"(g.lane_words), "s"(g.buf_words), "s"(g.tw_words));
   const uint32_t J = g.lane_words;
   uint32_t* buf = lds + wave * (g.buf_words + kWave * J);
   uint32_t* slot = buf + g.buf_words;
@@ -2184,7 +2202,10 @@ nwc_status launch_gemv(const Launch* L, const uint16_t* const* x, void* const* y
   const size_t lds = nw * per_wave + best.group_lds(sums);
   if (set_lds(k_gemv<TR, MAXW, NB, FIT2, QUAD>, lds) != hipSuccess) return NWC_ERR_HIP;
   g.waves = nw;
-  return launch(k_gemv<TR, MAXW, NB, FIT2, QUAD>, dim3(groups), dim3(nw * kWave), lds, s, g);
+  uint32_t f[kMaxJobs];
+  for (int j = 1; j < kMaxJobs; j++) f[j] = j < count ? g.job[j].g0 : 0xFFFFFFFFu;
+  return launch(k_gemv<TR, MAXW, NB, FIT2, QUAD>, dim3(groups), dim3(nw * kWave), lds, s, f[1], f[2], f[3], f[4], f[5],
+                f[6], f[7], g);
 }
 
 // The batch-1 launch for the matrices' tile height: two pairs per window
