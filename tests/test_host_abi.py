@@ -415,3 +415,48 @@ def test_unknown_code_family_is_rejected():
     w = workloads.gaussian_bits((16, 512), 0.02, 1)
     with pytest.raises(nwc.NwcError):
         nwc.nwc_encode(w, dict(code_family=2))
+
+
+def _device_metadata():
+    """The AMDGPU kernel metadata of the built library's gfx950 code object
+    (section .hip_fatbin, unbundled, notes read), as parsed YAML; None when
+    the ROCm LLVM tools are not there."""
+    import shutil
+    import subprocess
+    import tempfile
+    import yaml
+    tools = "/opt/rocm/llvm/bin"
+    objcopy, bundler, readelf = (os.path.join(tools, t) for t in ("llvm-objcopy", "clang-offload-bundler", "llvm-readelf"))
+    if not all(os.path.exists(t) for t in (objcopy, bundler, readelf)):
+        return None
+    lib = os.path.join(ROOT, "decode_gemv_byte_amd", "libnwc.so")
+    with tempfile.TemporaryDirectory() as d:
+        fb, co = os.path.join(d, "fb.bin"), os.path.join(d, "co.o")
+        shutil.copy(lib, os.path.join(d, "lib.so"))
+        subprocess.run([objcopy, "--dump-section", ".hip_fatbin=" + fb, os.path.join(d, "lib.so"),
+                        os.path.join(d, "out.so")], check=True, capture_output=True)
+        subprocess.run([bundler, "--unbundle", "--type=o", "--input=" + fb,
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", "--output=" + co], check=True, capture_output=True)
+        notes = subprocess.run([readelf, "--notes", co], check=True, capture_output=True, text=True).stdout
+    text = notes[notes.index("---"):]
+    text = text[text.index("\n") + 1:text.index("\n...")]
+    return yaml.safe_load(text)
+
+
+def test_k_gemv_argument_layout():
+    # k_gemv reads its group argument through the kernel-argument segment at
+    # a fixed byte offset (after seven 32-bit arguments that the build
+    # preloads into scalar registers): every k_gemv in the built code object
+    # must have the group at exactly that offset, and the seven arguments
+    # before it (a wrong offset reads garbage pointers on the GPU)
+    meta = _device_metadata()
+    if meta is None:
+        pytest.skip("ROCm LLVM tools not found")
+    kernels = [k for k in meta["amdhsa.kernels"] if k[".name"].startswith("_ZN12_GLOBAL__N_16k_gemvI")]
+    assert len(kernels) >= 30
+    for k in kernels:
+        args = k[".args"]
+        assert [a[".offset"] for a in args[:7]] == [0, 4, 8, 12, 16, 20, 24], k[".name"]
+        assert all(a[".size"] == 4 for a in args[:7]), k[".name"]
+        assert args[7][".offset"] == 32 and args[7][".size"] > 1000, k[".name"]
+        assert k[".kernarg_segment_size"] >= 32 + args[7][".size"]
