@@ -39,6 +39,10 @@
 //      added in LDS in column order; a row block that range edges cut is
 //      finished along a chain of 64-bit atomic exchanges in the workspace, so
 //      the summation order is fixed and no workgroup waits for another.
+//    - Prologue: nothing is asked of HBM before a wavefront knows its job,
+//      range and first tile, so the job boundaries come as preloaded scalar
+//      arguments, the job's fields in one batch of scalar loads, and range
+//      edges and tile row blocks from host-computed reciprocals (div_magic).
 //    - Skinny mode: whole row blocks per range; up to 4 X rows are
 //      multiplied as each pair is decoded, more (16-row tiles) from the
 //      decoded tile in registers.
@@ -663,9 +667,10 @@ __device__ __forceinline__ GemvJob kernarg_job(const GemvGroup& g, int j) {
 // where the tile's stream starts.  Every load goes through a buffer resource
 // built from wave-uniform addresses (row offsets in scalar registers, one
 // constant lane offset), so issuing a tile costs almost no vector ALU work.
-// The tile's word offsets (tw0, tw1) come in from a vector load issued one
-// tile earlier: a scalar load would share its wait counter with the LDS
-// reads of the decode loop and stall it for a full memory round trip.
+// The tile's word offsets (tw0, tw1) are read from the copy of the range's
+// offsets in LDS (a wavefront's first tile: by scalar loads, before any LDS
+// read is in flight): a scalar load inside the decode loop would share its
+// wait counter with the LDS reads and stall them for a memory round trip.
 template <int TR, int NX>
 struct TileRegs {
   uint2 raw[TR];
