@@ -1499,9 +1499,13 @@ __global__ __launch_bounds__(kMcMaxWaves * kWave) void k_skinny_mc(const GemvGro
   float* part = reinterpret_cast<float*>(done + g.rb_words);
   const uint32_t n_tc = b.n_tc;
   const uint32_t B = g.batch;
-  // this workgroup's row blocks [rb_a, rb_b) and tiles [r0, r1)
-  const uint64_t G = job.groups, gi = blockIdx.x;
-  const uint64_t rb_a = gi * b.n_tr / G, rb_b = (gi + 1) * b.n_tr / G;
+  // this workgroup's row blocks [rb_a, rb_b) and tiles [r0, r1): edge i is
+  // floor(i n_tr / G) = i rq + floor(i rrem / G) (host-computed, as in k_gemv)
+  const uint32_t gi = blockIdx.x;
+  auto edge = [&](uint32_t i) __attribute__((always_inline)) {
+    return static_cast<uint64_t>(i) * job.rq + div_magic(i * job.rrem, job.gm_hi, job.gm_lo);
+  };
+  const uint64_t rb_a = edge(gi), rb_b = edge(gi + 1);
   const uint32_t n_rb = static_cast<uint32_t>(rb_b - rb_a);
   const uint64_t r0 = rb_a * n_tc;
   const uint32_t n_r = n_rb * n_tc;
@@ -2325,6 +2329,12 @@ nwc_status launch_skinny_mc(const Launch& L, const uint16_t* X, void* Y, int y_f
   g.job[0].x = X;
   g.job[0].y = Y;
   g.job[0].groups = static_cast<uint32_t>(best_g[ch]);
+  if (best_g[ch] >= (1u << 16)) return NWC_ERR_UNSUPPORTED;  // div_magic's divisor range
+  g.job[0].rq = static_cast<uint32_t>(L.b.n_tr / best_g[ch]);
+  g.job[0].rrem = static_cast<uint32_t>(L.b.n_tr % best_g[ch]);
+  const uint64_t mg = ((1ull << 48) + best_g[ch] - 1) / best_g[ch];
+  g.job[0].gm_hi = static_cast<uint32_t>(mg >> 32);
+  g.job[0].gm_lo = static_cast<uint32_t>(mg);
   g.job[0].whole_rows = 1;
   g.count = 1;
   g.y_f32 = y_f32;
